@@ -1,5 +1,283 @@
 """QLoRA NF4 hot path on MI355X (gfx950): thin Python binding over the C ABI.
 
-The library is loaded lazily so that ``bit_nf4_quantized_22_amd.synth`` (the
-seeded input generators) can be imported without it.
+The functions here have the names of the C entry points in
+``include/qlora_nf4.h`` and only marshal arguments: they check that tensors
+are contiguous device tensors of the right dtype and size, allocate outputs
+with torch when the caller passes none, and call the library on torch's
+current stream.  Every step of the computation runs in the HIP kernels of
+``lib/libqlora_nf4.so``; there is no other code path.  If the library is not
+built, every call raises.
+
+The library is loaded lazily so that ``bit_nf4_quantized_22_amd.synth`` can
+be imported without it.
 """
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "libqlora_nf4.so")
+
+QN_OK, QN_ERR_NULL, QN_ERR_SHAPE, QN_ERR_ALIGN = 0, -1, -2, -3
+QN_ERR_UNSUPPORTED, QN_ERR_WORKSPACE, QN_ERR_HIP = -4, -5, -6
+QN_F32, QN_BF16 = 0, 1
+QN_OP_FWD, QN_OP_BWD_DX, QN_OP_LORA_GRADS = 0, 1, 2
+BLOCKSIZE, GROUP = 64, 256
+
+EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
+           "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
+           "lora_grads")
+
+
+class QnError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+class qn_weight(ctypes.Structure):
+    _fields_ = [("packed", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
+                ("gscale", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
+                ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("blocksize", ctypes.c_int32), ("group", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load_library():
+    """Load lib/libqlora_nf4.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m bit_nf4_quantized_22_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                             ctypes.c_float, ctypes.c_size_t)
+    wp = ctypes.POINTER(qn_weight)
+    sig = {
+        "qn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+        "nf4_quantize": (ctypes.c_int, [vp, i32, i64, i32, vp, vp, vp]),
+        "dq_quantize_scales": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+        "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
+        "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
+        "qlora_linear_fwd": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "qlora_linear_bwd_dx": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "lora_grads": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp,
+                                      vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(fn, status):
+    if status != QN_OK:
+        msg = load_library().qn_status_string(status).decode()
+        raise QnError(fn, status, msg)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, dtype, numel=None, name="tensor"):
+    torch = _torch()
+    if t is None:
+        return None
+    if not t.is_cuda or not t.is_contiguous() or t.dtype != dtype:
+        raise ValueError(f"{name}: need a contiguous {dtype} device tensor")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name}: expected {numel} elements, got {t.numel()}")
+    return t
+
+
+class QuantWeight:
+    """Device tensors of an NF4 weight W[N, K] (+ double-quantised constants).
+
+    packed uint8[N*K/2]; qscale uint8[N*K/64] and gscale fp32[ceil(N*K/64/256)]
+    when double-quantised, else absmax fp32[N*K/64].
+    """
+
+    def __init__(self, packed, N, K, qscale=None, gscale=None, absmax=None):
+        self.packed, self.qscale, self.gscale, self.absmax = packed, qscale, gscale, absmax
+        self.N, self.K = int(N), int(K)
+
+    def c_struct(self):
+        return qn_weight(self.packed.data_ptr(),
+                         None if self.qscale is None else self.qscale.data_ptr(),
+                         None if self.gscale is None else self.gscale.data_ptr(),
+                         None if self.absmax is None else self.absmax.data_ptr(),
+                         self.N, self.K, BLOCKSIZE, GROUP)
+
+
+def nf4_codebook():
+    """The 16 fp32 NF4 code points (host call), as a list of floats."""
+    out = (ctypes.c_float * 16)()
+    _check("nf4_codebook", load_library().nf4_codebook(out))
+    return list(out)
+
+
+def nf4_quantize(w, packed=None, absmax=None, stream=None):
+    """Blockwise NF4 quantisation of a fp32 or bf16 device tensor (flattened).
+
+    Returns (packed uint8[numel/2], absmax fp32[ceil(numel/64)]).
+    """
+    torch = _torch()
+    lib = load_library()
+    if w.dtype == torch.float32:
+        dt = QN_F32
+    elif w.dtype == torch.bfloat16:
+        dt = QN_BF16
+    else:
+        raise ValueError("nf4_quantize: weights must be float32 or bfloat16")
+    _dev(w, w.dtype, name="w")
+    n = w.numel()
+    nb = -(-n // BLOCKSIZE)
+    if packed is None:
+        packed = torch.empty(n // 2, dtype=torch.uint8, device=w.device)
+    if absmax is None:
+        absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
+    _dev(packed, torch.uint8, n // 2, "packed")
+    _dev(absmax, torch.float32, nb, "absmax")
+    _check("nf4_quantize", lib.nf4_quantize(_ptr(w), dt, n, BLOCKSIZE, _ptr(packed),
+                                            _ptr(absmax), _stream(stream)))
+    return packed, absmax
+
+
+def dq_quantize_scales(absmax, qscale=None, gscale=None, stream=None):
+    """Double quantisation: returns (qscale uint8[nb], gscale fp32[ceil(nb/256)])."""
+    torch = _torch()
+    lib = load_library()
+    _dev(absmax, torch.float32, name="absmax")
+    nb = absmax.numel()
+    ng = -(-nb // GROUP)
+    if qscale is None:
+        qscale = torch.empty(nb, dtype=torch.uint8, device=absmax.device)
+    if gscale is None:
+        gscale = torch.empty(ng, dtype=torch.float32, device=absmax.device)
+    _dev(qscale, torch.uint8, nb, "qscale")
+    _dev(gscale, torch.float32, ng, "gscale")
+    _check("dq_quantize_scales", lib.dq_quantize_scales(_ptr(absmax), nb, GROUP, _ptr(qscale),
+                                                        _ptr(gscale), _stream(stream)))
+    return qscale, gscale
+
+
+def quantize_weight(w, double_quant=True, stream=None):
+    """nf4_quantize (+ dq_quantize_scales) of a [N, K] tensor -> QuantWeight."""
+    N, K = w.shape
+    packed, absmax = nf4_quantize(w, stream=stream)
+    if not double_quant:
+        return QuantWeight(packed, N, K, absmax=absmax)
+    qscale, gscale = dq_quantize_scales(absmax, stream=stream)
+    return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale)
+
+
+def nf4_dequant(qw, out_dtype=None, out=None, stream=None):
+    """Materialise W[N, K] as fp32 or bf16."""
+    torch = _torch()
+    lib = load_library()
+    out_dtype = out_dtype or torch.bfloat16
+    dt = QN_BF16 if out_dtype == torch.bfloat16 else QN_F32
+    if out is None:
+        out = torch.empty((qw.N, qw.K), dtype=out_dtype, device=qw.packed.device)
+    _dev(out, out_dtype, qw.N * qw.K, "out")
+    cw = qw.c_struct()
+    _check("nf4_dequant", lib.nf4_dequant(ctypes.byref(cw), dt, _ptr(out), _stream(stream)))
+    return out
+
+
+def qn_workspace_bytes(op, M, N, K, r):
+    return int(load_library().qn_workspace_bytes(op, M, N, K, r))
+
+
+def _workspace(op, M, N, K, r, ws, device):
+    torch = _torch()
+    need = qn_workspace_bytes(op, M, N, K, r)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, (0 if ws is None else ws.numel())
+
+
+def qlora_linear_fwd(qw, x, A, B, r, alpha, y=None, u_out=None, ws=None, stream=None):
+    """y = x W^T + (alpha/r) (x A^T) B^T  (bf16 in/out)."""
+    torch = _torch()
+    lib = load_library()
+    M = x.shape[0]
+    _dev(x, torch.bfloat16, M * qw.K, "x")
+    if r:
+        _dev(A, torch.bfloat16, r * qw.K, "A")
+        _dev(B, torch.bfloat16, qw.N * r, "B")
+    if y is None:
+        y = torch.empty((M, qw.N), dtype=torch.bfloat16, device=x.device)
+    _dev(y, torch.bfloat16, M * qw.N, "y")
+    _dev(u_out, torch.bfloat16, M * r, "u_out")
+    ws, wsb = _workspace(QN_OP_FWD, M, qw.N, qw.K, r, ws, x.device)
+    cw = qw.c_struct()
+    _check("qlora_linear_fwd", lib.qlora_linear_fwd(
+        ctypes.byref(cw), _ptr(x), M, _ptr(A) if r else None, _ptr(B) if r else None, r,
+        float(alpha), _ptr(y), _ptr(u_out), _ptr(ws), wsb, _stream(stream)))
+    return y
+
+
+def qlora_linear_bwd_dx(qw, dy, A, B, r, alpha, dx=None, t_out=None, ws=None, stream=None):
+    """dx = dy W + (alpha/r) (dy B) A  (bf16 in/out)."""
+    torch = _torch()
+    lib = load_library()
+    M = dy.shape[0]
+    _dev(dy, torch.bfloat16, M * qw.N, "dy")
+    if r:
+        _dev(A, torch.bfloat16, r * qw.K, "A")
+        _dev(B, torch.bfloat16, qw.N * r, "B")
+    if dx is None:
+        dx = torch.empty((M, qw.K), dtype=torch.bfloat16, device=dy.device)
+    _dev(dx, torch.bfloat16, M * qw.K, "dx")
+    _dev(t_out, torch.bfloat16, M * r, "t_out")
+    ws, wsb = _workspace(QN_OP_BWD_DX, M, qw.N, qw.K, r, ws, dy.device)
+    cw = qw.c_struct()
+    _check("qlora_linear_bwd_dx", lib.qlora_linear_bwd_dx(
+        ctypes.byref(cw), _ptr(dy), M, _ptr(A) if r else None, _ptr(B) if r else None, r,
+        float(alpha), _ptr(dx), _ptr(t_out), _ptr(ws), wsb, _stream(stream)))
+    return dx
+
+
+def lora_grads(x, dy, A, B, r, alpha, u=None, t=None, dA=None, dB=None, ws=None, stream=None):
+    """(dA fp32[r, K], dB fp32[N, r]) = ((alpha/r) (dy B)^T x, (alpha/r) dy^T (x A^T))."""
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    N = dy.shape[1]
+    _dev(x, torch.bfloat16, M * K, "x")
+    _dev(dy, torch.bfloat16, M * N, "dy")
+    _dev(A, torch.bfloat16, r * K, "A")
+    _dev(B, torch.bfloat16, N * r, "B")
+    _dev(u, torch.bfloat16, M * r, "u")
+    _dev(t, torch.bfloat16, M * r, "t")
+    if dA is None:
+        dA = torch.empty((r, K), dtype=torch.float32, device=x.device)
+    if dB is None:
+        dB = torch.empty((N, r), dtype=torch.float32, device=x.device)
+    _dev(dA, torch.float32, r * K, "dA")
+    _dev(dB, torch.float32, N * r, "dB")
+    ws, wsb = _workspace(QN_OP_LORA_GRADS, M, N, K, r, ws, x.device)
+    _check("lora_grads", lib.lora_grads(
+        _ptr(x), _ptr(dy), _ptr(u), _ptr(t), _ptr(A), _ptr(B), M, N, K, r, float(alpha),
+        _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(stream)))
+    return dA, dB

@@ -1,0 +1,246 @@
+// C ABI of the QLoRA NF4 library: argument validation on the host, then the
+// launches on the caller's stream.  See include/qlora_nf4.h for the contract
+// of every entry point.
+
+#include "qlora_nf4.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "qn_launch.h"
+#include "qn_tables.h"
+
+namespace {
+
+constexpr int kBlock = 64;
+constexpr int kGroup = 256;
+constexpr int kMaxRank = 128;
+constexpr int64_t kGemvMaxM = 16;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? QN_OK : QN_ERR_HIP; }
+
+// Validates a quantised weight for the linear ops and fills a view.
+int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
+  if (!w || !w->packed) return QN_ERR_NULL;
+  if (w->blocksize != kBlock || w->group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (w->N < 0 || w->K < 0) return QN_ERR_SHAPE;
+  if (linear && (w->N % 64 != 0 || w->K % 64 != 0)) return QN_ERR_SHAPE;
+  if (w->qscale) {
+    if (!w->gscale) return QN_ERR_NULL;
+  } else if (!w->absmax) {
+    return QN_ERR_NULL;
+  }
+  if (!aligned(w->packed, 16)) return QN_ERR_ALIGN;
+  if ((w->gscale && !aligned(w->gscale, 4)) || (w->absmax && !aligned(w->absmax, 4)))
+    return QN_ERR_ALIGN;
+  v.packed = w->packed;
+  v.qscale = w->qscale;
+  v.gscale = w->gscale;
+  v.absmax = w->qscale ? nullptr : w->absmax;
+  v.N = w->N;
+  v.K = w->K;
+  return QN_OK;
+}
+
+size_t fwd_ws(int64_t M, int32_t r) {
+  if (r == 0 || M == 0) return 0;
+  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+  return round_up(mr * 4, 256) + round_up(mr * 2, 256);
+}
+
+size_t bwd_ws(int64_t M, int32_t r) {
+  if (r == 0 || M == 0) return 0;
+  return round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256);
+}
+
+size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (r == 0) return 0;
+  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+  return 2 * round_up(mr * 4, 256) + round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qn_status_string(int status) {
+  switch (status) {
+    case QN_OK: return "ok";
+    case QN_ERR_NULL: return "a required pointer is NULL";
+    case QN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case QN_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QN_ERR_UNSUPPORTED: return "unsupported parameter (blocksize 64, group 256, fp32/bf16 only)";
+    case QN_ERR_WORKSPACE: return "workspace missing or too small";
+    case QN_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int nf4_codebook(float out[16]) {
+  if (!out) return QN_ERR_NULL;
+  const qn::Tables* t = qn::tables();
+  if (!t) return QN_ERR_UNSUPPORTED;
+  std::memcpy(out, t->q32, sizeof(t->q32));
+  return QN_OK;
+}
+
+int nf4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+                 uint8_t* packed, float* absmax, void* stream) {
+  if (blocksize != kBlock) return QN_ERR_UNSUPPORTED;
+  if (dtype != QN_F32 && dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
+  if (numel < 0 || (numel & 1)) return QN_ERR_SHAPE;
+  if (numel == 0) return QN_OK;
+  if (!w || !packed || !absmax) return QN_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_quantize(w, dtype == QN_BF16, numel, packed, absmax, as_stream(stream)));
+}
+
+int dq_quantize_scales(const float* absmax, int64_t nblocks, int32_t group, uint8_t* qscale,
+                       float* gscale, void* stream) {
+  if (group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (nblocks < 0) return QN_ERR_SHAPE;
+  if (nblocks == 0) return QN_OK;
+  if (!absmax || !qscale || !gscale) return QN_ERR_NULL;
+  if (!aligned(absmax, 4) || !aligned(gscale, 4)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_dq(absmax, nblocks, qscale, gscale, as_stream(stream)));
+}
+
+int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, false);
+  if (st != QN_OK) return st;
+  if (out_dtype != QN_F32 && out_dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
+  if ((w->N * w->K) % 32 != 0) return QN_ERR_SHAPE;
+  if (w->N * w->K == 0) return QN_OK;
+  if (!out) return QN_ERR_NULL;
+  if (!aligned(out, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_dequant(v, out_dtype == QN_BF16, out, as_stream(stream)));
+}
+
+size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (M < 0 || N < 0 || K < 0 || r < 0 || r > kMaxRank) return 0;
+  switch (op) {
+    case QN_OP_FWD: return fwd_ws(M, r);
+    case QN_OP_BWD_DX: return bwd_ws(M, r);
+    case QN_OP_LORA_GRADS: return grads_ws(M, N, K, r);
+    default: return 0;
+  }
+}
+
+int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_bf16* A,
+                     const qn_bf16* B, int32_t r, float alpha, qn_bf16* y, qn_bf16* u_out,
+                     void* ws, size_t ws_bytes, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, true);
+  if (st != QN_OK) return st;
+  if (M < 0 || r < 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (M == 0 || w->N == 0) return QN_OK;
+  if (!x || !y || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2))) ||
+      (u_out && !aligned(u_out, 2)))
+    return QN_ERR_ALIGN;
+  const size_t need = fwd_ws(M, r);
+  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  float* u32 = nullptr;
+  uint16_t* us = nullptr;
+  if (r > 0) {
+    const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+    u32 = static_cast<float*>(ws);
+    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round_up(mr * 4, 256));
+    hipError_t e = qn::launch_skinny(x, M, w->K, A, true, r, scale, M <= kGemvMaxM ? u32 : nullptr,
+                                     M <= kGemvMaxM ? nullptr : us, u_out, s);
+    if (e != hipSuccess) return QN_ERR_HIP;
+  }
+  if (M <= kGemvMaxM)
+    return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, B, r, scale, y, s));
+  return hip_status(qn::launch_gemm_fwd(v, x, M, us, B, r, y, s));
+}
+
+int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
+                        const qn_bf16* B, int32_t r, float alpha, qn_bf16* dx, qn_bf16* t_out,
+                        void* ws, size_t ws_bytes, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, true);
+  if (st != QN_OK) return st;
+  if (M < 0 || r < 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (M == 0 || w->K == 0) return QN_OK;
+  if (!dy || !dx || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
+      (t_out && !aligned(t_out, 2)))
+    return QN_ERR_ALIGN;
+  const size_t need = bwd_ws(M, r);
+  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  uint16_t* ts = nullptr;
+  if (r > 0) {
+    ts = static_cast<uint16_t*>(ws);
+    hipError_t e = qn::launch_skinny(dy, M, w->N, B, false, r, scale, nullptr, ts, t_out, s);
+    if (e != hipSuccess) return QN_ERR_HIP;
+  }
+  return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
+}
+
+int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_bf16* t,
+               const qn_bf16* A, const qn_bf16* B, int64_t M, int64_t N, int64_t K, int32_t r,
+               float alpha, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || r < 0) return QN_ERR_SHAPE;
+  if (r == 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (N % 64 != 0 || K % 64 != 0) return QN_ERR_SHAPE;
+  if (!dA || !dB) return QN_ERR_NULL;
+  if (M > 0 && (!x || !dy || (!u && !A) || (!t && !B))) return QN_ERR_NULL;
+  if ((x && !aligned(x, 16)) || (dy && !aligned(dy, 16)) || (A && !aligned(A, 16)) ||
+      (B && !aligned(B, 2)) || (u && !aligned(u, 2)) || (t && !aligned(t, 2)) ||
+      !aligned(dA, 4) || !aligned(dB, 4))
+    return QN_ERR_ALIGN;
+  const size_t need = grads_ws(M, N, K, r);
+  if (!ws || ws_bytes < need) return QN_ERR_WORKSPACE;
+  if (!aligned(ws, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const float scale = alpha / static_cast<float>(r);
+  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+  char* base = static_cast<char*>(ws);
+  float* u32 = reinterpret_cast<float*>(base);
+  float* t32 = reinterpret_cast<float*>(base + round_up(mr * 4, 256));
+  void* part = base + 2 * round_up(mr * 4, 256);
+  if (M > 0 && !u) {
+    if (qn::launch_skinny(x, M, K, A, true, r, 1.0f, u32, nullptr, nullptr, s) != hipSuccess)
+      return QN_ERR_HIP;
+  }
+  if (M > 0 && !t) {
+    if (qn::launch_skinny(dy, M, N, B, false, r, 1.0f, t32, nullptr, nullptr, s) != hipSuccess)
+      return QN_ERR_HIP;
+  }
+  return hip_status(qn::launch_grads_impl(x, dy, u ? static_cast<const void*>(u) : u32, u != nullptr,
+                                          t ? static_cast<const void*>(t) : t32, t != nullptr, M,
+                                          N, K, r, scale, dA, dB, part, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Host-side launch functions, one per kernel family.  The C ABI in
+// qn_api.cpp validates arguments and then calls these; each returns the
+// hipError_t of its launch(es).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qn {
+
+struct WeightView {
+  const uint8_t* packed;
+  const uint8_t* qscale;  // nullptr: not double-quantised
+  const float* gscale;
+  const float* absmax;
+  int64_t N, K;
+};
+
+hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* packed,
+                           float* absmax, hipStream_t s);
+hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
+                     hipStream_t s);
+hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s);
+
+// out[M, r] = in[M, L] * P^T where P is [r, L] row-major (p_is_rl) or the
+// transpose of a row-major [L, r] matrix.  Writes any of: fp32 result,
+// bf16(scale * result), bf16(result).
+hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P,
+                         bool p_is_rl, int r, float scale, float* out_f32,
+                         uint16_t* out_scaled_bf16, uint16_t* out_bf16, hipStream_t s);
+
+// Decode path (M <= 16): y = x W^T + s u B^T with u given in fp32.
+hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const float* u,
+                       const uint16_t* B, int r, float s, uint16_t* y, hipStream_t st);
+
+// Fused dequant GEMM, forward: y[M,N] = x W^T + us B^T (us = bf16(s*u), [M, r]).
+hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
+                           const uint16_t* us, const uint16_t* B, int r, uint16_t* y,
+                           hipStream_t st);
+
+// Fused dequant GEMM, backward to the input: dx[M,K] = dy W + ts A.
+hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
+                           const uint16_t* ts, const uint16_t* A, int r, uint16_t* dx,
+                           hipStream_t st);
+
+// LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
+// fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.
+size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
+hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const void* u, bool u_bf16,
+                             const void* t, bool t_bf16, int64_t M, int64_t N, int64_t K,
+                             int r, float s, float* dA, float* dB, void* ws, hipStream_t st);
+
+}  // namespace qn

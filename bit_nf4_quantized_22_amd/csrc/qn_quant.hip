@@ -1,0 +1,259 @@
+// Blockwise NF4 quantisation, double quantisation of the block constants,
+// and dequantisation (gfx950).
+//
+// [rkmt "QLORA技术解析" §2.2.1-2.2.2] blocks of 64 weights, one fp32 constant
+// per block, nearest NF4 code per weight; second quantisation of the
+// constants to 8 bits.  [kwkr "QLoRA原理深入" §2.3, §3.1] 4-bit storage,
+// dequantised for compute; block size 64; 8-bit constants.
+//
+// All three kernels are HBM-streaming: one pass over the input, one write
+// of the output, 16-byte vector loads and stores, no re-reads.
+
+#include "qn_device.h"
+#include "qn_launch.h"
+
+namespace qn {
+
+namespace {
+
+constexpr int kQThreads = 256;     // 4 waves
+constexpr int kQPerThread = 16;    // 16 weights per lane, 4 lanes per block of 64
+constexpr int kQPerGroup = kQThreads * kQPerThread;  // 4096 weights per workgroup
+constexpr float kDanger = 0x1p-20f;  // see the fast path below
+constexpr float kTiny = 0x1p-100f;
+
+template <bool kBf16>
+__device__ __forceinline__ void load16(const void* __restrict__ w, int64_t e0, int64_t numel,
+                                       float x[16]) {
+  if (e0 + 16 <= numel) {
+    if constexpr (kBf16) {
+      const uint4* p = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(w) + e0);
+      uint4 a = p[0], b = p[1];
+      uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[2 * i] = bf16_lo(v[i]);
+        x[2 * i + 1] = bf16_hi(v[i]);
+      }
+    } else {
+      const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(w) + e0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float4 f = p[i];
+        x[4 * i] = f.x;
+        x[4 * i + 1] = f.y;
+        x[4 * i + 2] = f.z;
+        x[4 * i + 3] = f.w;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      int64_t e = e0 + i;
+      float v = 0.0f;
+      if (e < numel) {
+        if constexpr (kBf16) v = bf16_to_f32(static_cast<const uint16_t*>(w)[e]);
+        else v = static_cast<const float*>(w)[e];
+      }
+      x[i] = v;
+    }
+  }
+}
+
+// Code of v: base + (v > thr) of v's bucket.  Exact for any fp32 v in
+// [-1, 1] because each bucket holds at most one threshold and the bucket
+// function is monotone (the host built the table with the same function).
+__device__ __forceinline__ uint32_t bucket_code(const QuantBucket* sbk, float v, float sc,
+                                                float top, float& thr) {
+  float f = fminf(fmaxf(fmaf(v, sc, sc), 0.0f), top);
+  QuantBucket e = sbk[static_cast<uint32_t>(f)];
+  thr = e.thr;
+  return e.base + (v > e.thr ? 1u : 0u);
+}
+
+// Each lane owns 16 consecutive weights; the 4 lanes of a 64-weight block
+// reduce their absmax with two cross-lane steps.  Code of a weight:
+//   fast path  q = w * rcp(c) (|q - fl32(w/c)| <= 2^-22 for |w| <= c,
+//              c >= 2^-100); the bucket lookup on q gives the code of q.
+//              It equals the code of fl32(w/c) unless a threshold lies
+//              within 2^-22 of q.  Thresholds sit >= 2^-19 inside their
+//              bucket (host-checked), so only the bucket's own threshold
+//              can; a lane whose q comes within 2^-20 of it ("danger"),
+//              or whose block constant is below 2^-100, redoes its 16
+//              weights on the exact path.
+//   exact path q = fl32(w / c) by IEEE division, then the same lookup.
+template <bool kBf16>
+__global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
+    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, QuantParams P) {
+  __shared__ QuantBucket sbk[kMaxBuckets];
+  for (uint32_t i = threadIdx.x; i < P.nbuckets; i += kQThreads) sbk[i] = P.bk[i];
+  __syncthreads();
+
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kQThreads + threadIdx.x) * kQPerThread;
+  float x[16];
+  load16<kBf16>(w, e0, numel, x);
+
+  float m = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(x[i]));
+  m = fmaxf(m, __shfl_xor(m, 1, 64));
+  m = fmaxf(m, __shfl_xor(m, 2, 64));
+  const float c = m;
+
+  const float sc = P.scale;
+  const float top = static_cast<float>(P.nbuckets - 1);
+  const float rc = c > 0.0f ? __builtin_amdgcn_rcpf(c) : 0.0f;
+  bool danger = (c > 0.0f) && (c < kTiny);
+  uint32_t code[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float thr;
+    const float q = x[i] * rc;
+    code[i] = bucket_code(sbk, q, sc, top, thr);
+    danger |= fabsf(q - thr) <= kDanger;
+  }
+  if (danger) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float thr;
+      code[i] = bucket_code(sbk, x[i] / c, sc, top, thr);
+    }
+  }
+
+  if (e0 < numel) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= ((code[2 * i] << 4) | code[2 * i + 1]) << (8 * i);
+      hi |= ((code[8 + 2 * i] << 4) | code[8 + 2 * i + 1]) << (8 * i);
+    }
+    uint8_t* dst = packed + e0 / 2;
+    if (e0 + 16 <= numel) {
+      *reinterpret_cast<uint2*>(dst) = make_uint2(lo, hi);
+    } else {
+      const int64_t nbytes = (numel - e0) / 2;  // numel is even
+      for (int64_t b = 0; b < nbytes; ++b)
+        dst[b] = static_cast<uint8_t>(((b < 4 ? lo : hi) >> (8 * (b & 3))) & 0xFF);
+    }
+    if ((threadIdx.x & 3) == 0) absmax[e0 / 64] = c;
+  }
+}
+
+// One workgroup of 256 lanes per group of 256 block constants.
+__global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restrict__ absmax,
+                                                          int64_t nblocks,
+                                                          uint8_t* __restrict__ qscale,
+                                                          float* __restrict__ gscale,
+                                                          DqParams P) {
+  __shared__ float sthr[256];
+  __shared__ float smax[4];
+  sthr[threadIdx.x] = P.thr8[threadIdx.x];
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const float c = i < nblocks ? absmax[i] : 0.0f;
+  const float wm = wave_max(c);
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  if (threadIdx.x == 0) gscale[blockIdx.x] = c2;
+  if (i < nblocks) {
+    int q = 0;
+    if (c2 > 0.0f) {
+      const float v = c / c2;  // IEEE division
+      q = static_cast<int>(fminf(fmaxf(fmaf(v, 255.0f, 0.5f), 0.0f), 255.0f));
+      while (q < 255 && v > sthr[q]) ++q;
+      while (q > 0 && !(v > sthr[q - 1])) --q;
+    }
+    qscale[i] = static_cast<uint8_t>(q);
+  }
+}
+
+// Each lane expands 32 codes (16 packed bytes, half a block, one constant).
+template <bool kOutBf16>
+__global__ __launch_bounds__(256) void nf4_dequant_kernel(
+    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
+    const float* __restrict__ gscale, const float* __restrict__ absmax, int64_t numel,
+    void* __restrict__ out, PairF32Params P) {
+  __shared__ float2 spair[256];
+  spair[threadIdx.x] = make_float2(P.pair[2 * threadIdx.x], P.pair[2 * threadIdx.x + 1]);
+  __syncthreads();
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 32;
+  if (e0 >= numel) return;
+  const float cs = block_scale(qscale, gscale, absmax, e0 >> 6);
+  const uint4 pk = *reinterpret_cast<const uint4*>(packed + e0 / 2);
+  const uint32_t words[4] = {pk.x, pk.y, pk.z, pk.w};
+  float v[32];
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const float2 pr = spair[(words[wi] >> (8 * b)) & 0xFF];
+      v[8 * wi + 2 * b] = __fmul_rn(pr.x, cs);
+      v[8 * wi + 2 * b + 1] = __fmul_rn(pr.y, cs);
+    }
+  }
+  if constexpr (kOutBf16) {
+    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      dst[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
+                          pack_bf16x2(v[8 * i + 4], v[8 * i + 5]),
+                          pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
+  } else {
+    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* packed,
+                           float* absmax, hipStream_t s) {
+  if (numel == 0) return hipSuccess;
+  const Tables* t = tables();
+  QuantParams P;
+  P.scale = t->bucket_scale;
+  P.nbuckets = static_cast<uint32_t>(t->nbuckets);
+  for (int i = 0; i < kMaxBuckets; ++i) P.bk[i] = t->buckets[i];
+  const int64_t groups = (numel + kQPerGroup - 1) / kQPerGroup;
+  if (bf16)
+    hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3(static_cast<uint32_t>(groups)),
+                       dim3(kQThreads), 0, s, w, numel, packed, absmax, P);
+  else
+    hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3(static_cast<uint32_t>(groups)),
+                       dim3(kQThreads), 0, s, w, numel, packed, absmax, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
+                     hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  const Tables* t = tables();
+  DqParams P;
+  for (int i = 0; i < 255; ++i) P.thr8[i] = t->thr8[i];
+  P.thr8[255] = INFINITY;
+  const int64_t groups = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(dq_quantize_kernel, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s,
+                     absmax, nblocks, qscale, gscale, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s) {
+  const int64_t numel = w.N * w.K;
+  if (numel == 0) return hipSuccess;
+  const Tables* t = tables();
+  PairF32Params P;
+  for (int i = 0; i < 512; ++i) P.pair[i] = t->pair_f32[i];
+  const int64_t groups = (numel / 32 + 255) / 256;
+  if (out_bf16)
+    hipLaunchKernelGGL(nf4_dequant_kernel<true>, dim3(static_cast<uint32_t>(groups)), dim3(256),
+                       0, s, w.packed, w.qscale, w.gscale, w.absmax, numel, out, P);
+  else
+    hipLaunchKernelGGL(nf4_dequant_kernel<false>, dim3(static_cast<uint32_t>(groups)), dim3(256),
+                       0, s, w.packed, w.qscale, w.gscale, w.absmax, numel, out, P);
+  return hipGetLastError();
+}
+
+}  // namespace qn

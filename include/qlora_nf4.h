@@ -1,0 +1,205 @@
+/*
+ * qlora_nf4.h -- C ABI of the QLoRA NF4 hot path for AMD Instinct MI355X
+ * (gfx950, CDNA4).
+ *
+ * What it computes is described on these pages (cited by title, site in
+ * brackets, and the page's own section number):
+ *   [rkmt] "QLORA技术解析：4-bit量化与LoRA结合，单卡微调百亿大模型" (rkmt.cn)
+ *   [czcl] "QLoRA技術解析：4-bit量化與高效微調實戰" (czchanglian.com)
+ *   [tgd]  "QLoRA微调" (theguodong.com)
+ *   [kwkr] "【79.PythonAI】QLoRA原理深入：4-bit量化+LoRA，24G显存也能微调7B模型" (kwkr.cn)
+ *
+ * General rules for every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller, unless a
+ *     function says "host".  Tensors are dense, row-major, and 16-byte
+ *     aligned.  The library never keeps a pointer after a call returns.
+ *   - Every device call is asynchronous on `stream` (a hipStream_t passed
+ *     as void*; NULL means the default stream).  No call synchronises.
+ *   - Every call returns an int status: QN_OK (0) or a negative QN_ERR_*.
+ *     Argument errors are found on the host before anything is launched;
+ *     when one is returned nothing was launched and no output was touched.
+ *     QN_ERR_HIP means a launch failed (hipGetLastError after the launch);
+ *     outputs are then undefined.  No C++ exception crosses the ABI.
+ *   - The library allocates no device memory.  Scratch space comes from a
+ *     caller-provided workspace sized by qn_workspace_bytes().
+ *   - Inputs must be finite.  NaN or Inf in a weight or activation gives
+ *     undefined (but memory-safe) results.
+ *   - Calls are thread-safe; the only global state is a read-only table
+ *     built once on first use.
+ *   - Only block size 64 and double-quantisation group 256 are built; other
+ *     values return QN_ERR_UNSUPPORTED.  fp16 compute is not offered: the
+ *     pages require bf16 ([rkmt] §3.2, [kwkr] §4.1).
+ */
+#ifndef QLORA_NF4_H
+#define QLORA_NF4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define QN_API __attribute__((visibility("default")))
+#else
+#define QN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define QN_OK                0
+#define QN_ERR_NULL         -1  /* a required pointer is NULL              */
+#define QN_ERR_SHAPE        -2  /* a size is negative, odd or inconsistent */
+#define QN_ERR_ALIGN        -3  /* a pointer is not 16-byte aligned        */
+#define QN_ERR_UNSUPPORTED  -4  /* valid request this build does not offer */
+#define QN_ERR_WORKSPACE    -5  /* workspace missing or too small          */
+#define QN_ERR_HIP          -6  /* a HIP launch failed                      */
+
+/* element types */
+#define QN_F32   0
+#define QN_BF16  1
+
+/* operation ids for qn_workspace_bytes */
+#define QN_OP_FWD         0
+#define QN_OP_BWD_DX      1
+#define QN_OP_LORA_GRADS  2
+
+typedef uint16_t qn_bf16; /* bf16 bit pattern */
+
+/*
+ * A quantised weight W[N, K] (N = out_features, K = in_features).
+ *   packed  uint8[N*K/2]: 4-bit codes of the row-major flattening of W, two
+ *           per byte, the even element in the high nibble.
+ *   qscale  uint8[N*K/64]: 8-bit code of each block constant, or NULL when
+ *           the weight is not double-quantised.
+ *   gscale  fp32[ceil((N*K/64)/256)]: one constant per 256 blocks; required
+ *           iff qscale != NULL.
+ *   absmax  fp32[N*K/64]: the block constants themselves; used iff
+ *           qscale == NULL.
+ *   blocksize must be 64 and group 256.  The linear ops need K % 64 == 0 and
+ *   N % 64 == 0, so a block never crosses a row.
+ */
+typedef struct qn_weight {
+  const uint8_t* packed;
+  const uint8_t* qscale;
+  const float* gscale;
+  const float* absmax;
+  int64_t N;
+  int64_t K;
+  int32_t blocksize;
+  int32_t group;
+} qn_weight;
+
+/* Human-readable text for a status code (static storage, never NULL). */
+QN_API const char* qn_status_string(int status);
+
+/*
+ * nf4_codebook -- HOST function.  Writes the 16 NF4 code points (ascending,
+ * fp32) to out[16].
+ * [kwkr] §2.2: the codes are standard-normal quantiles, dense near zero and
+ * sparse in the tails; [rkmt] §2.2.1: quantiles of a truncated normal that
+ * split the area into equal parts; [czcl] §2.1: zero is represented exactly.
+ * Built in fp64 as 7 negative quantiles, 0 and 8 positive quantiles of the
+ * normal truncated at probability 1 - (1/32 + 1/30)/2, divided by the
+ * largest, then rounded to fp32: out[0] = -1, out[7] = +0, out[15] = +1.
+ * Returns QN_ERR_NULL if out is NULL.
+ */
+QN_API int nf4_codebook(float out[16]);
+
+/*
+ * nf4_quantize -- blockwise absmax NF4 quantisation of numel weights.
+ * [rkmt] §2.2.1-2.2.2, [kwkr] §3.1: blocks of 64 weights, one fp32 constant
+ * (the block's max |w|) each, every weight normalised by it and mapped to
+ * the nearest code point; only the 4-bit index is stored.
+ *   w        device, numel elements of type dtype (QN_F32 or QN_BF16), the
+ *            row-major flattening of the weight.
+ *   numel    even, >= 0; the last block may be partial.
+ *   packed   device uint8[numel/2] out.
+ *   absmax   device fp32[ceil(numel/blocksize)] out.
+ * Code of w: nearest code to fl32(w / absmax) (IEEE fp32 division), ties to
+ * the lower code; an all-zero block stores code 7 (exact zero).  Results
+ * are bit-identical on every run and on every device.
+ */
+QN_API int nf4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+                 uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * dq_quantize_scales -- double quantisation of the block constants.
+ * [rkmt] §2.2.2, [kwkr] §3.1, [tgd] §2: the fp32 block constants are
+ * quantised again to 8 bits, with fp32 constants for that second level,
+ * saving about 0.37 bit per weight.
+ *   absmax   device fp32[nblocks] in (non-negative, finite).
+ *   qscale   device uint8[nblocks] out: nearest level of fl32(q/255),
+ *            q = 0..255, to fl32(absmax / gscale), ties to the lower code.
+ *   gscale   device fp32[ceil(nblocks/group)] out: max of each group of 256.
+ */
+QN_API int dq_quantize_scales(const float* absmax, int64_t nblocks, int32_t group,
+                       uint8_t* qscale, float* gscale, void* stream);
+
+/*
+ * nf4_dequant -- materialise the weight.
+ * [rkmt] §2.2.1: look the 4-bit index up in the code table and scale it;
+ * [kwkr] §2.3: the 16-bit copy is a compute-time value.
+ *   out      device [N, K] of out_dtype (QN_F32 or QN_BF16).
+ * Value: c' = fl32(fl32(q/255) * gscale) (or absmax when not
+ * double-quantised), w = fl32(code_value * c'); bf16 output is the RNE of
+ * that fp32.  Bit-identical to the definition, including -0.0.
+ */
+QN_API int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * qn_workspace_bytes -- HOST function.  Bytes of device workspace that op
+ * (QN_OP_FWD, QN_OP_BWD_DX or QN_OP_LORA_GRADS) needs for these sizes.
+ * Returns 0 for invalid arguments.
+ */
+QN_API size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
+
+/*
+ * qlora_linear_fwd -- y = x * dequant(W)^T + (alpha/r) * (x * A^T) * B^T.
+ * [kwkr] §2.3: the 4-bit weight is expanded to 16 bits for the product and
+ * never stored back; [rkmt] §2.1 and §3.3: LoRA bypass B*A scaled by
+ * alpha/r.  bf16 operands, fp32 accumulation, bf16 output.
+ *   x      device bf16[M, K];  A bf16[r, K];  B bf16[N, r].
+ *   y      device bf16[M, N] out.
+ *   u_out  device bf16[M, r] out (x * A^T, kept for the backward), or NULL.
+ *   r      0 (frozen layer: A, B ignored) or 1..128.
+ *   ws     device workspace of ws_bytes >= qn_workspace_bytes(QN_OP_FWD,..).
+ */
+QN_API int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M,
+                     const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,
+                     qn_bf16* y, qn_bf16* u_out, void* ws, size_t ws_bytes,
+                     void* stream);
+
+/*
+ * qlora_linear_bwd_dx -- dx = dy * dequant(W) + (alpha/r) * (dy * B) * A.
+ * [kwkr] §2.3: the gradient flows through the frozen 4-bit weight to the
+ * input and into the LoRA bypass only.
+ *   dy     device bf16[M, N];  dx device bf16[M, K] out.
+ *   t_out  device bf16[M, r] out (dy * B), or NULL.
+ */
+QN_API int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M,
+                        const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,
+                        qn_bf16* dx, qn_bf16* t_out, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * lora_grads -- dA = (alpha/r) (dy B)^T x,  dB = (alpha/r) dy^T (x A^T).
+ * [kwkr] §2.3: only the LoRA matrices receive gradients; the 4-bit weight
+ * and its constants get none.
+ *   x bf16[M, K], dy bf16[M, N], A bf16[r, K], B bf16[N, r] (device).
+ *   u bf16[M, r] (x A^T from the forward) or NULL to recompute it in fp32;
+ *   t bf16[M, r] (dy B from the backward) or NULL to recompute it.
+ *   dA fp32[r, K] and dB fp32[N, r] out (overwritten, not accumulated).
+ *   r must be 1..128.  The reduction over M is split into fixed chunks and
+ *   summed in a fixed order, so results are bit-reproducible.
+ */
+QN_API int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u,
+               const qn_bf16* t, const qn_bf16* A, const qn_bf16* B,
+               int64_t M, int64_t N, int64_t K, int32_t r, float alpha,
+               float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLORA_NF4_H */

@@ -16,3 +16,13 @@ def pytest_configure(config):
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Print (unbuffered, uncaptured) the name of every GPU case before it
+    touches the device, so a run that dies mid-test still names its case."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield
