@@ -28,9 +28,9 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hi
          "-I", os.path.join(ROOT, "include"), "-I", CSRC]
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, extra=(), build_dir=BUILD):
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     errs = "\n".join(l for l in p.stderr.splitlines()
                      if "packed-fp32-ops" not in l)  # host pass does not know the feature
@@ -39,20 +39,21 @@ def _compile(src):
     return obj
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+def build(verbose=False, extra_flags=(), lib_path=LIB, build_dir=BUILD):
+    """Compile and link; extra_flags / lib_path / build_dir allow side builds."""
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib_path), exist_ok=True)
     with ThreadPoolExecutor(max_workers=min(6, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, extra_flags, build_dir), SOURCES))
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib_path}")
+    return lib_path
 
 
 if __name__ == "__main__":

@@ -50,10 +50,17 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   return QN_OK;
 }
 
+// Forward workspace: fp32 u (up to 16 partial sums of it on the decode
+// path) followed by bf16(s u).
+size_t fwd_u32_bytes(int64_t M, int32_t r) {
+  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+  return round_up(mr * 4 * (M <= kGemvMaxM ? 16 : 1), 256);
+}
+
 size_t fwd_ws(int64_t M, int32_t r) {
   if (r == 0 || M == 0) return 0;
   const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  return round_up(mr * 4, 256) + round_up(mr * 2, 256);
+  return fwd_u32_bytes(M, r) + round_up(mr * 2, 256);
 }
 
 size_t bwd_ws(int64_t M, int32_t r) {
@@ -163,16 +170,20 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   float* u32 = nullptr;
   uint16_t* us = nullptr;
+  const bool decode = M <= kGemvMaxM;
+  const int ks = decode ? qn::skinny_splits(M, w->K, r) : 1;
   if (r > 0) {
-    const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
     u32 = static_cast<float*>(ws);
-    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round_up(mr * 4, 256));
-    hipError_t e = qn::launch_skinny(x, M, w->K, A, true, r, scale, M <= kGemvMaxM ? u32 : nullptr,
-                                     M <= kGemvMaxM ? nullptr : us, u_out, s);
+    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fwd_u32_bytes(M, r));
+    hipError_t e = decode ? qn::launch_skinny(x, M, w->K, A, true, r, scale, u32, nullptr, nullptr,
+                                              ks, s)
+                          : qn::launch_skinny(x, M, w->K, A, true, r, scale, nullptr, us, u_out,
+                                              1, s);
     if (e != hipSuccess) return QN_ERR_HIP;
   }
-  if (M <= kGemvMaxM)
-    return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, B, r, scale, y, s));
+  if (decode)
+    return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, ks, B, r, scale, y,
+                                      r > 0 ? u_out : nullptr, s));
   return hip_status(qn::launch_gemm_fwd(v, x, M, us, B, r, y, s));
 }
 
@@ -199,7 +210,7 @@ int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const 
   uint16_t* ts = nullptr;
   if (r > 0) {
     ts = static_cast<uint16_t*>(ws);
-    hipError_t e = qn::launch_skinny(dy, M, w->N, B, false, r, scale, nullptr, ts, t_out, s);
+    hipError_t e = qn::launch_skinny(dy, M, w->N, B, false, r, scale, nullptr, ts, t_out, 1, s);
     if (e != hipSuccess) return QN_ERR_HIP;
   }
   return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
@@ -231,11 +242,11 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   float* t32 = reinterpret_cast<float*>(base + round_up(mr * 4, 256));
   void* part = base + 2 * round_up(mr * 4, 256);
   if (M > 0 && !u) {
-    if (qn::launch_skinny(x, M, K, A, true, r, 1.0f, u32, nullptr, nullptr, s) != hipSuccess)
+    if (qn::launch_skinny(x, M, K, A, true, r, 1.0f, u32, nullptr, nullptr, 1, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   if (M > 0 && !t) {
-    if (qn::launch_skinny(dy, M, N, B, false, r, 1.0f, t32, nullptr, nullptr, s) != hipSuccess)
+    if (qn::launch_skinny(dy, M, N, B, false, r, 1.0f, t32, nullptr, nullptr, 1, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   return hip_status(qn::launch_grads_impl(x, dy, u ? static_cast<const void*>(u) : u32, u != nullptr,

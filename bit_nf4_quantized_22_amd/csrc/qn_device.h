@@ -51,23 +51,47 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// Kernel parameter blocks (passed by value, copied to LDS by each workgroup).
+// Kernel parameters.  Tables are never indexed per lane out of the kernel
+// argument segment (that becomes a vector load per lane at the start of
+// every workgroup); each kernel builds its LDS tables from a few scalars
+// read with wave-uniform indices.
+
+// The 16 NF4 code values (fp32, ascending).
+struct CodeParams {
+  float q[16];
+};
+
+// q[c] for a per-lane code c: a select over the 16 uniform values.
+__device__ __forceinline__ float code_value(const CodeParams& P, uint32_t c) {
+  float v = P.q[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) v = (c == static_cast<uint32_t>(i)) ? P.q[i] : v;
+  return v;
+}
+
+// LDS byte table, `copies` interleaved copies: entry e of copy k at
+// e * copies + k holds (q[e >> 4], q[e & 15]) (even element first).
+__device__ __forceinline__ void fill_pair_f32(float2* tab, const CodeParams& P, int copies) {
+  for (int i = threadIdx.x; i < 256 * copies; i += blockDim.x) {
+    const uint32_t e = i / copies;
+    tab[i] = make_float2(code_value(P, e >> 4), code_value(P, e & 15));
+  }
+}
+
+// Same, as packed bf16 pairs (RNE), low half = even element.
+__device__ __forceinline__ void fill_pair_bf16(uint32_t* tab, const CodeParams& P, int copies) {
+  for (int i = threadIdx.x; i < 256 * copies; i += blockDim.x) {
+    const uint32_t e = i / copies;
+    tab[i] = pack_bf16x2(code_value(P, e >> 4), code_value(P, e & 15));
+  }
+}
+
+// Quantiser: bucket scale, bucket count and the 15 fp32 decision
+// thresholds; the bucket table itself is rebuilt in LDS by each workgroup.
 struct QuantParams {
   float scale;
   uint32_t nbuckets;
-  QuantBucket bk[kMaxBuckets];
-};
-
-struct DqParams {
-  float thr8[256];  // thr8[255] = +inf sentinel
-};
-
-struct PairF32Params {
-  float pair[512];
-};
-
-struct PairBf16Params {
-  uint32_t pair[256];
+  float thr[15];
 };
 
 }  // namespace qn

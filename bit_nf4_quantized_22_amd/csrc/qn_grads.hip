@@ -49,12 +49,20 @@ __global__ __launch_bounds__(256) void grads_partial_kernel(const uint16_t* __re
       sT[mm][j] = (mb + mm < mend && j < r) ? ld_narrow(Tn, (mb + mm) * r + j) : 0.f;
     }
     __syncthreads();
-    const int rows = (mend - mb < kRows) ? static_cast<int>(mend - mb) : kRows;
+    // Rows past mend have sT == 0; their loads are clamped to a valid row.
     if (col < C) {
-      for (int mm = 0; mm < rows; ++mm) {
-        const float xv = bf16_to_f32(X[(mb + mm) * C + col]);
+#pragma unroll 1
+      for (int mm = 0; mm < kRows; mm += 8) {
+        float xv[8];
 #pragma unroll
-        for (int j = 0; j < RT; ++j) acc[j] = fmaf(sT[mm][j], xv, acc[j]);
+        for (int q = 0; q < 8; ++q) {
+          const int64_t row = min(mb + mm + q, mend - 1);
+          xv[q] = bf16_to_f32(X[row * C + col]);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int j = 0; j < RT; ++j) acc[j] = fmaf(sT[mm + q][j], xv[q], acc[j]);
       }
     }
     __syncthreads();

@@ -23,15 +23,21 @@ hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, floa
 hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s);
 
 // out[M, r] = in[M, L] * P^T where P is [r, L] row-major (p_is_rl) or the
-// transpose of a row-major [L, r] matrix.  Writes any of: fp32 result,
-// bf16(scale * result), bf16(result).
+// transpose of a row-major [L, r] matrix.  ksplit == 1 writes any of: fp32
+// result, bf16(scale * result), bf16(result); ksplit > 1 splits L over
+// ksplit workgroups and writes fp32 partial sums out_f32[ksplit][M][r].
 hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P,
                          bool p_is_rl, int r, float scale, float* out_f32,
-                         uint16_t* out_scaled_bf16, uint16_t* out_bf16, hipStream_t s);
+                         uint16_t* out_scaled_bf16, uint16_t* out_bf16, int ksplit,
+                         hipStream_t s);
+// Number of L-slices launch_skinny uses for the decode path (M <= 16).
+int skinny_splits(int64_t M, int64_t L, int r);
 
-// Decode path (M <= 16): y = x W^T + s u B^T with u given in fp32.
-hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const float* u,
-                       const uint16_t* B, int r, float s, uint16_t* y, hipStream_t st);
+// Decode path (M <= 16): y = x W^T + s u B^T with u given as usplit fp32
+// partial sums [usplit][M][r]; optionally writes bf16(u) to u_out.
+hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const float* u, int usplit,
+                       const uint16_t* B, int r, float s, uint16_t* y, uint16_t* u_out,
+                       hipStream_t st);
 
 // Fused dequant GEMM, forward: y[M,N] = x W^T + us B^T (us = bf16(s*u), [M, r]).
 hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,

@@ -87,7 +87,24 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
     const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
     float* __restrict__ absmax, QuantParams P) {
   __shared__ QuantBucket sbk[kMaxBuckets];
-  for (uint32_t i = threadIdx.x; i < P.nbuckets; i += kQThreads) sbk[i] = P.bk[i];
+  const float sc = P.scale;
+  const float top = static_cast<float>(P.nbuckets - 1);
+  // Bucket table: bucket b holds the threshold whose bucket is b (if any)
+  // and counts the thresholds in lower buckets (same bucket function as
+  // bucket_code; the host checked that buckets hold at most one threshold
+  // with a margin).
+  for (uint32_t b = threadIdx.x; b < P.nbuckets; b += kQThreads) {
+    uint32_t base = 0;
+    float thr = INFINITY;
+#pragma unroll
+    for (int i = 0; i < 15; ++i) {
+      const float ti = P.thr[i];
+      const uint32_t bi = static_cast<uint32_t>(fminf(fmaxf(fmaf(ti, sc, sc), 0.0f), top));
+      base += bi < b ? 1u : 0u;
+      thr = bi == b ? ti : thr;
+    }
+    sbk[b] = QuantBucket{thr, base};
+  }
   __syncthreads();
 
   const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kQThreads + threadIdx.x) * kQPerThread;
@@ -101,8 +118,6 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
   m = fmaxf(m, __shfl_xor(m, 2, 64));
   const float c = m;
 
-  const float sc = P.scale;
-  const float top = static_cast<float>(P.nbuckets - 1);
   const float rc = c > 0.0f ? __builtin_amdgcn_rcpf(c) : 0.0f;
   bool danger = (c > 0.0f) && (c < kTiny);
   uint32_t code[16];
@@ -144,11 +159,21 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
 __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restrict__ absmax,
                                                           int64_t nblocks,
                                                           uint8_t* __restrict__ qscale,
-                                                          float* __restrict__ gscale,
-                                                          DqParams P) {
+                                                          float* __restrict__ gscale) {
   __shared__ float sthr[256];
   __shared__ float smax[4];
-  sthr[threadIdx.x] = P.thr8[threadIdx.x];
+  // Decision thresholds of the 8-bit grid: the largest fp32 <= the fp64
+  // mid-point of adjacent levels fl32(j / 255) (exact in fp64); +inf last.
+  {
+    const int j = threadIdx.x;
+    float thr = INFINITY;
+    if (j < 255) {
+      const double m = (static_cast<double>(l8_value(j)) + static_cast<double>(l8_value(j + 1))) * 0.5;
+      thr = static_cast<float>(m);
+      if (static_cast<double>(thr) > m) thr = nextafterf(thr, -INFINITY);
+    }
+    sthr[j] = thr;
+  }
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const float c = i < nblocks ? absmax[i] : 0.0f;
   const float wm = wave_max(c);
@@ -173,9 +198,9 @@ template <bool kOutBf16>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ gscale, const float* __restrict__ absmax, int64_t numel,
-    void* __restrict__ out, PairF32Params P) {
+    void* __restrict__ out, CodeParams P) {
   __shared__ float2 spair[256];
-  spair[threadIdx.x] = make_float2(P.pair[2 * threadIdx.x], P.pair[2 * threadIdx.x + 1]);
+  fill_pair_f32(spair, P, 1);
   __syncthreads();
   const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 32;
   if (e0 >= numel) return;
@@ -216,7 +241,7 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* pac
   QuantParams P;
   P.scale = t->bucket_scale;
   P.nbuckets = static_cast<uint32_t>(t->nbuckets);
-  for (int i = 0; i < kMaxBuckets; ++i) P.bk[i] = t->buckets[i];
+  for (int i = 0; i < 15; ++i) P.thr[i] = t->thr[i];
   const int64_t groups = (numel + kQPerGroup - 1) / kQPerGroup;
   if (bf16)
     hipLaunchKernelGGL(nf4_quantize_kernel<true>, dim3(static_cast<uint32_t>(groups)),
@@ -230,13 +255,9 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* pac
 hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
                      hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
-  const Tables* t = tables();
-  DqParams P;
-  for (int i = 0; i < 255; ++i) P.thr8[i] = t->thr8[i];
-  P.thr8[255] = INFINITY;
   const int64_t groups = (nblocks + 255) / 256;
   hipLaunchKernelGGL(dq_quantize_kernel, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s,
-                     absmax, nblocks, qscale, gscale, P);
+                     absmax, nblocks, qscale, gscale);
   return hipGetLastError();
 }
 
@@ -244,8 +265,8 @@ hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStre
   const int64_t numel = w.N * w.K;
   if (numel == 0) return hipSuccess;
   const Tables* t = tables();
-  PairF32Params P;
-  for (int i = 0; i < 512; ++i) P.pair[i] = t->pair_f32[i];
+  CodeParams P;
+  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
   const int64_t groups = (numel / 32 + 255) / 256;
   if (out_bf16)
     hipLaunchKernelGGL(nf4_dequant_kernel<true>, dim3(static_cast<uint32_t>(groups)), dim3(256),
