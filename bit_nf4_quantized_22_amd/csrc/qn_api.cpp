@@ -63,15 +63,23 @@ size_t fwd_ws(int64_t M, int32_t r) {
   return fwd_u32_bytes(M, r) + round_up(mr * 2, 256);
 }
 
-size_t bwd_ws(int64_t M, int32_t r) {
-  if (r == 0 || M == 0) return 0;
-  return round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256);
+// B^T [r, N] bf16: the row-major operand of t = dy B.
+size_t bt_bytes(int64_t N, int32_t r) {
+  return round_up(static_cast<size_t>(N) * static_cast<size_t>(r) * 2, 256);
 }
 
+// Backward workspace: bf16(s t) followed by B^T.
+size_t bwd_ws(int64_t M, int64_t N, int32_t r) {
+  if (r == 0 || M == 0) return 0;
+  return round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256) + bt_bytes(N, r);
+}
+
+// Gradient workspace: fp32 u, fp32 t, B^T, split-M partial sums.
 size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (r == 0) return 0;
   const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  return 2 * round_up(mr * 4, 256) + round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
+  return 2 * round_up(mr * 4, 256) + bt_bytes(N, r) +
+         round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
 }
 
 }  // namespace
@@ -142,7 +150,7 @@ size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
   if (M < 0 || N < 0 || K < 0 || r < 0 || r > kMaxRank) return 0;
   switch (op) {
     case QN_OP_FWD: return fwd_ws(M, r);
-    case QN_OP_BWD_DX: return bwd_ws(M, r);
+    case QN_OP_BWD_DX: return bwd_ws(M, N, r);
     case QN_OP_LORA_GRADS: return grads_ws(M, N, K, r);
     default: return 0;
   }
@@ -175,10 +183,8 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
   if (r > 0) {
     u32 = static_cast<float*>(ws);
     us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fwd_u32_bytes(M, r));
-    hipError_t e = decode ? qn::launch_skinny(x, M, w->K, A, true, r, scale, u32, nullptr, nullptr,
-                                              ks, s)
-                          : qn::launch_skinny(x, M, w->K, A, true, r, scale, nullptr, us, u_out,
-                                              1, s);
+    hipError_t e = decode ? qn::launch_skinny(x, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s)
+                          : qn::launch_skinny(x, M, w->K, A, r, scale, nullptr, us, u_out, 1, s);
     if (e != hipSuccess) return QN_ERR_HIP;
   }
   if (decode)
@@ -200,7 +206,7 @@ int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const 
   if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
       (t_out && !aligned(t_out, 2)))
     return QN_ERR_ALIGN;
-  const size_t need = bwd_ws(M, r);
+  const size_t need = bwd_ws(M, w->N, r);
   if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
   if (!qn::tables()) return QN_ERR_UNSUPPORTED;
@@ -210,7 +216,10 @@ int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const 
   uint16_t* ts = nullptr;
   if (r > 0) {
     ts = static_cast<uint16_t*>(ws);
-    hipError_t e = qn::launch_skinny(dy, M, w->N, B, false, r, scale, nullptr, ts, t_out, 1, s);
+    uint16_t* bt = reinterpret_cast<uint16_t*>(
+        static_cast<char*>(ws) + round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256));
+    if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
+    hipError_t e = qn::launch_skinny(dy, M, w->N, bt, r, scale, nullptr, ts, t_out, 1, s);
     if (e != hipSuccess) return QN_ERR_HIP;
   }
   return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
@@ -240,13 +249,15 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   char* base = static_cast<char*>(ws);
   float* u32 = reinterpret_cast<float*>(base);
   float* t32 = reinterpret_cast<float*>(base + round_up(mr * 4, 256));
-  void* part = base + 2 * round_up(mr * 4, 256);
+  uint16_t* bt = reinterpret_cast<uint16_t*>(base + 2 * round_up(mr * 4, 256));
+  void* part = base + 2 * round_up(mr * 4, 256) + bt_bytes(N, r);
   if (M > 0 && !u) {
-    if (qn::launch_skinny(x, M, K, A, true, r, 1.0f, u32, nullptr, nullptr, 1, s) != hipSuccess)
+    if (qn::launch_skinny(x, M, K, A, r, 1.0f, u32, nullptr, nullptr, 1, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   if (M > 0 && !t) {
-    if (qn::launch_skinny(dy, M, N, B, false, r, 1.0f, t32, nullptr, nullptr, 1, s) != hipSuccess)
+    if (qn::launch_transpose(B, N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
+    if (qn::launch_skinny(dy, M, N, bt, r, 1.0f, t32, nullptr, nullptr, 1, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   return hip_status(qn::launch_grads_impl(x, dy, u ? static_cast<const void*>(u) : u32, u != nullptr,

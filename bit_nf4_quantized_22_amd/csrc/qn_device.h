@@ -61,28 +61,43 @@ struct CodeParams {
   float q[16];
 };
 
-// q[c] for a per-lane code c: a select over the 16 uniform values.
-__device__ __forceinline__ float code_value(const CodeParams& P, uint32_t c) {
-  float v = P.q[0];
+// The 16 code values spread over lanes 0..15 of one VGPR (v_writelane of
+// the scalar kernel arguments).  q[c] for a per-lane c is then a
+// ds_bpermute from lane c: no memory access and no per-lane select, which
+// the compiler would otherwise turn back into an indexed load from the
+// argument segment or a scratch array.
+struct CodeRegs {
+  int lanes;
+};
+
+__device__ __forceinline__ CodeRegs code_regs(const CodeParams& P) {
+  int v = 0;
 #pragma unroll
-  for (int i = 1; i < 16; ++i) v = (c == static_cast<uint32_t>(i)) ? P.q[i] : v;
-  return v;
+  for (int i = 0; i < 16; ++i)
+    asm volatile("v_writelane_b32 %0, %1, %2" : "+v"(v) : "s"(__float_as_int(P.q[i])), "n"(i));
+  return CodeRegs{v};
+}
+
+__device__ __forceinline__ float code_value(const CodeRegs& R, uint32_t c) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(c << 2), R.lanes));
 }
 
 // LDS byte table, `copies` interleaved copies: entry e of copy k at
 // e * copies + k holds (q[e >> 4], q[e & 15]) (even element first).
 __device__ __forceinline__ void fill_pair_f32(float2* tab, const CodeParams& P, int copies) {
+  const CodeRegs R = code_regs(P);
   for (int i = threadIdx.x; i < 256 * copies; i += blockDim.x) {
     const uint32_t e = i / copies;
-    tab[i] = make_float2(code_value(P, e >> 4), code_value(P, e & 15));
+    tab[i] = make_float2(code_value(R, e >> 4), code_value(R, e & 15));
   }
 }
 
 // Same, as packed bf16 pairs (RNE), low half = even element.
 __device__ __forceinline__ void fill_pair_bf16(uint32_t* tab, const CodeParams& P, int copies) {
+  const CodeRegs R = code_regs(P);
   for (int i = threadIdx.x; i < 256 * copies; i += blockDim.x) {
     const uint32_t e = i / copies;
-    tab[i] = pack_bf16x2(code_value(P, e >> 4), code_value(P, e & 15));
+    tab[i] = pack_bf16x2(code_value(R, e >> 4), code_value(R, e & 15));
   }
 }
 

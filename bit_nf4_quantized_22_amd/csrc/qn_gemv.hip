@@ -6,17 +6,21 @@
 // scaled by alpha / r.
 //
 // GEMV design: the weight stream (0.516 byte per weight) is the only HBM
-// traffic that matters.  The 16x16x32 bf16 MFMA does the multiply-adds
-// (VALU would need 16 FMAs per weight at M = 16); the weight operand is the
-// *unscaled* code value bf16(q[code]) looked up two codes at a time from a
-// 256-entry byte table in LDS, and the block constant c' is applied once per
-// 64-weight block to the fp32 partial sum (4 FMAs per lane per block).  Every
-// MFMA therefore covers the 16 rows x 32 k-slots of one block: lane
-// (n = l%16, g = l/16) holds codes k = 64b + 16g + [0, 16) of row n (one
-// 8-byte load), and the two MFMAs of a block take the first and second 8 of
-// them; the x operand uses the same k-slot map.  Each wave works through
-// groups of 4 consecutive blocks and issues the loads of its next group
-// before computing the current one.
+// traffic that matters, and at 4096 x 4096 the whole matrix is about one
+// memory latency's worth of bytes for the chip, so the kernel is built to
+// put every weight byte in flight at once and to serialise nothing behind
+// it.  The 16x16x32 bf16 MFMA does the multiply-adds (VALU would need 16
+// FMAs per weight at M = 16); the weight operand is the *unscaled* code
+// value bf16(q[code]) looked up two codes at a time from a 256-entry byte
+// table in LDS, and the block constant c' is applied once per 64-weight
+// block to the fp32 partial sum.  Every MFMA covers 16 rows x 32 k-slots of
+// one block: lane (n = l%16, g = l/16) holds codes k = 64b + 16g + [0, 16)
+// of row n (one 8-byte load), the two MFMAs of a block take the first and
+// second 8 of them, and the x operand uses the same k-slot map.
+//
+// The byte table has 32 copies, lane l reading copy l % 32, so the random
+// lookups of a wave spread over all LDS banks (a single shared copy halves
+// the lookup rate on gfx950).
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -25,271 +29,500 @@ namespace qn {
 
 namespace {
 
-constexpr int kGemvWaves = 8;
-constexpr int kUParts = 16;  // LoRA partial sums held per thread in the GEMV
-constexpr int kPairCopies = 8;  // lane l uses copy l % 8 (fewer LDS bank conflicts)
+constexpr int kUParts = 8;   // LoRA partial sums held per thread in the GEMV
+constexpr int kXAhead = 3;   // x prefetch distance, in blocks (register ring)
+constexpr int kXMaxM = 4;    // token rows staged in LDS instead (M <= 4)
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// out[M, r] = in[M, L] * P^T.  Grid: (16-row tiles of `in`) x ksplit; the 4
-// waves of a workgroup split its L-slice in 32-wide chunks; MFMA 16x16x32
-// with in-rows as the M side and up to 8 column tiles of 16 (r <= 128).
+// ---------------------------------------------------------------------------
+// Skinny projection out[M, r] = in[M, L] * P^T, P row-major [r, L].
+//
+// Grid: (16-row tiles of `in`) x ksplit L-slices; kWaves waves per workgroup
+// split the slice in 32-wide chunks, wave w taking chunks w, w + kWaves, ...
+// Each round a wave issues the loads of kCh chunks (x: one 16-byte load per
+// lane per chunk; P: one per lane per 16-column tile) before any MFMA, so a
+// round costs one memory latency.  16x16x32 MFMA with in-rows on the M side
+// and kCols column tiles of 16 (r <= 16 kCols).
 // ksplit == 1: writes the finished result (fp32 and/or bf16 forms).
 // ksplit > 1: writes fp32 partial sums out_f32[slice][M][r].
-template <bool kPRowMajor>
-__global__ __launch_bounds__(256) void skinny_kernel(const uint16_t* __restrict__ in, int64_t M,
-                                                     int64_t L, const uint16_t* __restrict__ P,
-                                                     int r, float scale, int ksplit,
-                                                     float* __restrict__ out_f32,
-                                                     uint16_t* __restrict__ out_sbf16,
-                                                     uint16_t* __restrict__ out_bf16) {
-  __shared__ float sred[4][8][16][17];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+template <int kCols, int kWaves>
+__global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
+    const uint16_t* __restrict__ in, int64_t M, int64_t L, const uint16_t* __restrict__ P, int r,
+    float scale, int ksplit, float* __restrict__ out_f32, uint16_t* __restrict__ out_sbf16,
+    uint16_t* __restrict__ out_bf16) {
+  constexpr int kCh = kCols >= 8 ? 1 : 8 / kCols;
+  __shared__ float sred[kWaves][16][17];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int mi = lane & 15, g = lane >> 4;
   const int64_t m = static_cast<int64_t>(blockIdx.x) * 16 + mi;
   const int64_t mc = m < M ? m : M - 1;  // clamped: rows >= M are never stored
-  const int ncol = (r + 15) >> 4;
   const int64_t nchunk = L >> 5;
   const int64_t c_lo = nchunk * blockIdx.y / ksplit, c_hi = nchunk * (blockIdx.y + 1) / ksplit;
-  f32x4_t acc[8];
+  const uint16_t* arow = in + mc * L + 8 * g;
+  // Column j = 16 c + mi of P, clamped into [0, r); columns >= r read row
+  // r - 1 and are zeroed.
+  const uint16_t* prow[kCols];
+  bool pvalid[kCols];
 #pragma unroll
-  for (int c = 0; c < 8; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < kCols; ++c) {
+    const int j = c * 16 + mi;
+    pvalid[c] = j < r;
+    prow[c] = P + static_cast<int64_t>(j < r ? j : r - 1) * L + 8 * g;
+  }
+  f32x4_t acc[kCols];
+#pragma unroll
+  for (int c = 0; c < kCols; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  for (int64_t ch = c_lo + wave; ch < c_hi; ch += 4) {
-    const int64_t kk = ch * 32 + 8 * g;
-    const uint4 a = *reinterpret_cast<const uint4*>(in + mc * L + kk);
+  // chunks of this wave: c_lo + wave + kWaves * i, i < cnt
+  const int64_t first = c_lo + wave;
+  const int64_t cnt = first < c_hi ? (c_hi - first + kWaves - 1) / kWaves : 0;
+  for (int64_t i0 = 0; i0 < cnt; i0 += kCh) {
+    uint4 a[kCh], b[kCh][kCols];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (c < ncol) {
-        const int j = c * 16 + mi;
-        uint4 b = make_uint4(0, 0, 0, 0);
-        if (j < r) {
-          if constexpr (kPRowMajor) {
-            b = *reinterpret_cast<const uint4*>(P + static_cast<int64_t>(j) * L + kk);
-          } else {
-            uint32_t e[8];
+    for (int i = 0; i < kCh; ++i) {
+      const int64_t ii = i0 + i < cnt ? i0 + i : cnt - 1;
+      const int64_t kk = (first + ii * kWaves) * 32;
+      a[i] = *reinterpret_cast<const uint4*>(arow + kk);
 #pragma unroll
-            for (int t = 0; t < 8; ++t) e[t] = P[(kk + t) * r + j];
-            b = make_uint4(e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16),
-                           e[6] | (e[7] << 16));
-          }
+      for (int c = 0; c < kCols; ++c) b[i][c] = *reinterpret_cast<const uint4*>(prow[c] + kk);
+    }
+#pragma unroll
+    for (int i = 0; i < kCh; ++i) {
+      if (i0 + i < cnt) {
+#pragma unroll
+        for (int c = 0; c < kCols; ++c) {
+          const uint4 bb = pvalid[c] ? b[i][c] : make_uint4(0, 0, 0, 0);
+          acc[c] = mfma16(a[i], bb, acc[c]);
         }
-        acc[c] = mfma16(a, b, acc[c]);
       }
     }
   }
+
+  // Cross-wave sum, one 16-column tile at a time, fixed order.
+  const int ncol = (r + 15) >> 4;
 #pragma unroll
-  for (int c = 0; c < 8; ++c)
-    if (c < ncol)
+  for (int c = 0; c < kCols; ++c) {
+    if (c < ncol) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sred[wave][c][4 * g + v][mi] = acc[c][v];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 16 * ncol * 16; idx += 256) {
-    const int row = idx / (ncol * 16), col = idx % (ncol * 16);
-    const int c = col >> 4, cj = col & 15;
-    const int64_t mm = static_cast<int64_t>(blockIdx.x) * 16 + row;
-    if (mm >= M || col >= r) continue;
-    const float v = sred[0][c][row][cj] + sred[1][c][row][cj] + sred[2][c][row][cj] +
-                    sred[3][c][row][cj];
-    const int64_t o = mm * r + col;
-    if (ksplit > 1) {
-      out_f32[static_cast<int64_t>(blockIdx.y) * M * r + o] = v;
-      continue;
+      for (int v = 0; v < 4; ++v) sred[wave][4 * g + v][mi] = acc[c][v];
+      __syncthreads();
+      for (int idx = threadIdx.x; idx < 256; idx += kWaves * 64) {
+        const int row = idx >> 4, cj = idx & 15;
+        const int col = c * 16 + cj;
+        const int64_t mm = static_cast<int64_t>(blockIdx.x) * 16 + row;
+        if (mm < M && col < r) {
+          float v = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) v += sred[w][row][cj];
+          const int64_t o = mm * r + col;
+          if (ksplit > 1) {
+            out_f32[static_cast<int64_t>(blockIdx.y) * M * r + o] = v;
+          } else {
+            if (out_f32) out_f32[o] = v;
+            if (out_sbf16) out_sbf16[o] = static_cast<uint16_t>(pack_bf16x2(scale * v, 0.f) & 0xFFFF);
+            if (out_bf16) out_bf16[o] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
+          }
+        }
+      }
+      __syncthreads();
     }
-    if (out_f32) out_f32[o] = v;
-    if (out_sbf16) out_sbf16[o] = static_cast<uint16_t>(pack_bf16x2(scale * v, 0.f) & 0xFFFF);
-    if (out_bf16) out_bf16[o] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
   }
 }
 
-// Dequant-GEMV.  One workgroup (8 waves) per band of 16 output features
-// (rows of W).  Wave w owns a contiguous slice of at most kGemvMaxBlocks
-// blocks of the band's K range (longer rows are done in several passes) and
-// issues all of its weight loads (8 bytes per lane per block) and block
-// constants at once, before anything else: the whole weight matrix is in
-// flight almost from the start, which is what an HBM-latency-bound stream
-// needs.  x is read per block, two blocks ahead.  Partial sums meet in LDS;
-// the workgroup adds the LoRA term (u as `usplit` fp32 partial sums
-// [usplit][M][r]) and writes y as bf16.
-constexpr int kGemvMaxBlocks = 24;
+// out[c][l] = in[l][c] for a row-major [L, C] bf16 matrix (C <= 128): turns
+// B [N, r] into the row-major [r, N] operand of the skinny kernel.  One
+// workgroup per 64 rows of `in`, staged through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in,
+                                                        int64_t L, int C,
+                                                        uint16_t* __restrict__ out) {
+  __shared__ uint16_t t[64][129];
+  const int64_t l0 = static_cast<int64_t>(blockIdx.x) * 64;
+  const int rows = static_cast<int>(L - l0 < 64 ? L - l0 : 64);
+  for (int idx = threadIdx.x; idx < rows * C; idx += 256) {
+    const int lr = idx / C, c = idx % C;
+    t[lr][c] = in[(l0 + lr) * C + c];
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < rows * C; idx += 256) {
+    const int c = idx / rows, lr = idx % rows;
+    out[static_cast<int64_t>(c) * L + l0 + lr] = t[lr][c];
+  }
+}
 
-template <bool kDQ>
-__global__ __launch_bounds__(kGemvWaves * 64) void gemv_kernel(
-    const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
-    const float* __restrict__ gscale, const float* __restrict__ absmax, int64_t N, int64_t K,
-    const uint16_t* __restrict__ x, int M, const float* __restrict__ u, int usplit,
-    const uint16_t* __restrict__ B, int r, float s, uint16_t* __restrict__ y,
-    uint16_t* __restrict__ u_out, CodeParams P) {
-  __shared__ uint32_t spair[256 * kPairCopies];
+// ---------------------------------------------------------------------------
+// Dequant-GEMV.  One workgroup of kWaves waves per band of 16 output
+// features (rows of W).  Wave w owns a contiguous slice of at most kS
+// blocks of the band's K range (longer rows take several passes) and issues
+// all of its weight loads (8 bytes per lane per block) and block constants
+// before anything else.  x is read per block, kXAhead blocks ahead (it is
+// small and L2-resident).  The LoRA inputs (u as `usplit` fp32 partial
+// sums [usplit][M][r], and the band's 16 rows of B) are loaded at the start
+// with plain indexing and only consumed in the epilogue.  Partial sums meet
+// in LDS in a fixed order (bit-reproducible).
+//
+// Everything before the weight loads is kept to a few instructions: at
+// these sizes the whole matrix is in flight within a microsecond or two,
+// so every serial step (a division in address arithmetic, an LDS round trip
+// per block) shows up directly in the kernel time.
+struct GemvArgs {
+  const uint8_t* packed;
+  const uint8_t* qscale;
+  const float* gscale;
+  const float* absmax;
+  int64_t N, K;
+  const uint16_t* x;
+  const float* u;
+  const uint16_t* B;
+  uint16_t* y;
+  uint16_t* u_out;
+  int M, usplit, r;
+  float s;
+};
+
+// kXM: token rows of x staged in LDS per wave (1 or 4; 0: no staging, x
+// read per block from memory into a register ring).  kCopiesT: pair-table
+// copies, 64 for 16-wave workgroups (entry address (e << 8) | 4 lane is one
+// v_perm), else 32 (LDS for several workgroups per CU).
+template <int kWaves, int kS, bool kDQ, int kXM>
+__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, const CodeParams P) {
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kCopiesT = kWaves == 16 ? 64 : 32;
+  constexpr int kTabWords = 256 * kCopiesT;
+  constexpr int kBPer = (16 * 128 + kThreads - 1) / kThreads;  // B-tile elements per thread
+  constexpr bool kXL = kXM > 0;
+  // staged x per wave: [token m < kXM][block i < kS][64 bf16]
+  constexpr int kXBytes = kXL ? kXM * kS * 128 : 16;
+  constexpr int kXPer = kXL ? (kXM * kS * 8 + 63) / 64 : 1;  // 16-byte chunks per lane
+  // Pair table during the walk; afterwards the same memory holds u and the
+  // band's B rows for the epilogue.
+  __shared__ __attribute__((aligned(16))) uint32_t stab[kTabWords];
   __shared__ float sl8[256];
-  __shared__ float spart[kGemvWaves][16][17];
-  __shared__ float su[16 * 128];
+  __shared__ float spart[kWaves][16][17];
+  __shared__ __attribute__((aligned(16))) char sx[kXL ? kWaves * kXBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint4 sxz[kXL ? kS * 8 + 8 : 1];  // zeros
+  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2, "epilogue buffers must fit");
 
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
-  const int64_t nblk = K >> 6;
+  const int64_t K = a.K, nblk = K >> 6;
   const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
   const int64_t n = n0 + nl;
-  const uint8_t* wrow = packed + n * (K >> 1);
-  // Lanes of token rows >= M read row M - 1 (unconditional loads keep the
-  // load counter exact) and zero the value.
+  const int M = a.M, r = a.r, mr = M * r, usplit = a.usplit;
+
+  // -- LoRA inputs (consumed only in the epilogue) --
+  // Issued without any branch (a branch join would wait for them); with
+  // r == 0 the host points B and u at valid memory and element 0 is read.
+  // Thread t owns element t of u[M][r] (elements >= kThreads are summed
+  // from memory in the epilogue); partial s < kUParts reads slice
+  // min(s, usplit - 1), and the epilogue keeps only s < usplit.
+  uint32_t bt[kBPer];  // 32-bit so the compiler does not pack them (that waits on the loads)
+  float upart[kUParts];
+  {
+    const int nbt = 16 * r;
+#pragma unroll
+    for (int q = 0; q < kBPer; ++q) {
+      const int e = tid + q * kThreads;
+      bt[q] = a.B[n0 * r + (e < nbt ? e : (nbt > 0 ? nbt - 1 : 0))];
+    }
+    const float* ut = a.u + (tid < mr ? tid : 0);
+#pragma unroll
+    for (int q = 0; q < kUParts; ++q) {
+      const int sl = q < usplit ? q : usplit - 1;
+      upart[q] = ut[static_cast<int64_t>(sl) * mr];
+    }
+  }
+
+  const uint8_t* wrow = a.packed + n * (K >> 1) + 8 * g;
+  // Token rows >= M: the ring path reads row M - 1 and zeroes the value;
+  // the staged path reads a zero region.
   const bool xvalid = nl < M;
-  const uint16_t* xrow = x + static_cast<int64_t>(xvalid ? nl : M - 1) * K;
+  const int xm = xvalid ? nl : M - 1;
+  const uint16_t* xrow = a.x + static_cast<int64_t>(xm) * K + 16 * g;
   const int64_t rowblk0 = n * nblk;
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+  char* sxw = sx + (kXL ? wave * kXBytes : 0);
+  const char* xbase = kXL ? (xvalid ? sxw + xm * (kS * 128) + g * 32
+                                    : reinterpret_cast<const char*>(sxz) + g * 32)
+                          : nullptr;
   const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
   f32x4_t acc = zero;
 
-  // LoRA partial sums: loaded first (thread t owns elements t, t + 512, ..
-  // of u[M][r], kUParts values in all), summed after the main loop, so their
-  // latency hides behind the weight stream.  The host keeps
-  // usplit * ceil(M r / 512) <= kUParts.
-  const int mr = M * r;
-  const int ue = (mr + kGemvWaves * 64 - 1) / (kGemvWaves * 64);
-  float upart[kUParts];
+  const int64_t per_pass = static_cast<int64_t>(kWaves) * kS;
+  for (int64_t p0 = 0; p0 < nblk; p0 += per_pass) {
+    const int64_t pn = min(per_pass, nblk - p0);
+    const int64_t b_lo = p0 + pn * wave / kWaves;  // <= nblk - 1 even for an empty slice
+    const int nb = static_cast<int>(p0 + pn * (wave + 1) / kWaves - b_lo);
+    const int nbc = nb > 0 ? nb - 1 : 0;
+
+    // 1. tables (first pass only): the barrier they need comes before the
+    // loads of the slice, so no wave then waits for another wave's loads
+    if (p0 == 0) {
+      // uint4 f of the table holds entry f / (kCopiesT / 4), copies
+      // 4 (f % (kCopiesT / 4)) .. + 3; for f = tid + i kThreads the odd
+      // element (low nibble, e & 15) is fixed per thread and the even
+      // element (e >> 4) is wave-uniform.
+      const CodeRegs R = code_regs(P);
+      constexpr int kPer = kCopiesT / 4;  // uint4 per entry
+      const int e_hi0 = __builtin_amdgcn_readfirstlane(tid / (16 * kPer));
+      constexpr int kFill = kTabWords / 4 / kThreads;
+      const float q_odd = code_value(R, static_cast<uint32_t>((tid / kPer) & 15));
 #pragma unroll
-  for (int q = 0; q < kUParts; ++q) {
-    const int e = q / usplit, sp = q % usplit;
-    const int idx = threadIdx.x + e * kGemvWaves * 64;
-    upart[q] = (e < ue && idx < mr) ? u[static_cast<int64_t>(sp) * mr + idx] : 0.f;
-  }
-
-  const int64_t per_pass = static_cast<int64_t>(kGemvWaves) * kGemvMaxBlocks;
-  bool tables_ready = false;
-  for (int64_t pass0 = 0; pass0 < nblk; pass0 += per_pass) {
-    const int64_t pass_n = min(per_pass, nblk - pass0);
-    const int64_t b_lo = pass0 + pass_n * wave / kGemvWaves;
-    const int64_t b_hi = pass0 + pass_n * (wave + 1) / kGemvWaves;
-    const int nb = static_cast<int>(b_hi - b_lo);
-
-    // 1. all weight loads and block constants of this wave's slice
-    uint2 w[kGemvMaxBlocks];
-    float cq[kGemvMaxBlocks];
-#pragma unroll
-    for (int i = 0; i < kGemvMaxBlocks; ++i) {
-      // clamped into the slice (an empty slice reads its first block, which
-      // exists since b_lo < nblk); blocks past the slice are skipped below
-      const int64_t b = b_lo + min(i, max(nb - 1, 0));
-      w[i] = *reinterpret_cast<const uint2*>(wrow + b * 32 + g * 8);
-      if constexpr (kDQ) cq[i] = __uint_as_float(static_cast<uint32_t>(qscale[rowblk0 + b]));
-      else cq[i] = absmax[rowblk0 + b];
-    }
-    float g_lo = 0.f, g_hi = 0.f;
-    if constexpr (kDQ) {
-      g_lo = gscale[(rowblk0 + b_lo) >> 8];
-      g_hi = gscale[(rowblk0 + max(b_hi - 1, b_lo)) >> 8];
-    }
-
-    // 2. tables (once), overlapping the loads
-    if (!tables_ready) {
-      fill_pair_bf16(spair, P, kPairCopies);
-      for (int i = threadIdx.x; i < 256; i += kGemvWaves * 64) sl8[i] = l8_value(i);
+      for (int i = 0; i < kFill; ++i) {
+        const uint32_t wv = pack_bf16x2(
+            code_value(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
+        reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
+      }
+      for (int i = tid; i < 256; i += kThreads) sl8[i] = l8_value(static_cast<uint32_t>(i));
+      if constexpr (kXL)
+        for (int i = tid; i < kS * 8 + 8; i += kThreads) sxz[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
-      tables_ready = true;
     }
 
-    // 3. walk the slice: x two blocks ahead, decode, MFMA, block scale
-    const int cp = threadIdx.x & (kPairCopies - 1);
-    uint4 xa[3][2];  // x of blocks i, i+1, i+2 in slots i % 3, ...
-    auto load_x = [&](int i) {
-      const uint4* xp = reinterpret_cast<const uint4*>(xrow + (b_lo + i) * 64 + g * 16);
-      xa[i % 3][0] = xp[0];
-      xa[i % 3][1] = xp[1];
-    };
-    auto x_of = [&](int slot, int h) {
-      const uint4 v = xa[slot][h];
-      return xvalid ? v : make_uint4(0, 0, 0, 0);
-    };
-    if (nb > 0) load_x(0);
-    if (nb > 1) load_x(1);
+    // 2. x of the slice into registers (staged path): 16-byte chunk c of
+    // the wave's [m][i][128 B] staging area; rows >= M and blocks past the
+    // slice re-read valid data and are never used.
+    uint4 xs[kXPer];
+    int xc[kXPer];
+    if constexpr (kXL) {
 #pragma unroll
-    for (int i = 0; i < kGemvMaxBlocks; ++i) {
-      if (i < nb) {
-        if (i + 2 < nb) load_x(i + 2);
-        const uint32_t w0 = w[i].x, w1 = w[i].y;
-        const uint4 d0 = make_uint4(spair[(w0 & 0xFF) * kPairCopies + cp],
-                                    spair[((w0 >> 8) & 0xFF) * kPairCopies + cp],
-                                    spair[((w0 >> 16) & 0xFF) * kPairCopies + cp],
-                                    spair[(w0 >> 24) * kPairCopies + cp]);
-        const uint4 d1 = make_uint4(spair[(w1 & 0xFF) * kPairCopies + cp],
-                                    spair[((w1 >> 8) & 0xFF) * kPairCopies + cp],
-                                    spair[((w1 >> 16) & 0xFF) * kPairCopies + cp],
-                                    spair[(w1 >> 24) * kPairCopies + cp]);
-        f32x4_t t = mfma16(x_of(i % 3, 0), d0, zero);
-        t = mfma16(x_of(i % 3, 1), d1, t);
-        float cs;
-        if constexpr (kDQ) {
-          const int64_t b = b_lo + i;
-          const float c2 = ((rowblk0 + b) >> 8) == ((rowblk0 + b_lo) >> 8) ? g_lo : g_hi;
-          cs = __fmul_rn(sl8[__float_as_uint(cq[i])], c2);
-        } else {
-          cs = cq[i];
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs, t[v], acc[v]);
+      for (int q = 0; q < kXPer; ++q) {
+        int c = lane + 64 * q;
+        c = c < kXM * kS * 8 ? c : kXM * kS * 8 - 1;
+        xc[q] = c;
+        const int cm = c / (kS * 8), ci = (c >> 3) % kS;
+        const int64_t m = cm < M ? cm : M - 1;
+        const int64_t bi = b_lo + (ci < nbc ? ci : nbc);
+        xs[q] = *reinterpret_cast<const uint4*>(a.x + m * K + bi * 64 + (c & 7) * 8);
       }
     }
-  }
-  // LoRA down-projection: sum the partials loaded at the start.
+
+    // 3. block constants and all weight loads of this wave's slice
+    const int64_t qb = rowblk0 + b_lo;  // index of the slice's first block constant
+    constexpr int kQD = kS / 4 + 1;
+    uint32_t qd[kQD];
+    float cq[kDQ ? 1 : kS];
+    float g_lo = 0.f, g_hi = 0.f;
+    if constexpr (kDQ) {
+      // 8-bit constants of the slice: aligned dwords covering
+      // [qb, qb + kS); the total count N K / 64 is a multiple of 4, so the
+      // clamp keeps every dword inside the array.
+      const uint32_t* q32 = reinterpret_cast<const uint32_t*>(a.qscale);
+      const int64_t dmax = ((a.N * nblk) >> 2) - 1;
 #pragma unroll
-  for (int e = 0; e < kUParts; ++e) {
-    if (e < ue) {
-      float v = 0.f;
+      for (int j = 0; j < kQD; ++j) {
+        const int64_t d = (qb >> 2) + j;
+        qd[j] = q32[d < dmax ? d : dmax];
+      }
+      g_lo = a.gscale[qb >> 8];
+      g_hi = a.gscale[(qb + nbc) >> 8];
+    } else {
 #pragma unroll
-      for (int q = 0; q < kUParts; ++q)
-        if (q / usplit == e) v += upart[q];
-      const int idx = threadIdx.x + e * kGemvWaves * 64;
-      if (idx < mr) su[idx] = v;
+      for (int i = 0; i < kS; ++i) cq[i] = a.absmax[qb + (i < nbc ? i : nbc)];
+    }
+    uint2 w[kS];
+#pragma unroll
+    for (int i = 0; i < kS; ++i)
+      w[i] = *reinterpret_cast<const uint2*>(wrow + (b_lo + (i < nbc ? i : nbc)) * 32);
+
+    // 4. x: staged slice to LDS (read back only by this wave), or the
+    // first blocks of the register ring
+    uint4 xr[kXL ? 1 : kXAhead + 1][2];
+    auto load_x = [&](int i) {
+      if constexpr (!kXL) {
+        const int ic = i < nbc ? i : nbc;
+        const uint4* xp = reinterpret_cast<const uint4*>(xrow + (b_lo + ic) * 64);
+        xr[i % (kXAhead + 1)][0] = xp[0];
+        xr[i % (kXAhead + 1)][1] = xp[1];
+      }
+    };
+    if constexpr (kXL) {
+#pragma unroll
+      for (int q = 0; q < kXPer; ++q) *reinterpret_cast<uint4*>(sxw + xc[q] * 16) = xs[q];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kXAhead; ++i) load_x(i);
+    }
+    auto x_of = [&](int i, int h) -> uint4 {
+      if constexpr (kXL) {
+        return *reinterpret_cast<const uint4*>(xbase + i * 128 + h * 16);
+      } else {
+        const uint4 v = xr[i % (kXAhead + 1)][h];
+        return xvalid ? v : make_uint4(0, 0, 0, 0);
+      }
+    };
+
+    // 5. block constants c' of every block of the slice (one LDS round trip)
+    float cs[kS];
+    if constexpr (kDQ) {
+      const uint32_t sh = static_cast<uint32_t>(qb & 3);
+      const int gfirst = static_cast<int>(qb & 255);
+#pragma unroll
+      for (int j = 0; j < kS / 4; ++j) {
+        const uint32_t al = __builtin_amdgcn_alignbyte(qd[j + 1], qd[j], sh);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * j + b;
+          const float c = __fmul_rn(sl8[(al >> (8 * b)) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
+          cs[i] = i < nb ? c : 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS; ++i) cs[i] = i < nb ? cq[i] : 0.f;
+    }
+
+    // 6. walk the slice; the pair lookups of block i + 1 are issued before
+    // the MFMAs of block i.  No control flow: blocks past the slice (the
+    // last wave of an uneven split) re-read valid data and have c' = 0 (a
+    // branch here lets the compiler sink the weight loads into it).
+    auto look = [&](uint32_t word, int byte) -> uint32_t {
+      uint32_t addr;
+      if constexpr (kCopiesT == 64) {
+        // bytes [4 lane, e, 0, 0]: (e << 8) | 4 lane
+        addr = __builtin_amdgcn_perm(word, lane4, 0x0C0C0400u + (static_cast<uint32_t>(byte) << 8));
+      } else {
+        addr = (((word >> (8 * byte)) & 0xFFu) << 7) | (lane4 & 0x7Cu);
+      }
+      return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(stab) + addr);
+    };
+    uint4 d[kS][2];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      d[i][0] = make_uint4(look(w[i].x, 0), look(w[i].x, 1), look(w[i].x, 2), look(w[i].x, 3));
+      d[i][1] = make_uint4(look(w[i].y, 0), look(w[i].y, 1), look(w[i].y, 2), look(w[i].y, 3));
+      if (i > 0) {
+        f32x4_t t = mfma16(x_of(i - 1, 0), d[i - 1][0], zero);
+        t = mfma16(x_of(i - 1, 1), d[i - 1][1], t);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[i - 1], t[v], acc[v]);
+      }
+      load_x(i + kXAhead);
+    }
+    {
+      f32x4_t t = mfma16(x_of(kS - 1, 0), d[kS - 1][0], zero);
+      t = mfma16(x_of(kS - 1, 1), d[kS - 1][1], t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[kS - 1], t[v], acc[v]);
     }
   }
+
+  // -- epilogue --
 #pragma unroll
   for (int v = 0; v < 4; ++v) spart[wave][4 * g + v][nl] = acc[v];
+  __syncthreads();  // every wave is done with the pair table
+  float* su = reinterpret_cast<float*>(stab);                  // [M][r] fp32
+  uint16_t* sB = reinterpret_cast<uint16_t*>(stab + 16 * 128);  // [16][r] bf16
+  if (r > 0) {
+    // u = sum of the usplit partial sums, slice order 0, 1, ..
+    if (tid < mr) {
+      float v = 0.f;
+#pragma unroll
+      for (int q = 0; q < kUParts; ++q) {
+        const uint32_t mask = q < usplit ? 0xFFFFFFFFu : 0u;  // an AND, not a select
+        v += __uint_as_float(__float_as_uint(upart[q]) & mask);
+      }
+      su[tid] = v;
+    }
+    for (int idx = tid + kThreads; idx < mr; idx += kThreads) {
+      float v = 0.f;
+      for (int q = 0; q < usplit; ++q) v += a.u[static_cast<int64_t>(q) * mr + idx];
+      su[idx] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < kBPer; ++q) {
+      const int e = tid + q * kThreads;
+      if (e < 16 * r) sB[e] = static_cast<uint16_t>(bt[q]);
+    }
+  }
   __syncthreads();
-  if (u_out && blockIdx.x == 0)
-    for (int i = threadIdx.x; i < M * r; i += kGemvWaves * 64)
-      u_out[i] = static_cast<uint16_t>(pack_bf16x2(su[i], 0.f) & 0xFFFF);
-  for (int idx = threadIdx.x; idx < 16 * M; idx += kGemvWaves * 64) {
+  if (a.u_out && blockIdx.x == 0)
+    for (int i = tid; i < mr; i += kThreads)
+      a.u_out[i] = static_cast<uint16_t>(pack_bf16x2(su[i], 0.f) & 0xFFFF);
+  for (int idx = tid; idx < 16 * M; idx += kThreads) {
     const int m = idx >> 4, nn = idx & 15;
     float v = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kGemvWaves; ++ww) v += spart[ww][m][nn];
+    for (int ww = 0; ww < kWaves; ++ww) v += spart[ww][m][nn];
     if (r > 0) {
       float lora = 0.f;
-      const uint16_t* brow = B + (n0 + nn) * r;
-      for (int j = 0; j < r; ++j) lora = fmaf(su[m * r + j], bf16_to_f32(brow[j]), lora);
-      v = fmaf(s, lora, v);
+      for (int j = 0; j < r; ++j) lora = fmaf(su[m * r + j], bf16_to_f32(sB[nn * r + j]), lora);
+      v = fmaf(a.s, lora, v);
     }
-    y[static_cast<int64_t>(m) * N + n0 + nn] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
+    a.y[static_cast<int64_t>(m) * a.N + n0 + nn] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
   }
 }
+
+// One GEMV configuration; four-row x staging only where its LDS fits
+// (otherwise the register ring).
+template <int W, int S>
+void gemv_config(int xmode, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
+                 const CodeParams& P) {
+  constexpr size_t kLds = 256 * (W == 16 ? 64 : 32) * 4 + W * kXMaxM * S * 128 +
+                          W * 16 * 17 * 4 + 1024 + (S * 8 + 8) * 16;
+  constexpr bool kFits4 = kLds <= 160 * 1024;
+  if (xmode == 1) {
+    hipLaunchKernelGGL((gemv_kernel<W, S, true, 1>), grid, dim3(W * 64), 0, st, a, P);
+  } else if (xmode == 4 && kFits4) {
+    if constexpr (kFits4) hipLaunchKernelGGL((gemv_kernel<W, S, true, 4>), grid, dim3(W * 64), 0, st, a, P);
+  } else if (dq) {
+    hipLaunchKernelGGL((gemv_kernel<W, S, true, 0>), grid, dim3(W * 64), 0, st, a, P);
+  } else {
+    hipLaunchKernelGGL((gemv_kernel<W, S, false, 0>), grid, dim3(W * 64), 0, st, a, P);
+  }
+}
+
+template <int kCols>
+void skinny_launch(dim3 grid, bool wide, hipStream_t s, const uint16_t* in, int64_t M, int64_t L,
+                   const uint16_t* P, int r, float scale, int ksplit, float* out_f32,
+                   uint16_t* out_sbf16, uint16_t* out_bf16) {
+  if (wide)
+    hipLaunchKernelGGL((skinny_kernel<kCols, 16>), grid, dim3(1024), 0, s, in, M, L, P, r, scale,
+                       ksplit, out_f32, out_sbf16, out_bf16);
+  else
+    hipLaunchKernelGGL((skinny_kernel<kCols, 8>), grid, dim3(512), 0, s, in, M, L, P, r, scale,
+                       ksplit, out_f32, out_sbf16, out_bf16);
+}
+
+int skinny_cols(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8; }
 
 }  // namespace
 
 int skinny_splits(int64_t M, int64_t L, int r) {
   if (M > 16 || r == 0) return 1;
-  // the GEMV holds usplit * ceil(M r / 512) partials per thread
-  const int64_t per_thread = (M * r + kGemvWaves * 64 - 1) / (kGemvWaves * 64);
-  int ks = static_cast<int>(kUParts / per_thread);
-  const int64_t chunks = L >> 5;
-  if (ks > chunks / 4) ks = static_cast<int>(chunks / 4);
-  return ks < 1 ? 1 : ks;
+  // as many slices as the GEMV takes partial sums (kUParts), each of the 8
+  // waves of a slice keeping at least one 32-wide chunk
+  int64_t ks = (L >> 5) / 8;
+  if (ks > kUParts) ks = kUParts;
+  return ks < 1 ? 1 : static_cast<int>(ks);
 }
 
-hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P,
-                         bool p_is_rl, int r, float scale, float* out_f32,
-                         uint16_t* out_scaled_bf16, uint16_t* out_bf16, int ksplit,
-                         hipStream_t s) {
+hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P, int r,
+                         float scale, float* out_f32, uint16_t* out_scaled_bf16,
+                         uint16_t* out_bf16, int ksplit, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
   const dim3 grid(static_cast<uint32_t>((M + 15) / 16), static_cast<uint32_t>(ksplit));
-  if (p_is_rl)
-    hipLaunchKernelGGL(skinny_kernel<true>, grid, dim3(256), 0, s, in, M, L, P, r, scale, ksplit,
-                       out_f32, out_scaled_bf16, out_bf16);
-  else
-    hipLaunchKernelGGL(skinny_kernel<false>, grid, dim3(256), 0, s, in, M, L, P, r, scale, ksplit,
-                       out_f32, out_scaled_bf16, out_bf16);
+  // Many row tiles: 16 waves per tile so each CU has enough loads in
+  // flight; decode (one row tile): 8 waves per slice, up to 8 slices.
+  const bool wide = M > 16;
+  switch (skinny_cols(r)) {
+    case 1: skinny_launch<1>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 2: skinny_launch<2>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 4: skinny_launch<4>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    default: skinny_launch<8>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out, hipStream_t s) {
+  if (L == 0 || C == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<uint32_t>((L + 63) / 64)), dim3(256), 0, s,
+                     in, L, C, out);
   return hipGetLastError();
 }
 
@@ -300,13 +533,43 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   const Tables* t = tables();
   CodeParams P;
   for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
-  const dim3 grid(static_cast<uint32_t>(w.N / 16));
-  if (w.qscale)
-    hipLaunchKernelGGL(gemv_kernel<true>, grid, dim3(kGemvWaves * 64), 0, st, w.packed, w.qscale,
-                       w.gscale, w.absmax, w.N, w.K, x, M, u, usplit, B, r, s, y, u_out, P);
-  else
-    hipLaunchKernelGGL(gemv_kernel<false>, grid, dim3(kGemvWaves * 64), 0, st, w.packed, w.qscale,
-                       w.gscale, w.absmax, w.N, w.K, x, M, u, usplit, B, r, s, y, u_out, P);
+  GemvArgs a;
+  a.packed = w.packed;
+  a.qscale = w.qscale;
+  a.gscale = w.gscale;
+  a.absmax = w.absmax;
+  a.N = w.N;
+  a.K = w.K;
+  a.x = x;
+  // with r == 0 the kernel still reads element 0 of u and B (never used)
+  a.u = r > 0 ? u : reinterpret_cast<const float*>(x);
+  a.B = r > 0 ? B : x;
+  a.y = y;
+  a.u_out = u_out;
+  a.M = M;
+  a.usplit = usplit < 1 ? 1 : usplit;
+  a.r = r;
+  a.s = s;
+  const int64_t nbands = w.N / 16, nblk = w.K >> 6;
+  const dim3 grid(static_cast<uint32_t>(nbands));
+  // About 16 resident waves per CU in one round: waves per band from
+  // 4096 / bands (4, 8 or 16), blocks per wave the smallest of 4, 8, 12, 16
+  // that covers the row (longer rows: 16 per pass, several passes).
+  int wv = 4;
+  while (wv < 16 && nbands * wv * 2 <= 4096) wv *= 2;
+  const int64_t need = (nblk + wv - 1) / wv;
+  int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 12 ? 12 : 16;
+  if (wv == 16 && sb == 16) sb = 12;  // 16 x 16 would spill at 1024 threads
+  const bool dq = w.qscale != nullptr;
+  // x staging: one row for M == 1, four for M <= 4, none above (ring);
+  // the unscaled-constant path (no double quantisation) uses the ring.
+  const int xmode = !dq ? 0 : M == 1 ? 1 : M <= kXMaxM ? 4 : 0;
+#define QN_GEMV(W, S) \
+  if (wv == W && sb == S) gemv_config<W, S>(xmode, dq, grid, st, a, P);
+  QN_GEMV(4, 4) QN_GEMV(4, 8) QN_GEMV(4, 12) QN_GEMV(4, 16)
+  QN_GEMV(8, 4) QN_GEMV(8, 8) QN_GEMV(8, 12) QN_GEMV(8, 16)
+  QN_GEMV(16, 4) QN_GEMV(16, 8) QN_GEMV(16, 12)
+#undef QN_GEMV
   return hipGetLastError();
 }
 

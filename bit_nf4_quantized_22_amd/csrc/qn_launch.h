@@ -22,14 +22,15 @@ hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, floa
                      hipStream_t s);
 hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s);
 
-// out[M, r] = in[M, L] * P^T where P is [r, L] row-major (p_is_rl) or the
-// transpose of a row-major [L, r] matrix.  ksplit == 1 writes any of: fp32
-// result, bf16(scale * result), bf16(result); ksplit > 1 splits L over
-// ksplit workgroups and writes fp32 partial sums out_f32[ksplit][M][r].
-hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P,
-                         bool p_is_rl, int r, float scale, float* out_f32,
-                         uint16_t* out_scaled_bf16, uint16_t* out_bf16, int ksplit,
-                         hipStream_t s);
+// out[M, r] = in[M, L] * P^T, P row-major [r, L] (in and P 16-byte
+// aligned, L % 32 == 0).  ksplit == 1 writes any of: fp32 result,
+// bf16(scale * result), bf16(result); ksplit > 1 splits L over ksplit
+// workgroups and writes fp32 partial sums out_f32[ksplit][M][r].
+hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P, int r,
+                         float scale, float* out_f32, uint16_t* out_scaled_bf16,
+                         uint16_t* out_bf16, int ksplit, hipStream_t s);
+// out[C, L] = in[L, C]^T (bf16, C <= 128).
+hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out, hipStream_t s);
 // Number of L-slices launch_skinny uses for the decode path (M <= 16).
 int skinny_splits(int64_t M, int64_t L, int r);
 
