@@ -54,7 +54,8 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
 // path) followed by bf16(s u).
 size_t fwd_u32_bytes(int64_t M, int32_t r) {
   const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  return round_up(mr * 4 * (M <= kGemvMaxM ? 16 : 1), 256);
+  // decode: up to kDecodeMaxSlices partial sums of u
+  return round_up(mr * 4 * (M <= kGemvMaxM ? static_cast<size_t>(qn::kDecodeMaxSlices) : 1), 256);
 }
 
 size_t fwd_ws(int64_t M, int32_t r) {
@@ -179,7 +180,7 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
   float* u32 = nullptr;
   uint16_t* us = nullptr;
   const bool decode = M <= kGemvMaxM;
-  const int ks = decode ? qn::skinny_splits(M, w->K, r) : 1;
+  const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K)) : 1;
   if (r > 0) {
     u32 = static_cast<float*>(ws);
     us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fwd_u32_bytes(M, r));

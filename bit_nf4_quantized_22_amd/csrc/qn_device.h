@@ -82,6 +82,11 @@ __device__ __forceinline__ float code_value(const CodeRegs& R, uint32_t c) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(static_cast<int>(c << 2), R.lanes));
 }
 
+// Same for a wave-uniform c: v_readlane, no LDS operation.
+__device__ __forceinline__ float code_value_uniform(const CodeRegs& R, uint32_t c) {
+  return __int_as_float(__builtin_amdgcn_readlane(R.lanes, static_cast<int>(c)));
+}
+
 // LDS byte table, `copies` interleaved copies: entry e of copy k at
 // e * copies + k holds (q[e >> 4], q[e & 15]) (even element first).
 __device__ __forceinline__ void fill_pair_f32(float2* tab, const CodeParams& P, int copies) {

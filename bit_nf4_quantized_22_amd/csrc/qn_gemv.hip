@@ -78,7 +78,10 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
 #pragma unroll
   for (int c = 0; c < kCols; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // chunks of this wave: c_lo + wave + kWaves * i, i < cnt
+  // chunks of this wave: c_lo + wave + kWaves * i, i < cnt.  Each round
+  // issues all of its loads (clamped to valid chunks) before any MFMA, and
+  // has no branches: chunks past cnt have their x operand masked to zero
+  // with an integer AND (a select would become a branch around the load).
   const int64_t first = c_lo + wave;
   const int64_t cnt = first < c_hi ? (c_hi - first + kWaves - 1) / kWaves : 0;
   for (int64_t i0 = 0; i0 < cnt; i0 += kCh) {
@@ -93,12 +96,13 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     }
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
-      if (i0 + i < cnt) {
+      const uint32_t am = i0 + i < cnt ? 0xFFFFFFFFu : 0u;
+      const uint4 ai = make_uint4(a[i].x & am, a[i].y & am, a[i].z & am, a[i].w & am);
 #pragma unroll
-        for (int c = 0; c < kCols; ++c) {
-          const uint4 bb = pvalid[c] ? b[i][c] : make_uint4(0, 0, 0, 0);
-          acc[c] = mfma16(a[i], bb, acc[c]);
-        }
+      for (int c = 0; c < kCols; ++c) {
+        const uint32_t bm = pvalid[c] ? 0xFFFFFFFFu : 0u;
+        const uint4 bb = make_uint4(b[i][c].x & bm, b[i][c].y & bm, b[i][c].z & bm, b[i][c].w & bm);
+        acc[c] = mfma16(ai, bb, acc[c]);
       }
     }
   }
@@ -205,7 +209,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   __shared__ float spart[kWaves][16][17];
   __shared__ __attribute__((aligned(16))) char sx[kXL ? kWaves * kXBytes : 16];
   __shared__ __attribute__((aligned(16))) uint4 sxz[kXL ? kS * 8 + 8 : 1];  // zeros
-  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2, "epilogue buffers must fit");
+  // epilogue: su [M r <= 2048] + sB [16 r <= 2048 bf16] + group sums [<= 1024]
+  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2 + 1024, "epilogue buffers must fit");
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,9 +223,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   // -- LoRA inputs (consumed only in the epilogue) --
   // Issued without any branch (a branch join would wait for them); with
   // r == 0 the host points B and u at valid memory and element 0 is read.
-  // Thread t owns element t of u[M][r] (elements >= kThreads are summed
-  // from memory in the epilogue); partial s < kUParts reads slice
-  // min(s, usplit - 1), and the epilogue keeps only s < usplit.
+  // u arrives as usplit partial sums [usplit][M][r].  Thread t works on
+  // element e = t % (M r) for slices sg, sg + G, sg + 2 G, .. (sg = t / (M r),
+  // G = threads / (M r) groups), kUParts of them at most: the host keeps
+  // usplit <= G kUParts.  Unused slots read slice 0 and are masked in the
+  // epilogue, which sums each thread's slots, then the groups, in a fixed
+  // order.  With M r > threads, elements >= threads are summed from memory
+  // in the epilogue.
   uint32_t bt[kBPer];  // 32-bit so the compiler does not pack them (that waits on the loads)
   float upart[kUParts];
   {
@@ -230,15 +239,24 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
       const int e = tid + q * kThreads;
       bt[q] = a.B[n0 * r + (e < nbt ? e : (nbt > 0 ? nbt - 1 : 0))];
     }
-    const float* ut = a.u + (tid < mr ? tid : 0);
+    const int ugroups = mr > 0 && mr <= kThreads ? kThreads / mr : 1;
+    const int ue = mr > 0 ? tid % mr : 0, ug = mr > 0 ? tid / mr : 0;
+    const float* ut = a.u + (ug < ugroups ? ue : 0);
 #pragma unroll
     for (int q = 0; q < kUParts; ++q) {
-      const int sl = q < usplit ? q : usplit - 1;
-      upart[q] = ut[static_cast<int64_t>(sl) * mr];
+      const int sl = ug + q * ugroups;
+      upart[q] = ut[static_cast<int64_t>(sl < usplit && ug < ugroups ? sl : 0) * mr];
     }
   }
 
-  const uint8_t* wrow = a.packed + n * (K >> 1) + 8 * g;
+  // Weight loads: lane l reads 8 bytes of row n0 + l / 4 at byte 8 (l % 4)
+  // of the block, so each group of 4 consecutive lanes reads 32 contiguous
+  // bytes (one row's block); ds_bpermute then moves them to the MFMA lane
+  // (row l % 16, byte group l / 16), i.e. from lane 4 (l % 16) + l / 16.
+  // (Loading in MFMA lane order directly, consecutive lanes in different
+  // rows, streams about a third slower.)
+  const uint8_t* wrow = a.packed + (n0 + (lane >> 2)) * (K >> 1) + 8 * (lane & 3);
+  const int wperm = ((lane & 15) * 4 + (lane >> 4)) * 4;
   // Token rows >= M: the ring path reads row M - 1 and zeroes the value;
   // the staged path reads a zero region.
   const bool xvalid = nl < M;
@@ -275,7 +293,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
 #pragma unroll
       for (int i = 0; i < kFill; ++i) {
         const uint32_t wv = pack_bf16x2(
-            code_value(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
+            code_value_uniform(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
         reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
       }
       for (int i = tid; i < 256; i += kThreads) sl8[i] = l8_value(static_cast<uint32_t>(i));
@@ -394,8 +412,10 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
     uint4 d[kS][2];
 #pragma unroll
     for (int i = 0; i < kS; ++i) {
-      d[i][0] = make_uint4(look(w[i].x, 0), look(w[i].x, 1), look(w[i].x, 2), look(w[i].x, 3));
-      d[i][1] = make_uint4(look(w[i].y, 0), look(w[i].y, 1), look(w[i].y, 2), look(w[i].y, 3));
+      const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].x)));
+      const uint32_t w1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].y)));
+      d[i][0] = make_uint4(look(w0, 0), look(w0, 1), look(w0, 2), look(w0, 3));
+      d[i][1] = make_uint4(look(w1, 0), look(w1, 1), look(w1, 2), look(w1, 3));
       if (i > 0) {
         f32x4_t t = mfma16(x_of(i - 1, 0), d[i - 1][0], zero);
         t = mfma16(x_of(i - 1, 1), d[i - 1][1], t);
@@ -418,16 +438,18 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   __syncthreads();  // every wave is done with the pair table
   float* su = reinterpret_cast<float*>(stab);                  // [M][r] fp32
   uint16_t* sB = reinterpret_cast<uint16_t*>(stab + 16 * 128);  // [16][r] bf16
+  float* sug = reinterpret_cast<float*>(stab + 16 * 128 + 16 * 128 / 2);  // [groups][M r]
   if (r > 0) {
-    // u = sum of the usplit partial sums, slice order 0, 1, ..
-    if (tid < mr) {
+    const int ugroups = mr <= kThreads ? kThreads / mr : 1;
+    const int ue = tid % mr, ug = tid / mr;
+    if (ug < ugroups) {
       float v = 0.f;
 #pragma unroll
       for (int q = 0; q < kUParts; ++q) {
-        const uint32_t mask = q < usplit ? 0xFFFFFFFFu : 0u;  // an AND, not a select
+        const uint32_t mask = ug + q * ugroups < usplit ? 0xFFFFFFFFu : 0u;  // an AND, not a select
         v += __uint_as_float(__float_as_uint(upart[q]) & mask);
       }
-      su[tid] = v;
+      sug[ug * mr + ue] = v;
     }
     for (int idx = tid + kThreads; idx < mr; idx += kThreads) {
       float v = 0.f;
@@ -438,6 +460,12 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
     for (int q = 0; q < kBPer; ++q) {
       const int e = tid + q * kThreads;
       if (e < 16 * r) sB[e] = static_cast<uint16_t>(bt[q]);
+    }
+    __syncthreads();
+    if (tid < mr && tid < kThreads) {
+      float v = 0.f;
+      for (int gq = 0; gq < ugroups; ++gq) v += sug[gq * mr + tid];
+      su[tid] = v;
     }
   }
   __syncthreads();
@@ -493,12 +521,22 @@ int skinny_cols(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8; }
 
 }  // namespace
 
-int skinny_splits(int64_t M, int64_t L, int r) {
+int gemv_threads(int64_t N, int64_t K) {
+  int wv = 4;
+  while (wv < 16 && (N / 16) * wv * 2 <= 4096) wv *= 2;
+  (void)K;
+  return wv * 64;
+}
+
+int skinny_splits(int64_t M, int64_t L, int r, int gemv_thr) {
   if (M > 16 || r == 0) return 1;
-  // as many slices as the GEMV takes partial sums (kUParts), each of the 8
-  // waves of a slice keeping at least one 32-wide chunk
+  // each of the 8 waves of a slice keeps at least one 32-wide chunk; the
+  // GEMV sums at most (threads / (M r)) * kUParts partial sums per element
+  const int64_t mr = M * r;
+  const int64_t groups = mr <= gemv_thr ? gemv_thr / mr : 1;
   int64_t ks = (L >> 5) / 8;
-  if (ks > kUParts) ks = kUParts;
+  if (ks > groups * kUParts) ks = groups * kUParts;
+  if (ks > kDecodeMaxSlices) ks = kDecodeMaxSlices;
   return ks < 1 ? 1 : static_cast<int>(ks);
 }
 
@@ -555,8 +593,7 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   // About 16 resident waves per CU in one round: waves per band from
   // 4096 / bands (4, 8 or 16), blocks per wave the smallest of 4, 8, 12, 16
   // that covers the row (longer rows: 16 per pass, several passes).
-  int wv = 4;
-  while (wv < 16 && nbands * wv * 2 <= 4096) wv *= 2;
+  const int wv = gemv_threads(w.N, w.K) / 64;
   const int64_t need = (nblk + wv - 1) / wv;
   int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 12 ? 12 : 16;
   if (wv == 16 && sb == 16) sb = 12;  // 16 x 16 would spill at 1024 threads

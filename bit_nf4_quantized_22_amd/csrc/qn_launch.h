@@ -31,8 +31,16 @@ hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_
                          uint16_t* out_bf16, int ksplit, hipStream_t s);
 // out[C, L] = in[L, C]^T (bf16, C <= 128).
 hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out, hipStream_t s);
-// Number of L-slices launch_skinny uses for the decode path (M <= 16).
-int skinny_splits(int64_t M, int64_t L, int r);
+// Largest number of L-slices of the decode LoRA-down (the forward
+// workspace holds that many fp32 partial sums of u).
+constexpr int kDecodeMaxSlices = 512;
+
+// Threads per workgroup of the decode GEMV for an N x K weight.
+int gemv_threads(int64_t N, int64_t K);
+// Number of L-slices launch_skinny uses for the decode path (M <= 16),
+// given the GEMV's threads per workgroup (which bounds the partial sums it
+// can take).
+int skinny_splits(int64_t M, int64_t L, int r, int gemv_thr);
 
 // Decode path (M <= 16): y = x W^T + s u B^T with u given as usplit fp32
 // partial sums [usplit][M][r]; optionally writes bf16(u) to u_out.
