@@ -13,20 +13,20 @@
 //
 // Tiling.  Workgroup tile BM x BN = 128 x 128, 4 waves in a 2 x 2 grid, each
 // wave 64 x 64 = 2 x 2 tiles of the 32x32x16 bf16 MFMA; K step 64 (one
-// quantisation block).  LDS double-buffered (rows padded by 16 bytes, 74 KB
-// per workgroup) so two workgroups share a CU and the hardware overlaps one
-// workgroup's dequantise/LDS phase with the other's MFMAs.  The global
-// loads of step k+1 are issued before the MFMAs of step k and written to
-// the other LDS buffer after them.  (Measured on MI355X: deeper register
-// prefetch, a branch-free loop with clamped loads, an XCD-grouped tile
-// order and a 128 x 256 tile with the weight decoded into MFMA registers
-// were all slower than this configuration.)
+// quantisation block).  One LDS buffer per operand (rows padded by 16
+// bytes, 37 KB per workgroup), so several workgroups share a CU and the
+// hardware overlaps one workgroup's dequantise/store phase with another's
+// MFMAs.  The global loads of step k+1 are issued before the MFMAs of step
+// k and written to LDS after them, between two barriers.  (Measured on
+// MI355X: double-buffered LDS, deeper register prefetch, a branch-free loop
+// with clamped loads, an XCD-grouped tile order, 256 x 128 tiles, a
+// replicated decode table and a 128 x 256 tile with the weight decoded into
+// MFMA registers were all slower than this configuration.)
 // The dequantisation is a byte -> (q[hi], q[lo]) lookup in an LDS table,
 // a multiply by the block constant and a packed bf16 conversion.  The
 // forward stages the weight tile row-major ([n][k]); the backward needs 8
 // consecutive n per MFMA lane, so it writes the dequantised tile transposed
-// ([k][n]).  The epilogue goes through LDS so the bf16 output is written
-// with 16-byte row-contiguous stores.
+// ([k][n]).
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -37,7 +37,6 @@ namespace {
 
 constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kLD = kBK + 8;    // bf16 per LDS operand row (144 bytes)
-constexpr int kLDC = kBN + 8;   // bf16 per LDS output row
 constexpr int kTM = kBM / 64, kTN = kBN / 64;  // MFMA tiles per wave (wave tile 64 x 64)
 constexpr int kAChunks = kBM * 8 / 256;        // 16-byte activation chunks per thread
 
@@ -175,8 +174,8 @@ __device__ __forceinline__ void mma_steps(const uint16_t* __restrict__ sA,
 
 template <bool kBwd>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[1][kBM * kLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[1][kBN * kLD];
   __shared__ float2 spair[256];
   const int t = threadIdx.x;
   fill_pair_f32(spair, P, 1);
@@ -201,10 +200,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) 
   store_step<kBwd>(g, pf, spair, sA[0], sB[0]);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
     if (kt + 1 < nk) load_step<kBwd>(g, m0, c0, kt + 1, pf);
-    mma_steps(sA[cur], sB[cur], kBK / 16, acc);
-    if (kt + 1 < nk) store_step<kBwd>(g, pf, spair, sA[cur ^ 1], sB[cur ^ 1]);
+    mma_steps(sA[0], sB[0], kBK / 16, acc);
+    __syncthreads();
+    if (kt + 1 < nk) store_step<kBwd>(g, pf, spair, sA[0], sB[0]);
     __syncthreads();
   }
 
@@ -235,9 +234,9 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) 
     __syncthreads();
   }
 
-  // Epilogue: accumulators -> bf16 tile in LDS -> 16-byte row stores.
-  uint16_t* sC = &sA[0][0];
-  static_assert(kBM * kLDC <= 2 * kBM * kLD, "output tile must fit in the activation buffers");
+  // Epilogue: accumulators straight to bf16 in HBM.  Lane (li, lg) of an
+  // MFMA tile holds column li of rows 8 (v / 4) + 4 lg + v % 4, so each
+  // store instruction writes 32 consecutive columns of two rows.
   {
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -250,16 +249,10 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) 
         for (int v = 0; v < 16; ++v) {
           const int row = wm * (kBM / 2) + i * 32 + 8 * (v >> 2) + 4 * lg + (v & 3);
           const int col = wn * (kBN / 2) + j * 32 + li;
-          sC[row * kLDC + col] = static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.f) & 0xFFFF);
+          const int64_t m = m0 + row, n = c0 + col;
+          if (m < g.M && n < ncols)
+            g.out[m * ncols + n] = static_cast<uint16_t>(pack_bf16x2(acc[i][j][v], 0.f) & 0xFFFF);
         }
-  }
-  __syncthreads();
-  for (int c = t; c < kBM * (kBN / 8); c += 256) {
-    const int row = c / (kBN / 8), col = (c % (kBN / 8)) * 8;
-    const int64_t m = m0 + row, n = c0 + col;
-    if (m < g.M && n < ncols)
-      *reinterpret_cast<uint4*>(g.out + m * ncols + n) =
-          *reinterpret_cast<const uint4*>(sC + row * kLDC + col);
   }
 }
 
