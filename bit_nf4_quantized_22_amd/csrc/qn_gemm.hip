@@ -13,15 +13,13 @@
 //
 // Tiling.  Workgroup tile BM x BN = 128 x 128, 4 waves in a 2 x 2 grid, each
 // wave 64 x 64 = 2 x 2 tiles of the 32x32x16 bf16 MFMA; K step 64 (one
-// quantisation block).  One LDS buffer per operand (rows padded by 16
-// bytes, 37 KB per workgroup), so several workgroups share a CU and the
-// hardware overlaps one workgroup's dequantise/store phase with another's
-// MFMAs.  The global loads of step k+1 are issued before the MFMAs of step
-// k and written to LDS after them, between two barriers.  (Measured on
-// MI355X: double-buffered LDS, deeper register prefetch, a branch-free loop
-// with clamped loads, an XCD-grouped tile order, 256 x 128 tiles, a
-// replicated decode table and a 128 x 256 tile with the weight decoded into
-// MFMA registers were all slower than this configuration.)
+// quantisation block).  Two LDS buffers per operand (rows padded by 16
+// bytes, 74 KB per workgroup, two workgroups per CU).  While the MFMAs of
+// step k read one buffer, the same waves dequantise step k+1 from registers
+// into the other, a quarter per 16-deep MFMA step, and the global loads of
+// step k+2 are in flight: one barrier per K step.  All global loads are
+// unconditional (edge rows re-read a valid row), which keeps the compiler
+// from serialising them behind branches.
 // The dequantisation is a byte -> (q[hi], q[lo]) lookup in an LDS table,
 // a multiply by the block constant and a packed bf16 conversion.  The
 // forward stages the weight tile row-major ([n][k]); the backward needs 8
@@ -56,9 +54,11 @@ struct GemmArgs {
 // Registers of the next K step: activation chunks, one 16-byte weight chunk
 // (32 codes of one block) and its block constant (q8 code + group
 // constant, or absmax).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 struct Prefetch {
-  uint4 a[kAChunks];
-  uint4 w;
+  u32x4 a[kAChunks];
+  u32x4 w;
   uint32_t q8;
   float c;
 };
@@ -68,87 +68,99 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Dequantise 32 consecutive codes (16 packed bytes, one block constant) to
-// 16 bf16 pairs.
-__device__ __forceinline__ void decode32(const float2* __restrict__ spair, const uint4& pk,
-                                         float cs, uint32_t out[16]) {
-  const uint32_t words[4] = {pk.x, pk.y, pk.z, pk.w};
-#pragma unroll
-  for (int wi = 0; wi < 4; ++wi)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const float2 pr = spair[(words[wi] >> (8 * b)) & 0xFF];
-      out[4 * wi + b] = pack_bf16x2(__fmul_rn(pr.x, cs), __fmul_rn(pr.y, cs));
-    }
-}
-
 // Global loads of contraction step kt into registers.
 //   activation: thread t owns rows (t/8) + 32 i, 16 bytes at column 8 (t%8)
 //   forward weight: thread t owns row c0 + t/2, codes k0 + 32 (t%2) .. +32
 //   backward weight: thread t owns row k0 + t%64, codes c0 + 32 (t/64) .. +32
-template <bool kBwd>
+template <bool kBwd, bool kDQ>
 __device__ __forceinline__ void load_step(const GemmArgs& g, int64_t m0, int64_t c0, int kt,
                                           Prefetch& pf) {
   const int t = threadIdx.x;
   const int64_t L = kBwd ? g.N : g.K;
   const int64_t k0 = static_cast<int64_t>(kt) * kBK;
+  // Rows past M and weight rows/columns past the output edge re-read a
+  // valid row: they only feed outputs that are never stored.
 #pragma unroll
   for (int i = 0; i < kAChunks; ++i) {
     const int row = (t >> 3) + 32 * i, col = (t & 7) * 8;
-    const int64_t m = m0 + row;
-    pf.a[i] = m < g.M ? *reinterpret_cast<const uint4*>(g.act + m * L + k0 + col)
-                      : make_uint4(0, 0, 0, 0);
+    const int64_t m = m0 + row < g.M ? m0 + row : g.M - 1;
+    pf.a[i] = *reinterpret_cast<const u32x4*>(g.act + m * L + k0 + col);
   }
   int64_t n, k;
   if constexpr (kBwd) {
     n = k0 + (t & 63);
     k = c0 + 32 * (t >> 6);
+    k = k < g.K ? k : g.K - 32;
   } else {
     n = c0 + (t >> 1);
     k = k0 + 32 * (t & 1);
+    n = n < g.N ? n : g.N - 1;
   }
-  const bool live = kBwd ? (k < g.K) : (n < g.N);
-  pf.w = make_uint4(0, 0, 0, 0);
-  pf.q8 = 0;
-  pf.c = 0.f;
-  if (live) {
-    pf.w = *reinterpret_cast<const uint4*>(g.packed + n * (g.K >> 1) + (k >> 1));
-    const int64_t bi = n * (g.K >> 6) + (k >> 6);
-    if (g.qscale) {
-      pf.q8 = g.qscale[bi];
-      pf.c = g.gscale[bi >> 8];
-    } else {
-      pf.c = g.absmax[bi];
-    }
+  pf.w = *reinterpret_cast<const u32x4*>(g.packed + n * (g.K >> 1) + (k >> 1));
+  const int64_t bi = n * (g.K >> 6) + (k >> 6);
+  if constexpr (kDQ) {
+    pf.q8 = g.qscale[bi];
+    pf.c = g.gscale[bi >> 8];
+  } else {
+    pf.q8 = 0;
+    pf.c = g.absmax[bi];
   }
 }
 
-// Registers -> LDS buffer (dequantising the weight chunk).
+// Block constant of a prefetched weight chunk.
+template <bool kDQ>
+__device__ __forceinline__ float chunk_scale(const Prefetch& pf) {
+  return kDQ ? __fmul_rn(l8_value(pf.q8), pf.c) : pf.c;
+}
+
+// Part i (of 4) of the register -> LDS store of one K step: activation
+// chunk i as is, weight word i (8 codes) dequantised.
 template <bool kBwd>
-__device__ __forceinline__ void store_step(const GemmArgs& g, const Prefetch& pf,
+__device__ __forceinline__ void store_part(int i, const Prefetch& pf, float cs,
                                            const float2* __restrict__ spair,
                                            uint16_t* __restrict__ sA, uint16_t* __restrict__ sB) {
   const int t = threadIdx.x;
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
+  if (i < kAChunks) {
     const int row = (t >> 3) + 32 * i, col = (t & 7) * 8;
-    *reinterpret_cast<uint4*>(sA + row * kLD + col) = pf.a[i];
+    *reinterpret_cast<u32x4*>(sA + row * kLD + col) = pf.a[i];
   }
-  const float cs = g.qscale ? __fmul_rn(l8_value(pf.q8), pf.c) : pf.c;
-  uint32_t d[16];
-  decode32(spair, pf.w, cs, d);
+  const uint32_t word = pf.w[i];
+  uint32_t d[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float2 pr = spair[(word >> (8 * b)) & 0xFF];
+    d[b] = pack_bf16x2(__fmul_rn(pr.x, cs), __fmul_rn(pr.y, cs));
+  }
   if constexpr (kBwd) {
     const int row = t & 63, q = t >> 6;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sB[(32 * q + 2 * i) * kLD + row] = static_cast<uint16_t>(d[i] & 0xFFFF);
-      sB[(32 * q + 2 * i + 1) * kLD + row] = static_cast<uint16_t>(d[i] >> 16);
+    for (int b = 0; b < 4; ++b) {
+      sB[(32 * q + 8 * i + 2 * b) * kLD + row] = static_cast<uint16_t>(d[b] & 0xFFFF);
+      sB[(32 * q + 8 * i + 2 * b + 1) * kLD + row] = static_cast<uint16_t>(d[b] >> 16);
     }
   } else {
-    uint4* dst = reinterpret_cast<uint4*>(sB + (t >> 1) * kLD + 32 * (t & 1));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) dst[i] = make_uint4(d[4 * i], d[4 * i + 1], d[4 * i + 2], d[4 * i + 3]);
+    *reinterpret_cast<u32x4*>(sB + (t >> 1) * kLD + 32 * (t & 1) + 8 * i) = u32x4{d[0], d[1], d[2], d[3]};
   }
+}
+
+// One 16-deep MFMA step of the wave's 64 x 64 tile from LDS.
+__device__ __forceinline__ void mma_k16(const uint16_t* __restrict__ sA,
+                                        const uint16_t* __restrict__ sB, int kk,
+                                        f32x16_t (&acc)[kTM][kTN]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, lg = lane >> 5;
+  uint4 a[kTM], b[kTN];
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+    a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kLD + kk * 16 + 8 * lg);
+#pragma unroll
+  for (int j = 0; j < kTN; ++j)
+    b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+#pragma unroll
+    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
 }
 
 __device__ __forceinline__ void mma_steps(const uint16_t* __restrict__ sA,
@@ -172,19 +184,18 @@ __device__ __forceinline__ void mma_steps(const uint16_t* __restrict__ sA,
   }
 }
 
-template <bool kBwd>
+template <bool kBwd, bool kDQ>
 __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[1][kBM * kLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[1][kBN * kLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLD];
   __shared__ float2 spair[256];
   const int t = threadIdx.x;
   fill_pair_f32(spair, P, 1);
 
   const int64_t m0 = static_cast<int64_t>(blockIdx.y) * kBM;
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kBN;  // output column tile
-  const int64_t L = kBwd ? g.N : g.K;
   const int64_t ncols = kBwd ? g.K : g.N;
-  const int nk = static_cast<int>(L / kBK);
+  const int nk = static_cast<int>((kBwd ? g.N : g.K) / kBK);
 
   f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -194,18 +205,38 @@ __global__ __launch_bounds__(256, 2) void gemm_kernel(GemmArgs g, CodeParams P) 
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  Prefetch pf;
-  load_step<kBwd>(g, m0, c0, 0, pf);
+  // Two register sets and two LDS buffers.  While the MFMAs consume step k
+  // from LDS buffer k % 2, the same waves dequantise step k + 1 (loaded one
+  // step earlier) into the other buffer, and the loads of step k + 2 are in
+  // flight: one barrier per K step.  Steps past the end re-load the last
+  // step; what they store is never read.
+  Prefetch p0, p1;
+  load_step<kBwd, kDQ>(g, m0, c0, 0, p0);
+  load_step<kBwd, kDQ>(g, m0, c0, nk > 1 ? 1 : 0, p1);
   __syncthreads();  // spair visible
-  store_step<kBwd>(g, pf, spair, sA[0], sB[0]);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) load_step<kBwd>(g, m0, c0, kt + 1, pf);
-    mma_steps(sA[0], sB[0], kBK / 16, acc);
-    __syncthreads();
-    if (kt + 1 < nk) store_step<kBwd>(g, pf, spair, sA[0], sB[0]);
-    __syncthreads();
+  {
+    const float cs = chunk_scale<kDQ>(p0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) store_part<kBwd>(i, p0, cs, spair, sA[0], sB[0]);
   }
+  __syncthreads();
+  auto step = [&](int k, Prefetch& dec, Prefetch& ld, int cur) {
+    const int kl = k + 2 < nk ? k + 2 : nk - 1;
+    const float cs = chunk_scale<kDQ>(dec);
+    load_step<kBwd, kDQ>(g, m0, c0, kl, ld);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      mma_k16(sA[cur], sB[cur], kk, acc);
+      store_part<kBwd>(kk, dec, cs, spair, sA[cur ^ 1], sB[cur ^ 1]);
+    }
+    __syncthreads();
+  };
+  int k = 0;
+  for (; k + 1 < nk; k += 2) {
+    step(k, p1, p0, 0);
+    step(k + 1, p0, p1, 1);
+  }
+  if (k < nk) step(k, p1, p0, 0);
 
   // LoRA contraction of depth r, 64 at a time, through buffer 0.
   for (int j0 = 0; j0 < g.r; j0 += kBK) {
@@ -272,7 +303,10 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, x, us, B, r, y};
   const dim3 grid(static_cast<uint32_t>((w.N + kBN - 1) / kBN),
                   static_cast<uint32_t>((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(256), 0, st, g, code_params());
+  if (w.qscale)
+    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(256), 0, st, g, code_params());
+  else
+    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(256), 0, st, g, code_params());
   return hipGetLastError();
 }
 
@@ -283,7 +317,10 @@ hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, dy, ts, A, r, dx};
   const dim3 grid(static_cast<uint32_t>((w.K + kBN - 1) / kBN),
                   static_cast<uint32_t>((M + kBM - 1) / kBM));
-  hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(256), 0, st, g, code_params());
+  if (w.qscale)
+    hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(256), 0, st, g, code_params());
+  else
+    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(256), 0, st, g, code_params());
   return hipGetLastError();
 }
 
