@@ -97,7 +97,32 @@ def train_linear(N, K, M=2048, seed=3, r=16, alpha=32.0, heavy_tail=True, std=0.
                     alpha=alpha)
 
 
+def decoder_layer_projection(targets, idx, std, seed):
+    """bf16 N(0, std) weight of projection ``idx`` of one decoder layer.
+
+    Each projection has its own generator, ``default_rng([seed, idx])``, so
+    one projection can be drawn without drawing the others."""
+    name, n, k = targets[idx]
+    return bf16_bits(_normal(np.random.default_rng([seed, idx]), (n, k), std))
+
+
 def decoder_layer_weights(targets, std, seed):
     """bf16 N(0, std) weights for every projection of one decoder layer."""
-    rng = np.random.default_rng(seed)
-    return [(name, bf16_bits(_normal(rng, (n, k), std))) for (name, n, k) in targets]
+    return [(targets[i][0], decoder_layer_projection(targets, i, std, seed))
+            for i in range(len(targets))]
+
+
+def decoder_layer_linear(targets, idx, M, r, alpha, std, seed):
+    """One projection of a decoder layer as a training-step linear: the
+    weight of ``decoder_layer_projection``, then x [M, K], A [r, K], B [N, r]
+    and dy [M, N] from ``default_rng([seed, 1000 + idx])`` (x, dy N(0, 1);
+    A, B N(0, 0.01))."""
+    name, N, K = targets[idx]
+    W = decoder_layer_projection(targets, idx, std, seed)
+    rng = np.random.default_rng([seed, 1000 + idx])
+    x = bf16_bits(_normal(rng, (M, K), 1.0))
+    A = bf16_bits(_normal(rng, (r, K), 0.01))
+    B = bf16_bits(_normal(rng, (N, r), 0.01))
+    dy = bf16_bits(_normal(rng, (M, N), 1.0))
+    return Workload(name=f"{name} W {N}x{K} bf16 N(0,{std}), M={M}, r={r}", W=W,
+                    W_dtype="bf16", x=x, A=A, B=B, dy=dy, M=M, N=N, K=K, r=r, alpha=alpha)

@@ -4,6 +4,7 @@ oracle-side reference of one quantised layer."""
 import numpy as np
 import torch
 
+import bit_nf4_quantized_22_amd as qn
 from bit_nf4_quantized_22_amd import synth
 from oracle import linear, nf4
 
@@ -59,5 +60,69 @@ def f64(bits):
     return synth.bf16_to_f32(bits).astype(np.float64)
 
 
-__all__ = ["DEV", "bf16_dev", "f32_dev", "to_bits16", "to_np", "weight_dev", "weight_f32",
+TOL = 1e-2
+
+
+def check(name, got, ref, tol=TOL):
+    e = rel_frob(got, ref)
+    print(f"{name}: rel_frob={e:.3e}")
+    assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol}"
+
+
+def quantized_layer(wl, double_quant=True):
+    """Device-quantised weight of a workload and the oracle's quantisation."""
+    qw = qn.quantize_weight(weight_dev(wl.W, wl.W_dtype).reshape(wl.N, wl.K), double_quant)
+    ref = oracle_quant(wl.W, wl.W_dtype, double_quant)
+    return qw, ref
+
+
+def assert_quantized_equal(qw, ref):
+    """Packed codes and (double-quantised) constants bit-identical."""
+    torch.cuda.synchronize()
+    gp = qw.packed.cpu().numpy().ravel()
+    bad = np.nonzero(gp != ref["packed"].ravel())[0]
+    assert bad.size == 0, f"{bad.size} packed bytes differ, first at {bad[:5]}"
+    if ref["q8"] is not None:
+        assert np.array_equal(qw.qscale.cpu().numpy().ravel(), ref["q8"].ravel())
+        assert np.array_equal(qw.gscale.cpu().numpy().ravel().view(np.uint32),
+                              ref["c2"].ravel().view(np.uint32))
+    else:
+        assert np.array_equal(qw.absmax.cpu().numpy().ravel().view(np.uint32),
+                              ref["absmax"].ravel().view(np.uint32))
+
+
+def run_layer_checks(wl, M=None, rows=None, double_quant=True, grads=True, qw=None, ref=None):
+    """Forward, backward to the input and (optionally) the LoRA gradients of
+    one layer against the fp64 oracle; y, dx, u, t on ``rows`` (all rows by
+    default: each row depends only on the same row of x or dy), dA and dB in
+    full."""
+    M = wl.M if M is None else M
+    if qw is None:
+        qw, ref = quantized_layer(wl, double_quant)
+    x_bits, dy_bits = wl.x[:M], wl.dy[:M]
+    x, A, B, dy = bf16_dev(x_bits), bf16_dev(wl.A), bf16_dev(wl.B), bf16_dev(dy_bits)
+    u_out = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
+    t_out = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
+    y = qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha, u_out=u_out)
+    dx = qn.qlora_linear_bwd_dx(qw, dy, A, B, wl.r, wl.alpha, t_out=t_out)
+    if grads:
+        dA, dB = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha)
+        dA2, dB2 = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha, u=u_out, t=t_out)
+    torch.cuda.synchronize()
+    xf, dyf, Af, Bf = f64(x_bits), f64(dy_bits), f64(wl.A), f64(wl.B)
+    sel = np.arange(M) if rows is None else rows
+    What = ref["What"].astype(np.float64)
+    check("y", to_np(y)[sel], linear.linear_forward(xf[sel], What, Af, Bf, wl.alpha, wl.r))
+    check("dx", to_np(dx)[sel], linear.linear_backward_input(dyf[sel], What, Af, Bf, wl.alpha, wl.r))
+    check("u", to_np(u_out)[sel], linear.lora_down(xf[sel], Af))
+    check("t", to_np(t_out)[sel], linear.lora_up_input(dyf[sel], Bf))
+    if grads:
+        rA, rB = linear.lora_grads(xf, dyf, Af, Bf, wl.alpha, wl.r)
+        check("dA", to_np(dA), rA)
+        check("dB", to_np(dB), rB)
+        check("dA(saved u,t)", to_np(dA2), rA)
+        check("dB(saved u,t)", to_np(dB2), rB)
+
+
+__all__ = ["TOL", "check", "quantized_layer", "assert_quantized_equal", "run_layer_checks", "DEV", "bf16_dev", "f32_dev", "to_bits16", "to_np", "weight_dev", "weight_f32",
            "oracle_quant", "rel_frob", "f64", "linear", "nf4", "synth"]

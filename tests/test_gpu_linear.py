@@ -12,49 +12,15 @@ import pytest
 import torch
 
 import bit_nf4_quantized_22_amd as qn
-from tests.gpu_helpers import (bf16_dev, f32_dev, f64, linear, oracle_quant, rel_frob, synth,
-                               to_bits16, to_np, weight_dev)
+from tests.gpu_helpers import (TOL, bf16_dev, check, f32_dev, f64, linear, quantized_layer,
+                               rel_frob, run_layer_checks, synth, to_bits16, to_np)
 
 pytestmark = pytest.mark.gpu
-TOL = 1e-2
 
 
-def _layer(wl, double_quant=True):
-    qw = qn.quantize_weight(weight_dev(wl.W, wl.W_dtype).reshape(wl.N, wl.K), double_quant)
-    ref = oracle_quant(wl.W, wl.W_dtype, double_quant)
-    return qw, ref
-
-
-def _check(name, got, ref, tol=TOL):
-    e = rel_frob(got, ref)
-    print(f"{name}: rel_frob={e:.3e}")
-    assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol}"
-
-
-def _run_all(wl, M=None, rows=None, double_quant=True):
-    M = wl.M if M is None else M
-    qw, ref = _layer(wl, double_quant)
-    x_bits, dy_bits = wl.x[:M], wl.dy[:M]
-    x, A, B, dy = bf16_dev(x_bits), bf16_dev(wl.A), bf16_dev(wl.B), bf16_dev(dy_bits)
-    u_out = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
-    t_out = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
-    y = qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha, u_out=u_out)
-    dx = qn.qlora_linear_bwd_dx(qw, dy, A, B, wl.r, wl.alpha, t_out=t_out)
-    dA, dB = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha)
-    dA2, dB2 = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha, u=u_out, t=t_out)
-    torch.cuda.synchronize()
-    xf, dyf, Af, Bf = f64(x_bits), f64(dy_bits), f64(wl.A), f64(wl.B)
-    sel = np.arange(M) if rows is None else rows
-    What = ref["What"].astype(np.float64)
-    _check("y", to_np(y)[sel], linear.linear_forward(xf[sel], What, Af, Bf, wl.alpha, wl.r))
-    _check("dx", to_np(dx)[sel], linear.linear_backward_input(dyf[sel], What, Af, Bf, wl.alpha, wl.r))
-    rA, rB = linear.lora_grads(xf, dyf, Af, Bf, wl.alpha, wl.r)
-    _check("dA", to_np(dA), rA)
-    _check("dB", to_np(dB), rB)
-    _check("dA(saved u,t)", to_np(dA2), rA)
-    _check("dB(saved u,t)", to_np(dB2), rB)
-    _check("u", to_np(u_out)[sel], linear.lora_down(xf[sel], Af))
-    _check("t", to_np(t_out)[sel], linear.lora_up_input(dyf[sel], Bf))
+_layer = quantized_layer
+_check = check
+_run_all = run_layer_checks
 
 
 @pytest.mark.parametrize("M", [1, 16, 17, 33, 200])
@@ -81,6 +47,21 @@ def test_decode_gemv_4096(M):
     want = linear.linear_forward(f64(wl.x), ref["What"].astype(np.float64), f64(wl.A), f64(wl.B),
                                  wl.alpha, wl.r)
     _check(f"y M={M}", to_np(y), want)
+
+
+@pytest.mark.parametrize("M", [1, 5, 16])
+def test_decode_gemv_rank64(M):
+    # r = 64, alpha = 16 (the largest LoRA setting the tests use) on the decode path
+    wl = synth.decode_layer(M, 4096, 4096, seed=2, r=64, alpha=16.0)
+    qw, ref = _layer(wl)
+    u = torch.empty((M, wl.r), dtype=torch.bfloat16, device="cuda:0")
+    y = qn.qlora_linear_fwd(qw, bf16_dev(wl.x), bf16_dev(wl.A), bf16_dev(wl.B), wl.r, wl.alpha,
+                            u_out=u)
+    torch.cuda.synchronize()
+    want = linear.linear_forward(f64(wl.x), ref["What"].astype(np.float64), f64(wl.A), f64(wl.B),
+                                 wl.alpha, wl.r)
+    _check(f"y r=64 M={M}", to_np(y), want)
+    _check(f"u r=64 M={M}", to_np(u), linear.lora_down(f64(wl.x), f64(wl.A)))
 
 
 @pytest.mark.parametrize("shape", [(4096, 11008), (11008, 4096)])
