@@ -18,6 +18,12 @@ weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
             graphs are replayed each step: at 6-15 us per call, eager Python
             launches would measure the host, not the GPU.
 
+After the K steps, "quantise_65b" times the quantiser (nf4_quantize +
+dq_quantize_scales) over 80 layers of the 65B shapes (7 projections,
+809.5M weights per layer): 8 distinct device-resident layers of bf16
+N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
+beyond the Infinity Cache) quantised in turn 10 times over.
+
 Inputs are resident in HBM before the timed region.  Every phase is timed
 with HIP events on the stream the library launches on (torch's current
 stream); the K timed steps are bracketed by synchronisations.
@@ -51,6 +57,7 @@ M_TRAIN, RANK, ALPHA = 2048, 16, 32.0
 DECODE_M = (1, 4, 16)
 GEMV_HEADLINE = (4096, 11008, 1)
 ROTATE_BYTES = 512 << 20
+Q65_LAYERS, Q65_DISTINCT = 80, 8
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fwd_mlp_shapes_m2048_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "bit_nf4_quantized_22_amd", "csrc", "qn_gemm.hip")
 
@@ -142,6 +149,49 @@ def cpu_baseline(workloads):
                       "4096x11008, fp64 fwd+bwd_dx over all 2048 tokens (r=16) repeated "
                       f"{reps}x, LoRA grads once; {total:.1f} s wall, fwd+bwd {t_gemm:.1f} s; "
                       f"cpu_count={os.cpu_count()}"}
+
+
+def quantise_65b(qn, torch, dev, synth):
+    """Quantiser throughput over Q65_LAYERS layers of the 65B shapes."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    layers = []
+    for _ in range(Q65_DISTINCT):
+        proj = []
+        for (_, n, k) in synth.LLAMA65B_TARGETS:
+            w = (torch.randn(n * k, generator=gen, device=dev) * 0.015).to(torch.bfloat16)
+            proj.append((w, torch.empty(n * k // 2, dtype=torch.uint8, device=dev),
+                         torch.empty(n * k // 64, dtype=torch.float32, device=dev),
+                         torch.empty(n * k // 64, dtype=torch.uint8, device=dev),
+                         torch.empty(-(-n * k // (64 * 256)), dtype=torch.float32, device=dev)))
+        layers.append(proj)
+    numel = sum(n * k for (_, n, k) in synth.LLAMA65B_TARGETS)
+
+    def run():
+        for i in range(Q65_LAYERS):
+            for (w, packed, absmax, q8, c2) in layers[i % Q65_DISTINCT]:
+                qn.nf4_quantize(w, packed, absmax)
+                qn.dq_quantize_scales(absmax, q8, c2)
+
+    run()  # warm-up
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    run()
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e)
+    # read bf16 W, write codes + fp32 absmax; DQ: read absmax, write q8 + c2
+    nbytes = Q65_LAYERS * numel * (2 + 0.5 + (4 + 4 + 1) / 64)
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    del layers
+    torch.cuda.empty_cache()
+    return {"layers": Q65_LAYERS, "distinct_layers": Q65_DISTINCT,
+            "weights_per_layer": numel, "ms": round(ms, 3),
+            "ms_per_layer": round(ms / Q65_LAYERS, 4),
+            "weights_per_s": round(Q65_LAYERS * numel / (ms * 1e-3), 1),
+            "GBps": round(gbps, 1), "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def main():
@@ -337,6 +387,7 @@ def main():
                      "traffic": traffic,
                      "us_per_launch": round(fwd_us_per_launch, 2)},
     }
+    out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(workloads)
     print(json.dumps(out))
