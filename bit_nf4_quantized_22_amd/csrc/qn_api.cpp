@@ -32,7 +32,7 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   if (!w || !w->packed) return QN_ERR_NULL;
   if (w->blocksize != kBlock || w->group != kGroup) return QN_ERR_UNSUPPORTED;
   if (w->N < 0 || w->K < 0) return QN_ERR_SHAPE;
-  if (linear && (w->N % 64 != 0 || w->K % 64 != 0)) return QN_ERR_SHAPE;
+  if (linear && (w->N <= 0 || w->K <= 0 || w->N % 64 != 0 || w->K % 64 != 0)) return QN_ERR_SHAPE;
   if (w->qscale) {
     if (!w->gscale) return QN_ERR_NULL;
   } else if (!w->absmax) {
@@ -232,7 +232,7 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   if (M < 0 || N < 0 || K < 0 || r < 0) return QN_ERR_SHAPE;
   if (r == 0) return QN_ERR_SHAPE;
   if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
-  if (N % 64 != 0 || K % 64 != 0) return QN_ERR_SHAPE;
+  if (N == 0 || K == 0 || N % 64 != 0 || K % 64 != 0) return QN_ERR_SHAPE;
   if (!dA || !dB) return QN_ERR_NULL;
   if (M > 0 && (!x || !dy || (!u && !A) || (!t && !B))) return QN_ERR_NULL;
   if ((x && !aligned(x, 16)) || (dy && !aligned(dy, 16)) || (A && !aligned(A, 16)) ||

@@ -76,8 +76,9 @@ typedef uint16_t qn_bf16; /* bf16 bit pattern */
  *           iff qscale != NULL.
  *   absmax  fp32[N*K/64]: the block constants themselves; used iff
  *           qscale == NULL.
- *   blocksize must be 64 and group 256.  The linear ops need K % 64 == 0 and
- *   N % 64 == 0, so a block never crosses a row.
+ *   blocksize must be 64 and group 256.  The linear ops (and lora_grads)
+ *   need N and K to be positive multiples of 64, so a block never crosses a
+ *   row; other sizes return QN_ERR_SHAPE.
  */
 typedef struct qn_weight {
   const uint8_t* packed;

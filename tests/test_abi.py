@@ -106,6 +106,14 @@ def test_linear_argument_errors(lib):
     fwd = lib.qlora_linear_fwd
     assert fwd(ctypes.byref(bad), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_need,
                None) == qn.QN_ERR_SHAPE
+    for n, k in ((0, 128), (128, 0)):  # an empty weight is rejected, not multiplied
+        empty = qn.qn_weight(0x100000, None, None, 0x100000, n, k, 64, 256)
+        assert fwd(ctypes.byref(empty), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE,
+                   ws_need, None) == qn.QN_ERR_SHAPE
+        assert lib.qlora_linear_bwd_dx(ctypes.byref(empty), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE,
+                                       None, FAKE, ws_need, None) == qn.QN_ERR_SHAPE
+        assert lib.lora_grads(FAKE, FAKE, None, None, FAKE, FAKE, 32, n, k, 8, 16.0, FAKE, FAKE,
+                              FAKE, ws_need, None) == qn.QN_ERR_SHAPE
     assert fwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None, None, 0,
                None) == qn.QN_ERR_WORKSPACE
     assert fwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_need - 1,
