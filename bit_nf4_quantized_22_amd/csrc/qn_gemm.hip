@@ -12,19 +12,21 @@
 // bf16(s u) (or bf16(s t)), the B-side operand is B (or A^T).
 //
 // Tiling.  Workgroup tile BM x BN = 256 x 128, K step 64 (one quantisation
-// block), one workgroup of 8 waves per CU with two LDS buffers per operand
-// (rows padded by 16 bytes, 112 KB).  The waves are specialised: waves 0-3
-// only read MFMA fragments from LDS and run the 32x32x16 bf16 MFMAs (2 x 2
-// grid of 128 x 64 wave tiles), waves 4-7 only load from HBM and
-// dequantise into LDS, so each SIMD holds one MFMA wave and one producer
-// wave whose LDS latency chains no longer stall the MFMA issue.  While the
-// MFMA waves consume step k from one buffer, the producers fill the other
-// with step k+1 from registers loaded two steps earlier (a ring of three
-// register sets); one barrier per K step.  The 256-row tile halves the
-// dequantisation per flop against 128 rows, which is what bounds the kernel:
-// the producers, not the MFMAs, set the pace.  All global loads are
-// unconditional (edge rows re-read a valid row), which keeps the compiler
-// from serialising them behind branches.
+// block), one workgroup of 8 waves per CU.  The waves are specialised, one
+// of each kind per SIMD:
+//   * waves 0-3 run the 32x32x16 bf16 MFMAs (2 x 2 grid of 128 x 64 wave
+//     tiles) and bring in the activation tile by direct-to-LDS DMA two K
+//     steps ahead (three activation buffers, 128-byte rows with an XOR
+//     swizzle instead of padding, so each 1 KB DMA fills whole rows and the
+//     fragment reads stay free of bank conflicts);
+//   * waves 4-7 load the 4-bit weight and its constants two steps ahead (a
+//     ring of three register sets) and dequantise one step ahead into the
+//     other of two weight buffers.
+// One barrier per K step.  The 256-row tile halves the dequantisation per
+// flop against 128 rows, and moving the activation copy to DMA leaves the
+// producer waves only the dequantisation: they, not the MFMAs, set the
+// pace.  All global loads are unconditional (edge rows re-read a valid
+// row), which keeps the compiler from serialising them behind branches.
 // The dequantisation looks each 4-bit code up in a 64-copy fp32 table in
 // LDS (lane l reads copy l, so a wave never has a bank conflict), multiplies
 // by the block constant and packs to bf16.  The forward stages the weight
@@ -39,15 +41,18 @@ namespace qn {
 namespace {
 
 constexpr int kBM = 256, kBN = 128, kBK = 64;
-constexpr int kLD = kBK + 8;    // bf16 per LDS operand row (padded by 16 bytes)
+constexpr int kLD = kBK + 8;    // bf16 per row of the weight tile in LDS (padded by 16 bytes)
 constexpr int kTM = kBM / 64, kTN = kBN / 64;  // MFMA tiles per wave (wave tile kBM/2 x kBN/2)
-constexpr int kWGPerCU = kBM == 256 ? 1 : 2;
 constexpr int kParts = kBK / 16;               // 16-deep MFMA steps per K step
-constexpr int kAChunks = kBM * kBK / 8 / 256;  // 16-byte activation chunks per thread
-constexpr int kACols = kBK / 8;                // 16-byte chunks per activation row
-constexpr int kCodes = kBN * kBK / 256;        // weight codes per thread per K step
+constexpr int kMmaWaves = 4;                   // 2 x 2 grid of MFMA wave tiles
+constexpr int kProdWaves = 4;                  // dequantising waves
+constexpr int kProd = 64 * kProdWaves;         // producer threads
+constexpr int kThreads = 64 * (kMmaWaves + kProdWaves);
+constexpr int kCodes = kBN * kBK / kProd;      // weight codes per producer thread per K step
+constexpr int kCodeThreads = kBK / kCodes;     // producer threads per weight row (forward)
 constexpr int kWords = kCodes / 8;             // their 32-bit words
-static_assert(kWords * 8 == kCodes, "whole words of codes per thread");
+constexpr int kADma = kBM * kBK * 2 / 1024 / kMmaWaves;  // 1 KB activation DMAs per MFMA wave
+static_assert(kWords * 8 == kCodes && kADma * 1024 * kMmaWaves == kBM * kBK * 2, "tile split");
 
 struct GemmArgs {
   const uint8_t* packed;
@@ -62,14 +67,15 @@ struct GemmArgs {
   uint16_t* out;         // y [M, N] or dx [M, K]
 };
 
-// Registers of the next K step: activation chunks, the thread's weight
-// codes (kCodes consecutive codes of one block) and their block constant
-// (q8 code + group constant, or absmax).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t wvec_t __attribute__((ext_vector_type(kWords)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
+// Registers of one K step of a producer thread: its weight codes (kCodes
+// consecutive codes of one block) and their block constant (q8 code +
+// group constant, or absmax).
 struct Prefetch {
-  u32x4 a[kAChunks];
   wvec_t w;
   uint32_t q8;
   float c;
@@ -80,32 +86,29 @@ __device__ __forceinline__ f32x16_t mfma32(const uint4& a, const uint4& b, f32x1
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-// Global loads of contraction step kt into registers.
-//   activation: thread t owns rows t / kACols + (256 / kACols) i, 16 bytes
-//     at column 8 (t % kACols)
-//   forward weight: thread t owns row c0 + t/2, codes k0 + kCodes (t%2) ..
-//   backward weight: thread t owns row k0 + t % kBK, codes c0 + kCodes (t / kBK) ..
+// Activation tile layout in LDS: kBM rows of 128 bytes (8 chunks of 16 B),
+// chunk c of row r in slot c ^ swz(r).  The swizzle makes the MFMA
+// fragment reads (16 lanes = 16 consecutive rows, one chunk) hit 16
+// distinct 4-bank groups without padding, so a 1 KB DMA fills 8 whole rows.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
+
+// Weight loads of contraction step kt (producer thread t):
+//   forward: row c0 + t / kCodeThreads, codes k0 + kCodes (t % kCodeThreads) ..
+//   backward: row k0 + t % kBK, codes c0 + kCodes (t / kBK) ..
+// Weight rows/columns past the output edge re-read a valid one: they only
+// feed outputs that are never stored.
 template <bool kBwd, bool kDQ>
-__device__ __forceinline__ void load_step(const GemmArgs& g, int64_t m0, int64_t c0, int kt,
-                                          Prefetch& pf, int t) {
-  const int64_t L = kBwd ? g.N : g.K;
+__device__ __forceinline__ void load_step(const GemmArgs& g, int64_t c0, int kt, Prefetch& pf,
+                                          int t) {
   const int64_t k0 = static_cast<int64_t>(kt) * kBK;
-  // Rows past M and weight rows/columns past the output edge re-read a
-  // valid row: they only feed outputs that are never stored.
-#pragma unroll
-  for (int i = 0; i < kAChunks; ++i) {
-    const int row = t / kACols + (256 / kACols) * i, col = (t % kACols) * 8;
-    const int64_t m = m0 + row < g.M ? m0 + row : g.M - 1;
-    pf.a[i] = *reinterpret_cast<const u32x4*>(g.act + m * L + k0 + col);
-  }
   int64_t n, k;
   if constexpr (kBwd) {
     n = k0 + (t % kBK);
     k = c0 + kCodes * (t / kBK);
     k = k < g.K ? k : g.K - kCodes;
   } else {
-    n = c0 + (t >> 1);
-    k = k0 + kCodes * (t & 1);
+    n = c0 + t / kCodeThreads;
+    k = k0 + kCodes * (t % kCodeThreads);
     n = n < g.N ? n : g.N - 1;
   }
   pf.w = *reinterpret_cast<const wvec_t*>(g.packed + n * (g.K >> 1) + (k >> 1));
@@ -125,15 +128,13 @@ __device__ __forceinline__ float chunk_scale(const Prefetch& pf) {
   return kDQ ? __fmul_rn(l8_value(pf.q8), pf.c) : pf.c;
 }
 
-// Register -> LDS store of one K step: the weight codes dequantised, then
-// the activation chunks as they are.  All table lookups are issued first
-// and the LDS stores last, so the in-order LDS return queue holds only
-// lookups while the arithmetic waits on them.
+// Dequantise one K step of weight codes into the LDS weight tile.  All
+// table lookups are issued first, so the in-order LDS return queue holds
+// only lookups while the arithmetic waits on them.
 template <bool kBwd>
 __device__ __forceinline__ void store_step(const Prefetch& pf, float cs,
                                            const float* __restrict__ scode,
-                                           uint16_t* __restrict__ sA, uint16_t* __restrict__ sB,
-                                           int t) {
+                                           uint16_t* __restrict__ sB, int t) {
   // Byte b of a word holds element 2b (high nibble) and 2b+1 (low nibble).
   // Code c of lane l sits at byte offset 256 c + 4 l of the 64-copy table,
   // so a wave's 64 lookups hit 64 different banks; the offset is one v_perm
@@ -166,27 +167,75 @@ __device__ __forceinline__ void store_step(const Prefetch& pf, float cs,
         sB[(kCodes * qd + 8 * i + 2 * b + 1) * kLD + row] = static_cast<uint16_t>(d[b] >> 16);
       }
     } else {
-      *reinterpret_cast<u32x4*>(sB + (t >> 1) * kLD + kCodes * (t & 1) + 8 * i) = u32x4{d[0], d[1], d[2], d[3]};
+      *reinterpret_cast<u32x4*>(sB + (t / kCodeThreads) * kLD + kCodes * (t % kCodeThreads) + 8 * i) =
+          u32x4{d[0], d[1], d[2], d[3]};
     }
-  }
-#pragma unroll
-  for (int c = 0; c < kAChunks; ++c) {
-    const int row = t / kACols + (256 / kACols) * c, col = (t % kACols) * 8;
-    *reinterpret_cast<u32x4*>(sA + row * kLD + col) = pf.a[c];
   }
 }
 
-// One 16-deep MFMA step of the wave's 64 x 64 tile from LDS.
+// Per-lane byte offsets of an MFMA wave's activation DMAs: DMA j of wave w
+// fills rows 64 w + 8 j .. +8; lane L writes slot L % 8 of row 64 w + 8 j +
+// L / 8, so it fetches chunk (L % 8) ^ swz(row) of that row.  Rows past M
+// re-read row M - 1.
+struct ADma {
+  uint32_t off[kADma];  // byte offset of the lane's chunk from the tile's row m0, column 0
+};
+
+__device__ __forceinline__ ADma adma_offsets(int64_t m0, int64_t M, int64_t L) {
+  ADma d;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int j = 0; j < kADma; ++j) {
+    const int row = 64 * w + 8 * j + (lane >> 3);
+    const int chunk = (lane & 7) ^ swz(row);
+    const int64_t m = m0 + row < M ? row : M - 1 - m0;
+    d.off[j] = static_cast<uint32_t>(m * L * 2 + chunk * 16);
+  }
+  return d;
+}
+
+// Issue the activation DMAs of K step kt into buffer `dst` (MFMA waves).
+// Written as inline assembly: for a DMA the compiler knows about it waits
+// for every outstanding one at each barrier, which would leave no time for
+// the DMA of step k + 2.  The MFMA waves issue no other vector-memory
+// instruction inside the K loop, so the explicit waits below count exactly
+// these DMAs.  M0 holds the wave's LDS destination; lane L writes 16 bytes
+// at M0 + 16 L.
+__device__ __forceinline__ void adma_issue(const ADma& d, const uint16_t* act_tile, int kt,
+                                           uint16_t* dst) {
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char* base = reinterpret_cast<const char*>(act_tile) + static_cast<int64_t>(kt) * kBK * 2;
+  const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)(dst + 64 * w * kBK)));
+#pragma unroll
+  for (int j = 0; j < kADma; ++j) {
+    const void* src = base + d.off[j];
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(lds + 8 * j * kBK * 2)
+                 : "memory", "m0");
+  }
+}
+
+// Wait until at most one K step of activation DMAs is outstanding.
+__device__ __forceinline__ void adma_wait_one_step() {
+  static_assert(kADma == 8, "the wait count below is kADma");
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+}
+
+// One 16-deep MFMA step of the wave's tile: activation fragments from the
+// swizzled tile, weight fragments from the padded tile.
 __device__ __forceinline__ void mma_k16(const uint16_t* __restrict__ sA,
                                         const uint16_t* __restrict__ sB, int kk,
                                         f32x16_t (&acc)[kTM][kTN]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lg = lane >> 5;
+  const int aslot = (2 * kk + lg) ^ swz(li);  // wave rows start at multiples of 32
   uint4 a[kTM], b[kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
-    a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kLD + kk * 16 + 8 * lg);
+    a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kBK + aslot * 8);
 #pragma unroll
   for (int j = 0; j < kTN; ++j)
     b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
@@ -196,34 +245,12 @@ __device__ __forceinline__ void mma_k16(const uint16_t* __restrict__ sA,
     for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
 }
 
-__device__ __forceinline__ void mma_steps(const uint16_t* __restrict__ sA,
-                                          const uint16_t* __restrict__ sB, int ksteps,
-                                          f32x16_t (&acc)[kTM][kTN]) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int li = lane & 31, lg = lane >> 5;
-  for (int kk = 0; kk < ksteps; ++kk) {
-    uint4 a[kTM], b[kTN];
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-      a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kLD + kk * 16 + 8 * lg);
-#pragma unroll
-    for (int j = 0; j < kTN; ++j)
-      b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
-#pragma unroll
-    for (int i = 0; i < kTM; ++i)
-#pragma unroll
-      for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
-  }
-}
-
 // Output tile of workgroup `bid` (1-D grid over nr x nc tiles).  Workgroups
 // are dealt to the 8 XCDs round-robin (bid % 8) and each XCD has its own
 // L2, so when the tile count divides by 8 each XCD gets one contiguous run
 // of the tile order below: bands of kBandRows row tiles, column-major
 // inside a band.  An XCD then works on a few row tiles x a slice of the
-// columns, which keeps its share of x and W small enough to be reused from
-// its L2 instead of being fetched by all 8 XCDs.
+// columns.
 constexpr int kBandRows = 4;
 
 __device__ __forceinline__ void tile_of(int bid, int nc, int nr, int& row, int& col) {
@@ -238,8 +265,13 @@ __device__ __forceinline__ void tile_of(int bid, int nc, int nr, int& row, int& 
 }
 
 template <bool kBwd, bool kDQ>
-__global__ __launch_bounds__(512, kWGPerCU) void gemm_kernel(GemmArgs g, CodeParams P) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][kBM * kLD];
+__global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParams P) {
+  // Three activation buffers (filled by DMA two steps ahead) and two weight
+  // buffers (dequantised one step ahead).  Separate arrays, so the compiler
+  // can tell a DMA into one activation buffer from reads of another.
+  __shared__ __attribute__((aligned(16))) uint16_t sA0[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA1[kBM * kBK];
+  __shared__ __attribute__((aligned(16))) uint16_t sA2[kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLD];
   __shared__ __attribute__((aligned(16))) float scode[16 * 64];  // q[c] for lane l at [64 c + l]
   const int t = threadIdx.x;
@@ -249,12 +281,13 @@ __global__ __launch_bounds__(512, kWGPerCU) void gemm_kernel(GemmArgs g, CodePar
   }
 
   const int64_t ncols = kBwd ? g.K : g.N;
+  const int64_t L = kBwd ? g.N : g.K;  // contraction length
   int trow, tcol;
   tile_of(blockIdx.x, static_cast<int>((ncols + kBN - 1) / kBN),
           static_cast<int>((g.M + kBM - 1) / kBM), trow, tcol);
   const int64_t m0 = static_cast<int64_t>(trow) * kBM;
   const int64_t c0 = static_cast<int64_t>(tcol) * kBN;  // output column tile
-  const int nk = static_cast<int>((kBwd ? g.N : g.K) / kBK);
+  const int nk = static_cast<int>(L / kBK);
 
   f32x16_t acc[kTM][kTN];
 #pragma unroll
@@ -264,35 +297,31 @@ __global__ __launch_bounds__(512, kWGPerCU) void gemm_kernel(GemmArgs g, CodePar
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  // Waves 0-3 run the MFMAs, waves 4-7 load and dequantise; each SIMD holds
-  // one of each.  Two LDS buffers: while the MFMA waves consume step k from
-  // buffer k % 2, the producer waves dequantise step k + 1 into the other
-  // buffer from registers loaded two steps earlier (a ring of three register
-  // sets, loads of steps k + 2 and k + 3 in flight).  One barrier per K
-  // step.  Steps past the end re-load the last step; what they store is
-  // never read.
-  if (t >= 256) {
-    const int pt = t - 256;
+  // Waves 0-3 run the MFMAs and fetch the activation tiles by DMA; waves
+  // 4-11 load and dequantise the weight.  Per K step k: the MFMA waves
+  // consume activation buffer k % 3 and weight buffer k % 2, and start the
+  // DMA of step k + 2; the producers dequantise step k + 1 (loaded two steps
+  // earlier, a ring of three register sets) into the other weight buffer.
+  // One barrier per K step.  Steps past the end re-load the last step; what
+  // they store is never read.
+  if (t >= 64 * kMmaWaves) {
+    const int pt = t - 64 * kMmaWaves;
     Prefetch p0, p1, p2;
-    load_step<kBwd, kDQ>(g, m0, c0, 0, p0, pt);
-    load_step<kBwd, kDQ>(g, m0, c0, nk > 1 ? 1 : nk - 1, p1, pt);
-    load_step<kBwd, kDQ>(g, m0, c0, nk > 2 ? 2 : nk - 1, p2, pt);
+    load_step<kBwd, kDQ>(g, c0, 0, p0, pt);
+    load_step<kBwd, kDQ>(g, c0, nk > 1 ? 1 : nk - 1, p1, pt);
+    load_step<kBwd, kDQ>(g, c0, nk > 2 ? 2 : nk - 1, p2, pt);
     __syncthreads();  // code table visible
-    {
-      const float cs = chunk_scale<kDQ>(p0);
-      store_step<kBwd>(p0, cs, scode, sA[0], sB[0], pt);
-    }
+    store_step<kBwd>(p0, chunk_scale<kDQ>(p0), scode, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
       const int kl = k + 3 < nk ? k + 3 : nk - 1;
-      const int nxt = (k & 1) ^ 1;
       // Pin the first use of the registers loaded two steps ago here, after
       // the barrier, so the compiler cannot hoist their address arithmetic
       // next to the loads it has just issued and wait for those.
       asm volatile("" : "+v"(dec.w), "+v"(dec.q8), "+v"(dec.c));
       const float cs = chunk_scale<kDQ>(dec);
-      load_step<kBwd, kDQ>(g, m0, c0, kl, ld, pt);
-      store_step<kBwd>(dec, cs, scode, sA[nxt], sB[nxt], pt);
+      load_step<kBwd, kDQ>(g, c0, kl, ld, pt);
+      store_step<kBwd>(dec, cs, scode, sB[(k & 1) ^ 1], pt);
       __syncthreads();
     };
     int k = 0;
@@ -304,26 +333,44 @@ __global__ __launch_bounds__(512, kWGPerCU) void gemm_kernel(GemmArgs g, CodePar
     if (k < nk) step(k, p1, p0);
     if (k + 1 < nk) step(k + 1, p2, p1);
   } else {
+    const ADma ad = adma_offsets(m0, g.M, L);
+    const uint16_t* act_tile = g.act + m0 * L;
+    adma_issue(ad, act_tile, 0, sA0);
+    adma_issue(ad, act_tile, nk > 1 ? 1 : nk - 1, sA1);
     __syncthreads();
+    adma_wait_one_step();  // step 0 landed
     __syncthreads();
-    for (int k = 0; k < nk; ++k) {
-      const int cur = k & 1;
+    auto step = [&](int k, const uint16_t* cur, uint16_t* next2) {
+      adma_issue(ad, act_tile, k + 2 < nk ? k + 2 : nk - 1, next2);
+      const uint16_t* wb = sB[k & 1];
 #pragma unroll
-      for (int kk = 0; kk < kParts; ++kk) mma_k16(sA[cur], sB[cur], kk, acc);
+      for (int kk = 0; kk < kParts; ++kk) mma_k16(cur, wb, kk, acc);
+      adma_wait_one_step();  // step k + 1 landed
       __syncthreads();
+    };
+    int k = 0;
+    for (; k + 2 < nk; k += 3) {
+      step(k, sA0, sA2);
+      step(k + 1, sA1, sA0);
+      step(k + 2, sA2, sA1);
     }
+    if (k < nk) step(k, sA0, sA2);
+    if (k + 1 < nk) step(k + 1, sA1, sA0);
+    // drain the DMAs of the steps past the end before the buffers are reused
+    __builtin_amdgcn_s_waitcnt(0);
   }
+  __syncthreads();
 
-  // LoRA contraction of depth r, kBK at a time, through buffer 0.
+  // LoRA contraction of depth r, kBK at a time, through sA0 and sB[0].
   for (int j0 = 0; j0 < g.r; j0 += kBK) {
-    for (int c = t; c < kBM * kBK; c += 512) {
+    for (int c = t; c < kBM * kBK; c += kThreads) {
       const int row = c / kBK, col = c % kBK;
       const int64_t m = m0 + row;
       uint16_t v = 0;
       if (m < g.M && j0 + col < g.r) v = g.lact[m * g.r + j0 + col];
-      sA[0][row * kLD + col] = v;
+      sA0[row * kBK + (((col >> 3) ^ swz(row)) << 3) + (col & 7)] = v;
     }
-    for (int c = t; c < kBN * kBK; c += 512) {
+    for (int c = t; c < kBN * kBK; c += kThreads) {
       uint16_t v = 0;
       if constexpr (kBwd) {  // sB[kcol][j] = A[j0 + j][c0 + kcol]
         const int kcol = c % kBN, j = c / kBN;
@@ -337,10 +384,11 @@ __global__ __launch_bounds__(512, kWGPerCU) void gemm_kernel(GemmArgs g, CodePar
     }
     __syncthreads();
     const int depth = g.r - j0 < kBK ? g.r - j0 : kBK;
-    if (t < 256) mma_steps(sA[0], sB[0], (depth + 15) >> 4, acc);
+    if (t < 64 * kMmaWaves)
+      for (int kk = 0; kk < (depth + 15) >> 4; ++kk) mma_k16(sA0, sB[0], kk, acc);
     __syncthreads();
   }
-  if (t >= 256) return;
+  if (t >= 64 * kMmaWaves) return;
 
   // Epilogue: accumulators straight to bf16 in HBM.  Lane (li, lg) of an
   // MFMA tile holds column li of rows 8 (v / 4) + 4 lg + v % 4, so each
@@ -380,9 +428,9 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, x, us, B, r, y};
   const dim3 grid(static_cast<uint32_t>(((w.N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
-    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(512), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(kThreads), 0, st, g, code_params());
   else
-    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(512), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(kThreads), 0, st, g, code_params());
   return hipGetLastError();
 }
 
@@ -393,9 +441,9 @@ hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, dy, ts, A, r, dx};
   const dim3 grid(static_cast<uint32_t>(((w.K + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
-    hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(512), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(kThreads), 0, st, g, code_params());
   else
-    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(512), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(kThreads), 0, st, g, code_params());
   return hipGetLastError();
 }
 
