@@ -223,26 +223,56 @@ __device__ __forceinline__ void adma_wait_one_step() {
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
 }
 
-// One 16-deep MFMA step of the wave's tile: activation fragments from the
-// swizzled tile, weight fragments from the padded tile.
-__device__ __forceinline__ void mma_k16(const uint16_t* __restrict__ sA,
-                                        const uint16_t* __restrict__ sB, int kk,
-                                        f32x16_t (&acc)[kTM][kTN]) {
+// MFMA fragments of one 16-deep step of the wave's tile: activation rows
+// from the swizzled tile, weight rows from the padded tile.
+struct Frags {
+  uint4 a[kTM], b[kTN];
+};
+
+__device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sA,
+                                           const uint16_t* __restrict__ sB, int kk, Frags& f) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int li = lane & 31, lg = lane >> 5;
   const int aslot = (2 * kk + lg) ^ swz(li);  // wave rows start at multiples of 32
-  uint4 a[kTM], b[kTN];
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
-    a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kBK + aslot * 8);
+    f.a[i] = *reinterpret_cast<const uint4*>(sA + (wm * (kBM / 2) + i * 32 + li) * kBK + aslot * 8);
 #pragma unroll
   for (int j = 0; j < kTN; ++j)
-    b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
+    f.b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
+}
+
+__device__ __forceinline__ void mma_frags(const Frags& f, f32x16_t (&acc)[kTM][kTN]) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
 #pragma unroll
-    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32(a[i], b[j], acc[i][j]);
+    for (int j = 0; j < kTN; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
+}
+
+__device__ __forceinline__ void mma_k16(const uint16_t* __restrict__ sA,
+                                        const uint16_t* __restrict__ sB, int kk,
+                                        f32x16_t (&acc)[kTM][kTN]) {
+  Frags f;
+  load_frags(sA, sB, kk, f);
+  mma_frags(f, acc);
+}
+
+// One K step (kParts 16-deep steps) with the fragments of step kk + 1 in
+// flight while the MFMAs of step kk run.
+__device__ __forceinline__ void mma_step(const uint16_t* __restrict__ sA,
+                                         const uint16_t* __restrict__ sB,
+                                         f32x16_t (&acc)[kTM][kTN]) {
+  static_assert(kParts % 2 == 0, "fragment double buffer");
+  Frags f0, f1;
+  load_frags(sA, sB, 0, f0);
+#pragma unroll
+  for (int kk = 0; kk < kParts; kk += 2) {
+    load_frags(sA, sB, kk + 1, f1);
+    mma_frags(f0, acc);
+    if (kk + 2 < kParts) load_frags(sA, sB, kk + 2, f0);
+    mma_frags(f1, acc);
+  }
 }
 
 // Output tile of workgroup `bid` (1-D grid over nr x nc tiles).  Workgroups
@@ -342,9 +372,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     __syncthreads();
     auto step = [&](int k, const uint16_t* cur, uint16_t* next2) {
       adma_issue(ad, act_tile, k + 2 < nk ? k + 2 : nk - 1, next2);
-      const uint16_t* wb = sB[k & 1];
-#pragma unroll
-      for (int kk = 0; kk < kParts; ++kk) mma_k16(cur, wb, kk, acc);
+      mma_step(cur, sB[k & 1], acc);
       adma_wait_one_step();  // step k + 1 landed
       __syncthreads();
     };
