@@ -52,16 +52,23 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
 
 // Forward workspace: fp32 u (up to 16 partial sums of it on the decode
 // path) followed by bf16(s u).
-size_t fwd_u32_bytes(int64_t M, int32_t r) {
+// fp32 partial sums of u (or t) over L-slices: up to kDecodeMaxSlices of
+// them on the decode path, kWideMaxSlices for token batches.
+size_t lora_part_bytes(int64_t M, int32_t r) {
   const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  // decode: up to kDecodeMaxSlices partial sums of u
-  return round_up(mr * 4 * (M <= kGemvMaxM ? static_cast<size_t>(qn::kDecodeMaxSlices) : 1), 256);
+  const size_t slices = M <= kGemvMaxM ? qn::kDecodeMaxSlices : qn::kWideMaxSlices;
+  return round_up(mr * 4 * slices, 256);
 }
 
+// bf16(s u) or bf16(s t), the LoRA operand of the fused GEMM.
+size_t lora_bf16_bytes(int64_t M, int32_t r) {
+  return round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256);
+}
+
+// Forward workspace: the partial sums of u, then bf16(s u).
 size_t fwd_ws(int64_t M, int32_t r) {
   if (r == 0 || M == 0) return 0;
-  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  return fwd_u32_bytes(M, r) + round_up(mr * 2, 256);
+  return lora_part_bytes(M, r) + lora_bf16_bytes(M, r);
 }
 
 // B^T [r, N] bf16: the row-major operand of t = dy B.
@@ -69,10 +76,11 @@ size_t bt_bytes(int64_t N, int32_t r) {
   return round_up(static_cast<size_t>(N) * static_cast<size_t>(r) * 2, 256);
 }
 
-// Backward workspace: bf16(s t) followed by B^T.
+// Backward workspace: the partial sums of t, bf16(s t), then B^T.
 size_t bwd_ws(int64_t M, int64_t N, int32_t r) {
   if (r == 0 || M == 0) return 0;
-  return round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256) + bt_bytes(N, r);
+  return lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) + lora_bf16_bytes(M, r) +
+         bt_bytes(N, r);
 }
 
 // Gradient workspace: fp32 u, fp32 t, B^T, split-M partial sums.
@@ -177,20 +185,25 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  // u = x A^T as fp32 partial sums over L-slices, added up (in slice order)
+  // by the GEMV or GEMM that applies the LoRA-up term
   float* u32 = nullptr;
-  uint16_t* us = nullptr;
   const bool decode = M <= kGemvMaxM;
-  const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K)) : 1;
+  const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K))
+                        : qn::skinny_wide_splits(M, w->K);
   if (r > 0) {
     u32 = static_cast<float*>(ws);
-    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + fwd_u32_bytes(M, r));
-    hipError_t e = decode ? qn::launch_skinny(x, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s)
-                          : qn::launch_skinny(x, M, w->K, A, r, scale, nullptr, us, u_out, 1, s);
-    if (e != hipSuccess) return QN_ERR_HIP;
+    if (qn::launch_skinny(x, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s) != hipSuccess)
+      return QN_ERR_HIP;
   }
   if (decode)
     return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, ks, B, r, scale, y,
                                       r > 0 ? u_out : nullptr, s));
+  uint16_t* us = nullptr;
+  if (r > 0) {
+    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(M, r));
+    if (qn::launch_lora_reduce(u32, ks, M * r, scale, us, u_out, s) != hipSuccess) return QN_ERR_HIP;
+  }
   return hip_status(qn::launch_gemm_fwd(v, x, M, us, B, r, y, s));
 }
 
@@ -214,14 +227,20 @@ int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const 
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  // t = dy B (through B^T, so both operands are row-major) as fp32 partial
+  // sums over N-slices, added up by the GEMM
   uint16_t* ts = nullptr;
+  const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
+  const int ks = qn::skinny_wide_splits(mp, w->N);
   if (r > 0) {
-    ts = static_cast<uint16_t*>(ws);
-    uint16_t* bt = reinterpret_cast<uint16_t*>(
-        static_cast<char*>(ws) + round_up(static_cast<size_t>(M) * static_cast<size_t>(r) * 2, 256));
+    float* t32 = static_cast<float*>(ws);
+    ts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r));
+    uint16_t* bt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r) +
+                                               lora_bf16_bytes(M, r));
     if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
-    hipError_t e = qn::launch_skinny(dy, M, w->N, bt, r, scale, nullptr, ts, t_out, 1, s);
-    if (e != hipSuccess) return QN_ERR_HIP;
+    if (qn::launch_skinny(dy, M, w->N, bt, r, scale, t32, nullptr, nullptr, ks, s) != hipSuccess)
+      return QN_ERR_HIP;
+    if (qn::launch_lora_reduce(t32, ks, M * r, scale, ts, t_out, s) != hipSuccess) return QN_ERR_HIP;
   }
   return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
 }

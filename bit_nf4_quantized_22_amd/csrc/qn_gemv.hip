@@ -41,29 +41,35 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_
 // ---------------------------------------------------------------------------
 // Skinny projection out[M, r] = in[M, L] * P^T, P row-major [r, L].
 //
-// Grid: (16-row tiles of `in`) x ksplit L-slices; kWaves waves per workgroup
-// split the slice in 32-wide chunks, wave w taking chunks w, w + kWaves, ...
-// Each round a wave issues the loads of kCh chunks (x: one 16-byte load per
-// lane per chunk; P: one per lane per 16-column tile) before any MFMA, so a
-// round costs one memory latency.  16x16x32 MFMA with in-rows on the M side
-// and kCols column tiles of 16 (r <= 16 kCols).
+// Grid: (row groups of 16 kRT rows of `in`) x ksplit L-slices; kWaves waves
+// per workgroup split the slice in 32-wide chunks, wave w taking chunks w,
+// w + kWaves, ...  Each round a wave issues the loads of kCh chunks (in: one
+// 16-byte load per lane per chunk and 16-row tile; P: one per lane per
+// 16-column tile) before any MFMA, so a round costs one memory latency.
+// 16x16x32 MFMA with in-rows on the M side and kCols column tiles of 16
+// (r <= 16 kCols); the kRT row tiles of a workgroup share each P load.
 // ksplit == 1: writes the finished result (fp32 and/or bf16 forms).
 // ksplit > 1: writes fp32 partial sums out_f32[slice][M][r].
-template <int kCols, int kWaves>
+template <int kCols, int kWaves, int kRT>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     const uint16_t* __restrict__ in, int64_t M, int64_t L, const uint16_t* __restrict__ P, int r,
     float scale, int ksplit, float* __restrict__ out_f32, uint16_t* __restrict__ out_sbf16,
     uint16_t* __restrict__ out_bf16) {
-  constexpr int kCh = kCols >= 8 ? 1 : 8 / kCols;
+  constexpr int kCh = kCols * kRT >= 8 ? 1 : 8 / (kCols * kRT);
   __shared__ float sred[kWaves][16][17];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int mi = lane & 15, g = lane >> 4;
-  const int64_t m = static_cast<int64_t>(blockIdx.x) * 16 + mi;
-  const int64_t mc = m < M ? m : M - 1;  // clamped: rows >= M are never stored
+  const int64_t row0 = static_cast<int64_t>(blockIdx.x) * 16 * kRT;
   const int64_t nchunk = L >> 5;
   const int64_t c_lo = nchunk * blockIdx.y / ksplit, c_hi = nchunk * (blockIdx.y + 1) / ksplit;
-  const uint16_t* arow = in + mc * L + 8 * g;
+  // rows >= M read row M - 1 and are never stored
+  const uint16_t* arow[kRT];
+#pragma unroll
+  for (int rt = 0; rt < kRT; ++rt) {
+    const int64_t m = row0 + 16 * rt + mi;
+    arow[rt] = in + (m < M ? m : M - 1) * L + 8 * g;
+  }
   // Column j = 16 c + mi of P, clamped into [0, r); columns >= r read row
   // r - 1 and are zeroed.
   const uint16_t* prow[kCols];
@@ -74,67 +80,95 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     pvalid[c] = j < r;
     prow[c] = P + static_cast<int64_t>(j < r ? j : r - 1) * L + 8 * g;
   }
-  f32x4_t acc[kCols];
+  f32x4_t acc[kRT][kCols];
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < kRT; ++rt)
+#pragma unroll
+    for (int c = 0; c < kCols; ++c) acc[rt][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // chunks of this wave: c_lo + wave + kWaves * i, i < cnt.  Each round
   // issues all of its loads (clamped to valid chunks) before any MFMA, and
-  // has no branches: chunks past cnt have their x operand masked to zero
+  // has no branches: chunks past cnt have their P operand masked to zero
   // with an integer AND (a select would become a branch around the load).
   const int64_t first = c_lo + wave;
   const int64_t cnt = first < c_hi ? (c_hi - first + kWaves - 1) / kWaves : 0;
   for (int64_t i0 = 0; i0 < cnt; i0 += kCh) {
-    uint4 a[kCh], b[kCh][kCols];
+    uint4 a[kCh][kRT], b[kCh][kCols];
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
       const int64_t ii = i0 + i < cnt ? i0 + i : cnt - 1;
       const int64_t kk = (first + ii * kWaves) * 32;
-      a[i] = *reinterpret_cast<const uint4*>(arow + kk);
+#pragma unroll
+      for (int rt = 0; rt < kRT; ++rt) a[i][rt] = *reinterpret_cast<const uint4*>(arow[rt] + kk);
 #pragma unroll
       for (int c = 0; c < kCols; ++c) b[i][c] = *reinterpret_cast<const uint4*>(prow[c] + kk);
     }
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
-      const uint32_t am = i0 + i < cnt ? 0xFFFFFFFFu : 0u;
-      const uint4 ai = make_uint4(a[i].x & am, a[i].y & am, a[i].z & am, a[i].w & am);
+      const uint32_t im = i0 + i < cnt ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int c = 0; c < kCols; ++c) {
-        const uint32_t bm = pvalid[c] ? 0xFFFFFFFFu : 0u;
+        const uint32_t bm = pvalid[c] ? im : 0u;
         const uint4 bb = make_uint4(b[i][c].x & bm, b[i][c].y & bm, b[i][c].z & bm, b[i][c].w & bm);
-        acc[c] = mfma16(ai, bb, acc[c]);
+#pragma unroll
+        for (int rt = 0; rt < kRT; ++rt) acc[rt][c] = mfma16(a[i][rt], bb, acc[rt][c]);
       }
     }
   }
 
-  // Cross-wave sum, one 16-column tile at a time, fixed order.
+  // Cross-wave sum, one 16 x 16 tile at a time, fixed order.
   const int ncol = (r + 15) >> 4;
 #pragma unroll
-  for (int c = 0; c < kCols; ++c) {
-    if (c < ncol) {
+  for (int rt = 0; rt < kRT; ++rt) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) sred[wave][4 * g + v][mi] = acc[c][v];
-      __syncthreads();
-      for (int idx = threadIdx.x; idx < 256; idx += kWaves * 64) {
-        const int row = idx >> 4, cj = idx & 15;
-        const int col = c * 16 + cj;
-        const int64_t mm = static_cast<int64_t>(blockIdx.x) * 16 + row;
-        if (mm < M && col < r) {
-          float v = 0.f;
+    for (int c = 0; c < kCols; ++c) {
+      if (c < ncol) {
 #pragma unroll
-          for (int w = 0; w < kWaves; ++w) v += sred[w][row][cj];
-          const int64_t o = mm * r + col;
-          if (ksplit > 1) {
-            out_f32[static_cast<int64_t>(blockIdx.y) * M * r + o] = v;
-          } else {
-            if (out_f32) out_f32[o] = v;
-            if (out_sbf16) out_sbf16[o] = static_cast<uint16_t>(pack_bf16x2(scale * v, 0.f) & 0xFFFF);
-            if (out_bf16) out_bf16[o] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
+        for (int v = 0; v < 4; ++v) sred[wave][4 * g + v][mi] = acc[rt][c][v];
+        __syncthreads();
+        for (int idx = threadIdx.x; idx < 256; idx += kWaves * 64) {
+          const int row = idx >> 4, cj = idx & 15;
+          const int col = c * 16 + cj;
+          const int64_t mm = row0 + 16 * rt + row;
+          if (mm < M && col < r) {
+            float v = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) v += sred[w][row][cj];
+            const int64_t o = mm * r + col;
+            if (ksplit > 1) {
+              out_f32[static_cast<int64_t>(blockIdx.y) * M * r + o] = v;
+            } else {
+              if (out_f32) out_f32[o] = v;
+              if (out_sbf16) out_sbf16[o] = static_cast<uint16_t>(pack_bf16x2(scale * v, 0.f) & 0xFFFF);
+              if (out_bf16) out_bf16[o] = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xFFFF);
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
+  }
+}
+
+// Fixed-order sum of the L-sliced partial sums of a LoRA projection: one
+// element per thread, the loads of all slices issued before they are added
+// up in slice order (bit-reproducible).
+__global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restrict__ part,
+                                                          int nslice, int64_t n, float scale,
+                                                          uint16_t* __restrict__ out_scaled,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t ec = e < n ? e : n - 1;  // past n: re-read the last element, store nothing
+  float v[kWideMaxSlices];
+#pragma unroll
+  for (int q = 0; q < kWideMaxSlices; ++q) v[q] = part[static_cast<int64_t>(q < nslice ? q : 0) * n + ec];
+  float sum = v[0];
+#pragma unroll
+  for (int q = 1; q < kWideMaxSlices; ++q)
+    if (q < nslice) sum += v[q];
+  if (e < n) {
+    out_scaled[e] = static_cast<uint16_t>(pack_bf16x2(scale * sum, 0.f) & 0xFFFF);
+    if (out) out[e] = static_cast<uint16_t>(pack_bf16x2(sum, 0.f) & 0xFFFF);
   }
 }
 
@@ -506,14 +540,22 @@ void gemv_config(int xmode, bool dq, dim3 grid, hipStream_t st, const GemvArgs& 
 }
 
 template <int kCols>
-void skinny_launch(dim3 grid, bool wide, hipStream_t s, const uint16_t* in, int64_t M, int64_t L,
+void skinny_launch(int rows, hipStream_t s, const uint16_t* in, int64_t M, int64_t L,
                    const uint16_t* P, int r, float scale, int ksplit, float* out_f32,
                    uint16_t* out_sbf16, uint16_t* out_bf16) {
-  if (wide)
-    hipLaunchKernelGGL((skinny_kernel<kCols, 16>), grid, dim3(1024), 0, s, in, M, L, P, r, scale,
+  const dim3 grid(static_cast<uint32_t>((M + rows - 1) / rows), static_cast<uint32_t>(ksplit));
+  if constexpr (kCols <= 4) {
+    if (rows == 64) {
+      hipLaunchKernelGGL((skinny_kernel<kCols, 16, 4>), grid, dim3(1024), 0, s, in, M, L, P, r,
+                         scale, ksplit, out_f32, out_sbf16, out_bf16);
+      return;
+    }
+  }
+  if (M > 16)
+    hipLaunchKernelGGL((skinny_kernel<kCols, 16, 1>), grid, dim3(1024), 0, s, in, M, L, P, r, scale,
                        ksplit, out_f32, out_sbf16, out_bf16);
   else
-    hipLaunchKernelGGL((skinny_kernel<kCols, 8>), grid, dim3(512), 0, s, in, M, L, P, r, scale,
+    hipLaunchKernelGGL((skinny_kernel<kCols, 8, 1>), grid, dim3(512), 0, s, in, M, L, P, r, scale,
                        ksplit, out_f32, out_sbf16, out_bf16);
 }
 
@@ -540,20 +582,39 @@ int skinny_splits(int64_t M, int64_t L, int r, int gemv_thr) {
   return ks < 1 ? 1 : static_cast<int>(ks);
 }
 
+int skinny_wide_splits(int64_t M, int64_t L) {
+  // about 256 workgroups of 64 rows, at least one 32-wide chunk per wave
+  const int64_t groups = (M + 63) / 64;
+  int64_t ks = (256 + groups - 1) / groups;
+  const int64_t maxk = (L >> 5) / 16;
+  if (ks > maxk) ks = maxk;
+  if (ks > kWideMaxSlices) ks = kWideMaxSlices;
+  return ks < 1 ? 1 : static_cast<int>(ks);
+}
+
 hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P, int r,
                          float scale, float* out_f32, uint16_t* out_scaled_bf16,
                          uint16_t* out_bf16, int ksplit, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
-  const dim3 grid(static_cast<uint32_t>((M + 15) / 16), static_cast<uint32_t>(ksplit));
-  // Many row tiles: 16 waves per tile so each CU has enough loads in
-  // flight; decode (one row tile): 8 waves per slice, up to 8 slices.
-  const bool wide = M > 16;
+  // Decode (M <= 16): one 16-row tile, 8 waves per L-slice.  Token batches:
+  // 64-row workgroups of 16 waves (each load of P serves four row tiles);
+  // r > 64 keeps 16-row workgroups (the accumulators of 4 x 8 tiles would
+  // not fit).
+  const int rows = M > 16 && r <= 64 ? 64 : 16;
   switch (skinny_cols(r)) {
-    case 1: skinny_launch<1>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    case 2: skinny_launch<2>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    case 4: skinny_launch<4>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    default: skinny_launch<8>(grid, wide, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 1: skinny_launch<1>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 2: skinny_launch<2>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 4: skinny_launch<4>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    default: skinny_launch<8>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_reduce(const float* part, int nslice, int64_t n, float scale,
+                              uint16_t* out_scaled, uint16_t* out, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(lora_reduce_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256),
+                     0, st, part, nslice, n, scale, out_scaled, out);
   return hipGetLastError();
 }
 

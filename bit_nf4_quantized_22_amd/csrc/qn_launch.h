@@ -34,6 +34,11 @@ hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out,
 // Largest number of L-slices of the decode LoRA-down (the forward
 // workspace holds that many fp32 partial sums of u).
 constexpr int kDecodeMaxSlices = 512;
+// Largest number of L-slices of the token-batch LoRA projections u = x A^T
+// and t = dy B, whose fp32 partial sums the fused GEMM adds up.
+constexpr int kWideMaxSlices = 16;
+// Number of L-slices launch_skinny uses for M > 16 tokens.
+int skinny_wide_splits(int64_t M, int64_t L);
 
 // Threads per workgroup of the decode GEMV for an N x K weight.
 int gemv_threads(int64_t N, int64_t K);
@@ -57,6 +62,12 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
 hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
                            const uint16_t* ts, const uint16_t* A, int r, uint16_t* dx,
                            hipStream_t st);
+
+// Sum of nslice (<= kWideMaxSlices) fp32 partial sums part[nslice][n] in
+// slice order: writes bf16(scale * sum) to out_scaled (and bf16(sum) to out
+// if non-null).
+hipError_t launch_lora_reduce(const float* part, int nslice, int64_t n, float scale,
+                              uint16_t* out_scaled, uint16_t* out, hipStream_t st);
 
 // LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
 // fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.

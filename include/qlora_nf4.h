@@ -151,7 +151,10 @@ QN_API int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* s
 /*
  * qn_workspace_bytes -- HOST function.  Bytes of device workspace that op
  * (QN_OP_FWD, QN_OP_BWD_DX or QN_OP_LORA_GRADS) needs for these sizes.
- * Returns 0 for invalid arguments.
+ * Returns 0 for invalid arguments.  The forward and backward keep the LoRA
+ * projection (x A^T or dy B) there as fp32 partial sums over slices of the
+ * contraction (at most 512 slices for M <= 16, 16 above), which are added
+ * up in a fixed order, so results are bit-reproducible.
  */
 QN_API size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r);
 
