@@ -24,6 +24,9 @@ dq_quantize_scales) over 80 layers of the 65B shapes (7 projections,
 N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
 beyond the Infinity Cache) quantised in turn 10 times over.
 
+"unfused_context" times, as context only, the unfused way of doing the
+same base products: nf4_dequant to bf16 in HBM, then torch's bf16 GEMM.
+
 Inputs are resident in HBM before the timed region.  Every phase is timed
 with HIP events on the stream the library launches on (torch's current
 stream); the K timed steps are bracketed by synchronisations.
@@ -149,6 +152,44 @@ def cpu_baseline(workloads):
                       "4096x11008, fp64 fwd+bwd_dx over all 2048 tokens (r=16) repeated "
                       f"{reps}x, LoRA grads once; {total:.1f} s wall, fwd+bwd {t_gemm:.1f} s; "
                       f"cpu_count={os.cpu_count()}"}
+
+
+def unfused_context(qn, torch, layers, reps=10):
+    """Context, not the metric: the same base products done the unfused way,
+    nf4_dequant of W to bf16 in HBM followed by torch's bf16 GEMM (hipBLASLt)
+    for y = x W^T and dx = dy W, without the LoRA terms.  Reports the plain
+    bf16 GEMM rate (the achievable MFMA rate of a library GEMM at these
+    shapes) and the rate of dequant + GEMM."""
+    F = torch.nn.functional
+    res = {}
+    for L in layers:
+        qw, N, K = L["qw"], L["N"], L["K"]
+        flops = 2.0 * M_TRAIN * N * K
+        for name, gemm in (("fwd", lambda: F.linear(L["x"], L["deq"])),
+                           ("bwd", lambda: torch.mm(L["dy"], L["deq"]))):
+            def run(with_dequant):
+                if with_dequant:
+                    qn.nf4_dequant(qw, torch.bfloat16, out=L["deq"])
+                return gemm()
+            for _ in range(3):
+                run(True)
+            torch.cuda.synchronize()
+            t = {}
+            for wd in (False, True):
+                s = torch.cuda.Event(enable_timing=True)
+                e = torch.cuda.Event(enable_timing=True)
+                s.record()
+                for _ in range(reps):
+                    run(wd)
+                e.record()
+                torch.cuda.synchronize()
+                t[wd] = s.elapsed_time(e) / reps
+            res[f"{name} {N}x{K}"] = {"gemm_us": round(t[False] * 1e3, 1),
+                                      "gemm_TFLOPs": round(flops / (t[False] * 1e-3) / 1e12, 1),
+                                      "dequant_plus_gemm_us": round(t[True] * 1e3, 1),
+                                      "dequant_plus_gemm_TFLOPs":
+                                          round(flops / (t[True] * 1e-3) / 1e12, 1)}
+    return res
 
 
 def quantise_65b(qn, torch, dev, synth):
@@ -317,6 +358,8 @@ def main():
         return float(np.mean([r[key][0].elapsed_time(r[key][1]) for r in recs]))
 
     ms = {ph: mean_ms(ph) for ph in phases if ph != "gemv"}
+    spread = {ph: [round(float(np.percentile([r[ph][0].elapsed_time(r[ph][1]) for r in recs], q)), 4)
+                   for q in (10, 50, 90)] for ph in phases if ph != "gemv"}
     gemv = {}
     gemv_ms_total = 0.0
     for key, (g, n) in graphs.items():
@@ -379,6 +422,7 @@ def main():
                  "frac_hbm": head["frac_hbm"], "us_per_call": head["us_per_call"],
                  "all": gemv},
         "phases_ms": {k: round(v, 4) for k, v in ms.items()},
+        "phases_ms_p10_p50_p90": spread,
         "phase_rates": {k: {"bound": v[0], "achieved": round(v[1], 2), "unit": v[3],
                             "frac": round(v[1] / v[2], 4)} for k, v in per_phase.items()},
         "roofline": {"kernel": "fused dequant GEMM (qlora_linear_fwd, M=2048, r=16)",
@@ -387,6 +431,7 @@ def main():
                      "traffic": traffic,
                      "us_per_launch": round(fwd_us_per_launch, 2)},
     }
+    out["unfused_context"] = unfused_context(qn, torch, layers)
     out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(workloads)
