@@ -9,6 +9,7 @@ of the bf16 activations / LoRA matrices and of the fp32 dequantised weight.
   forward          y  = x W^T + s (x A^T) B^T                s = alpha / r
   backward (input) dx = dy W + s (dy B) A
   LoRA gradients   dA = s (dy B)^T x,   dB = s dy^T (x A^T)
+  merge            W' = W + s B A
 
 [rkmt] §2.1: the update is the product B A of a d x r and an r x k matrix,
 with the frozen weight unchanged; [rkmt] §3.3: the low-rank update is scaled
@@ -63,3 +64,18 @@ def lora_grads(x, dy, A, B, alpha, r):
     dA = s * (lora_up_input(dy, B).T @ _f64(x))
     dB = s * (_f64(dy).T @ lora_down(x, A))
     return dA, dB
+
+
+def lora_merge(w_hat, A, B, alpha, r):
+    """W' = W + (alpha/r) B A in fp64 ([N, K]).
+
+    [rkmt] §2.1: for inference the adapter is folded into the weight,
+    W <- W + B A, which adds no latency; [tgd] §7: a QLoRA adapter is merged
+    into a 16-bit weight, never into the 4-bit form.  Reading: the weight is
+    the dequantised W the adapter was trained against (the value every
+    forward of this layer used), scaled update as in the forward.
+    """
+    w = _f64(w_hat)
+    if r:
+        w = w + _scale(alpha, r) * (_f64(B) @ _f64(A))
+    return w

@@ -202,6 +202,23 @@ def f32_to_bf16_bits(x):
     return r.astype(np.uint16)
 
 
+def f64_to_bf16_bits(x):
+    """Round fp64 straight to bf16 (nearest, ties to even); returns uint16.
+
+    x = m 2^e with 0.5 <= |m| < 1 has a bf16 spacing of 2^(e - 8) (8
+    significant bits; never below the subnormal step 2^-133), so
+    rint(x / spacing) * spacing is the rounding, exact in fp64, and the
+    result is exactly representable in fp32.  Finite inputs only.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("oracle: finite values only")
+    _, e = np.frexp(x)
+    step = np.ldexp(1.0, np.maximum(e - 8, -133))
+    y = np.rint(x / step) * step
+    return (np.ascontiguousarray(y.astype(np.float32)).view(np.uint32) >> 16).astype(np.uint16)
+
+
 def bf16_bits_to_f32(bits):
     """Exact widening of bf16 bit patterns to fp32."""
     b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
