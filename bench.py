@@ -11,6 +11,7 @@ weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
   fwd       qlora_linear_fwd    at M = 2048 (LoRA-down + fused dequant GEMM)
   bwd       qlora_linear_bwd_dx at M = 2048 (B^T, LoRA t + fused dequant GEMM)
   grads     lora_grads with the saved u, t
+  merge     qlora_merge: the merged bf16 weight dequant(W) + (alpha/r) B A
   gemv      qlora_linear_fwd at M = 1, 4, 16 (decode: LoRA-down + dequant
             GEMV), over rotating quantised copies totalling >= 512 MiB so no
             call is served from the 256 MiB Infinity Cache.  The decode calls
@@ -298,7 +299,7 @@ def main():
             graphs[(L["N"], L["K"], m)] = (g, len(L["copies"]))
     torch.cuda.synchronize()
 
-    phases = ["quantise", "dequant", "fwd", "bwd", "grads", "gemv"]
+    phases = ["quantise", "dequant", "fwd", "bwd", "grads", "merge", "gemv"]
 
     def step(record):
         ev = {}
@@ -328,6 +329,8 @@ def main():
                 elif ph == "bwd":
                     qn.qlora_linear_bwd_dx(qw, L["dy"], L["A"], L["B"], RANK, ALPHA, dx=L["dx"],
                                            t_out=L["t"], ws=L["ws"])
+                elif ph == "merge":
+                    qn.qlora_merge(qw, L["A"], L["B"], RANK, ALPHA, out=L["deq"])
                 elif ph == "grads":
                     qn.lora_grads(L["x"], L["dy"], L["A"], L["B"], RANK, ALPHA, u=L["u"],
                                   t=L["t"], dA=L["dA"], dB=L["dB"], ws=L["ws"])
@@ -382,6 +385,9 @@ def main():
     # grads: read x, dy (bf16) and the saved u, t (bf16); write dA, dB (fp32)
     gr_bytes = sum(2 * M_TRAIN * (L["N"] + L["K"]) + 2 * 2 * M_TRAIN * RANK
                    + 4 * RANK * (L["N"] + L["K"]) for L in layers)
+    # merge: read codes + constants, A and B; write the bf16 weight
+    mg_bytes = sum(L["N"] * L["K"] * (BYTES_PER_WEIGHT + 2) + 2 * RANK * (L["N"] + L["K"])
+                   for L in layers)
     hN, hK, hM = GEMV_HEADLINE
     head = gemv[f"{hN}x{hK}_M{hM}"]
     per_phase = {
@@ -390,6 +396,7 @@ def main():
         "fwd": ("mfma", fwd_flops / (ms["fwd"] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
         "bwd": ("mfma", fwd_flops / (ms["bwd"] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"),
         "grads": ("hbm", gr_bytes / (ms["grads"] * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"),
+        "merge": ("hbm", mg_bytes / (ms["merge"] * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"),
         "gemv": ("hbm", head["GBps"], PEAK_HBM_GBPS, "GB/s"),
     }
     # dominant kernel: the fused dequant GEMM of the forward (11008x4096, the

@@ -26,7 +26,7 @@ BLOCKSIZE, GROUP = 64, 256
 
 EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
-           "lora_grads")
+           "lora_grads", "qlora_merge")
 
 
 class QnError(RuntimeError):
@@ -68,6 +68,7 @@ def load_library():
         "qlora_linear_bwd_dx": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "lora_grads": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp,
                                       vp, sz, vp]),
+        "qlora_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -281,3 +282,21 @@ def lora_grads(x, dy, A, B, r, alpha, u=None, t=None, dA=None, dB=None, ws=None,
         _ptr(x), _ptr(dy), _ptr(u), _ptr(t), _ptr(A), _ptr(B), M, N, K, r, float(alpha),
         _ptr(dA), _ptr(dB), _ptr(ws), wsb, _stream(stream)))
     return dA, dB
+
+
+def qlora_merge(qw, A, B, r, alpha, out=None, stream=None):
+    """Merged 16-bit weight bf16[N, K] = bf16(dequant(W) + (alpha/r) B A)."""
+    torch = _torch()
+    lib = load_library()
+    N, K = qw.N, qw.K
+    if r:
+        _dev(A, torch.bfloat16, r * K, "A")
+        _dev(B, torch.bfloat16, N * r, "B")
+    if out is None:
+        out = torch.empty((N, K), dtype=torch.bfloat16, device=qw.packed.device)
+    _dev(out, torch.bfloat16, N * K, "out")
+    cw = qw.c_struct()
+    _check("qlora_merge", lib.qlora_merge(ctypes.byref(cw), _ptr(A) if r else None,
+                                          _ptr(B) if r else None, r, float(alpha), _ptr(out),
+                                          _stream(stream)))
+    return out

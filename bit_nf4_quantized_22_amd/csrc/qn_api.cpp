@@ -245,6 +245,21 @@ int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const 
   return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
 }
 
+int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,
+                qn_bf16* out, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, true);
+  if (st != QN_OK) return st;
+  if (r < 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (!out || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if (!aligned(out, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  return hip_status(qn::launch_merge(v, A, B, r, scale, out, as_stream(stream)));
+}
+
 int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_bf16* t,
                const qn_bf16* A, const qn_bf16* B, int64_t M, int64_t N, int64_t K, int32_t r,
                float alpha, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {

@@ -69,6 +69,10 @@ hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
 hipError_t launch_lora_reduce(const float* part, int nslice, int64_t n, float scale,
                               uint16_t* out_scaled, uint16_t* out, hipStream_t st);
 
+// LoRA merge: out[N, K] = bf16(dequant(W) + s B A) (A [r, K], B [N, r]).
+hipError_t launch_merge(const WeightView& w, const uint16_t* A, const uint16_t* B, int r, float s,
+                        uint16_t* out, hipStream_t st);
+
 // LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
 // fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.
 size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);

@@ -187,6 +187,22 @@ QN_API int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M,
                         void* stream);
 
 /*
+ * qlora_merge -- out = bf16(dequant(W) + (alpha/r) B A), the merged 16-bit
+ * weight.  [rkmt] §2.1: for inference the adapter is folded into the
+ * weight (W <- W + B A, no added latency); [tgd] §7: a QLoRA adapter is
+ * merged into a 16-bit weight, never into the 4-bit form.  W is the
+ * dequantised NF4 weight the adapter was trained against; re-quantise the
+ * result with nf4_quantize for a merged 4-bit model.
+ *   A bf16[r, K], B bf16[N, r] (device; ignored when r == 0).
+ *   out device bf16[N, K], overwritten.  Per element: the rank-r product is
+ *   an fp32 fma chain over j = 0 .. r-1, scaled by alpha/r in fp32, added
+ *   to the fp32 dequantised weight, then rounded to bf16 (nearest even).
+ *   r must be 0..128.  N and K must be positive multiples of 64.
+ */
+QN_API int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t r,
+                       float alpha, qn_bf16* out, void* stream);
+
+/*
  * lora_grads -- dA = (alpha/r) (dy B)^T x,  dB = (alpha/r) dy^T (x A^T).
  * [kwkr] §2.3: only the LoRA matrices receive gradients; the 4-bit weight
  * and its constants get none.

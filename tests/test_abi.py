@@ -136,3 +136,16 @@ def test_linear_argument_errors(lib):
              1 << 20, None) == qn.QN_ERR_SHAPE
     assert g(FAKE, FAKE, None, None, FAKE, FAKE, 32, 128, 128, 8, 16.0, FAKE, FAKE, None, 0,
              None) == qn.QN_ERR_WORKSPACE
+
+
+def test_merge_argument_errors(lib):
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256)
+    bad = qn.qn_weight(0x100000, None, None, 0x100000, 100, 128, 64, 256)
+    merge = lib.qlora_merge
+    assert merge(ctypes.byref(bad), FAKE, FAKE, 8, 16.0, FAKE, None) == qn.QN_ERR_SHAPE
+    assert merge(ctypes.byref(w), FAKE, FAKE, -1, 16.0, FAKE, None) == qn.QN_ERR_SHAPE
+    assert merge(ctypes.byref(w), FAKE, FAKE, 129, 16.0, FAKE, None) == qn.QN_ERR_UNSUPPORTED
+    assert merge(ctypes.byref(w), None, FAKE, 8, 16.0, FAKE, None) == qn.QN_ERR_NULL
+    assert merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, None, None) == qn.QN_ERR_NULL
+    assert merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, ODD, None) == qn.QN_ERR_ALIGN
+    assert merge(None, FAKE, FAKE, 8, 16.0, FAKE, None) == qn.QN_ERR_NULL

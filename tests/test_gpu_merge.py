@@ -1,0 +1,120 @@
+"""Parity of the LoRA merge (qlora_merge) with the fp64 oracle (GPU).
+
+The merged weight bf16(dequant(W) + (alpha/r) B A) is compared element by
+element with the oracle's fp64 value rounded straight to bf16.  The kernel
+forms the rank-r product in fp32 (an fma chain over j), so an element whose
+exact value lies within fp32 rounding of a bf16 rounding boundary may land
+one bf16 step away, and where the update nearly cancels the weight the
+fp32 error of the chain can span several steps of the small result.  The
+bar: every element within one bf16 step plus twice the fp32 error bound
+r 2^-24 (alpha/r) |B||A| of the chain, at most one step wherever that bound
+is under a quarter step, and at least 99.9% of the elements identical.  With B = 0 or r = 0 the merge is
+nf4_dequant's bf16 output, bit for bit.  Re-quantising the merged weight on
+the device matches the oracle's quantisation of the same bf16 values.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_22_amd as qn
+from tests.gpu_helpers import (bf16_dev, f64, linear, nf4, oracle_quant, quantized_layer, synth,
+                               to_bits16)
+
+pytestmark = pytest.mark.gpu
+
+
+def _ordered(bits):
+    """bf16 bit patterns -> integers in the order of the values."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int32)
+    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF) - 1 - 0x8000, b)
+
+
+def _spacing(v):
+    _, e = np.frexp(v)
+    return np.ldexp(1.0, np.maximum(e - 8, -133))
+
+
+def _check_merge(got_bits, want_bits, name, acc_err, min_exact=0.999):
+    """acc_err = r 2^-24 (alpha/r) |B| |A| elementwise bounds how far the
+    fp32 fma chain over r terms can be from the exact product; that can be
+    many bf16 steps of a result that nearly cancels the weight."""
+    steps = np.abs(_ordered(got_bits) - _ordered(want_bits))
+    exact = float(np.mean(steps == 0))
+    got = nf4.bf16_bits_to_f32(got_bits).astype(np.float64)
+    want = nf4.bf16_bits_to_f32(want_bits).astype(np.float64)
+    bound = _spacing(np.maximum(np.abs(got), np.abs(want))) + 2 * acc_err
+    well = acc_err < 0.25 * _spacing(np.abs(want))
+    print(f"{name}: exact {exact:.6f}, max bf16 steps {int(steps.max())} "
+          f"({int(steps[~well].max()) if (~well).any() else 0} where the sum nearly cancels)")
+    assert np.all(np.abs(got - want) <= bound), f"{name}: error beyond the fp32 accumulation bound"
+    assert steps[well].max() <= 1, f"{name}: {int((steps[well] > 1).sum())} elements off by more than one bf16 step"
+    assert exact >= min_exact, f"{name}: only {exact:.5f} of the elements exact"
+
+
+def _merge_case(wl, double_quant=True, rows=None, B_override=None):
+    qw, ref = quantized_layer(wl, double_quant)
+    B_bits = wl.B if B_override is None else B_override
+    out = qn.qlora_merge(qw, bf16_dev(wl.A), bf16_dev(B_bits), wl.r, wl.alpha)
+    torch.cuda.synchronize()
+    got = to_bits16(out)
+    sel = np.arange(wl.N) if rows is None else rows
+    want = nf4.f64_to_bf16_bits(linear.lora_merge(ref["What"][sel].astype(np.float64), f64(wl.A),
+                                                  f64(B_bits)[sel], wl.alpha, wl.r))
+    acc_err = wl.r * 2.0 ** -24 * (wl.alpha / wl.r) * (np.abs(f64(B_bits)[sel]) @ np.abs(f64(wl.A)))
+    return qw, ref, got, got[sel], want, acc_err
+
+
+def test_merge_tiny_fp32_layer():
+    wl = synth.tiny_layer(0)
+    _, _, _, got, want, mag = _merge_case(wl)
+    _check_merge(got, want, "tiny r=8", mag, min_exact=0.99)
+
+
+def test_merge_tiny_layer_without_double_quant():
+    wl = synth.tiny_layer(0)
+    _, _, _, got, want, mag = _merge_case(wl, double_quant=False)
+    _check_merge(got, want, "tiny r=8 absmax", mag, min_exact=0.99)
+
+
+def test_merge_decode_weight_r16():
+    wl = synth.decode_layer(1, 4096, 4096, seed=2)
+    _, _, _, got, want, mag = _merge_case(wl)
+    _check_merge(got, want, "4096x4096 r=16", mag)
+
+
+@pytest.mark.parametrize("shape", [(11008, 4096), (4096, 11008)])
+def test_merge_training_weights_r64(shape):
+    wl = synth.decoder_layer_linear(
+        [("w", shape[0], shape[1])], 0, M=16, r=64, alpha=16.0, std=0.02, seed=11)
+    rows = np.sort(np.random.default_rng(1).choice(shape[0], 512, replace=False))
+    _, _, _, got, want, mag = _merge_case(wl, rows=rows)
+    _check_merge(got, want, f"{shape} r=64 sampled rows", mag)
+
+
+def test_merge_with_b_zero_is_the_bf16_dequant():
+    wl = synth.decode_layer(1, 4096, 4096, seed=2)
+    qw, _, got_all, _, _, _ = _merge_case(wl, B_override=np.zeros_like(wl.B))
+    deq = to_bits16(qn.nf4_dequant(qw, torch.bfloat16))
+    assert np.array_equal(got_all, deq)
+
+
+def test_merge_rank_zero_is_the_bf16_dequant():
+    wl = synth.tiny_layer(0)
+    qw, _ = quantized_layer(wl)
+    out = qn.qlora_merge(qw, None, None, 0, 16.0)
+    deq = qn.nf4_dequant(qw, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_bits16(out), to_bits16(deq))
+
+
+def test_requantised_merge_matches_the_oracle():
+    wl = synth.tiny_layer(0)
+    qw, _ = quantized_layer(wl)
+    merged = qn.qlora_merge(qw, bf16_dev(wl.A), bf16_dev(wl.B), wl.r, wl.alpha)
+    q2 = qn.quantize_weight(merged)
+    torch.cuda.synchronize()
+    ref2 = oracle_quant(to_bits16(merged).reshape(wl.N, wl.K), "bf16")
+    assert np.array_equal(q2.packed.cpu().numpy().ravel(), ref2["packed"].ravel())
+    assert np.array_equal(q2.qscale.cpu().numpy().ravel(), ref2["q8"].ravel())
+    assert np.array_equal(q2.gscale.cpu().numpy().ravel().view(np.uint32), ref2["c2"].view(np.uint32))
