@@ -25,6 +25,9 @@ dq_quantize_scales) over 80 layers of the 65B shapes (7 projections,
 N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
 beyond the Infinity Cache) quantised in turn 10 times over.
 
+"adamw_7b_lora" times lora_adamw_step over all 40 M LoRA parameters of a
+7B model at r = 16 (seven projections x 32 layers).
+
 "unfused_context" times, as context only, the unfused way of doing the
 same base products: nf4_dequant to bf16 in HBM, then torch's bf16 GEMM.
 
@@ -191,6 +194,35 @@ def unfused_context(qn, torch, layers, reps=10):
                                       "dequant_plus_gemm_TFLOPs":
                                           round(flops / (t[True] * 1e-3) / 1e12, 1)}
     return res
+
+
+def adamw_7b_lora(qn, torch, dev, synth, steps=10):
+    """AdamW step over every LoRA parameter of a 7B model at r = 16 (A and B
+    of the seven projections of 32 layers, one flat fp32 buffer each for p,
+    g, m, v, plus the bf16 copy of p): HBM-bound, 30 bytes per parameter."""
+    n = 32 * sum(RANK * (nn + kk) for (_, nn, kk) in synth.LLAMA7B_TARGETS)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    p = torch.randn(n, generator=gen, device=dev) * 0.01
+    g = torch.randn(n, generator=gen, device=dev) * 1e-3
+    m = torch.zeros(n, device=dev)
+    v = torch.zeros(n, device=dev)
+    pb = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    qn.lora_adamw_step(p, g, m, v, 1, weight_decay=0.01, p_bf16=pb)
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for t in range(2, steps + 2):
+        qn.lora_adamw_step(p, g, m, v, t, weight_decay=0.01, p_bf16=pb)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    gbps = n * 30 / (ms * 1e-3) / 1e9
+    del p, g, m, v, pb
+    torch.cuda.empty_cache()
+    return {"params": n, "ms_per_step": round(ms, 4), "GBps": round(gbps, 1),
+            "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
 
 
 def quantise_65b(qn, torch, dev, synth):
@@ -440,6 +472,7 @@ def main():
     }
     out["unfused_context"] = unfused_context(qn, torch, layers)
     out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
+    out["adamw_7b_lora"] = adamw_7b_lora(qn, torch, dev, synth)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(workloads)
     print(json.dumps(out))

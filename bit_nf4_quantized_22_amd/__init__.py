@@ -26,7 +26,7 @@ BLOCKSIZE, GROUP = 64, 256
 
 EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
-           "lora_grads", "qlora_merge")
+           "lora_grads", "qlora_merge", "lora_adamw_step")
 
 
 class QnError(RuntimeError):
@@ -69,6 +69,8 @@ def load_library():
         "lora_grads": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, i64, i64, i64, i32, f32, vp, vp,
                                       vp, sz, vp]),
         "qlora_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, vp, vp]),
+        "lora_adamw_step": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32,
+                                           vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -300,3 +302,20 @@ def qlora_merge(qw, A, B, r, alpha, out=None, stream=None):
                                           _ptr(B) if r else None, r, float(alpha), _ptr(out),
                                           _stream(stream)))
     return out
+
+
+def lora_adamw_step(p, g, m, v, step, lr=2e-4, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0,
+                    p_bf16=None, stream=None):
+    """In-place AdamW step on fp32 p, m, v with gradient g; optionally writes
+    bf16(p) to p_bf16.  Returns p."""
+    torch = _torch()
+    lib = load_library()
+    n = p.numel()
+    for t, name in ((p, "p"), (g, "g"), (m, "m"), (v, "v")):
+        _dev(t, torch.float32, n, name)
+    if p_bf16 is not None:
+        _dev(p_bf16, torch.bfloat16, n, "p_bf16")
+    _check("lora_adamw_step", lib.lora_adamw_step(
+        _ptr(p), _ptr(g), _ptr(m), _ptr(v), _ptr(p_bf16), n, float(lr), float(betas[0]),
+        float(betas[1]), float(eps), float(weight_decay), int(step), _stream(stream)))
+    return p

@@ -260,6 +260,23 @@ int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t 
   return hip_status(qn::launch_merge(v, A, B, r, scale, out, as_stream(stream)));
 }
 
+int lora_adamw_step(float* p, const float* g, float* m, float* v, qn_bf16* p_bf16, int64_t n,
+                    float lr, float beta1, float beta2, float eps, float weight_decay, int32_t step,
+                    void* stream) {
+  if (n < 0 || step < 1) return QN_ERR_SHAPE;
+  if (n == 0) return QN_OK;
+  if (!p || !g || !m || !v) return QN_ERR_NULL;
+  if (!aligned(p, 16) || !aligned(g, 16) || !aligned(m, 16) || !aligned(v, 16) ||
+      (p_bf16 && !aligned(p_bf16, 8)))
+    return QN_ERR_ALIGN;
+  if (!(lr >= 0.0f) || !(beta1 >= 0.0f && beta1 < 1.0f) || !(beta2 >= 0.0f && beta2 < 1.0f) ||
+      !(eps > 0.0f) || !(weight_decay >= 0.0f))
+    return QN_ERR_SHAPE;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_adamw(p, g, m, v, p_bf16, n, lr, beta1, beta2, eps, weight_decay,
+                                     step, as_stream(stream)));
+}
+
 int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_bf16* t,
                const qn_bf16* A, const qn_bf16* B, int64_t M, int64_t N, int64_t K, int32_t r,
                float alpha, float* dA, float* dB, void* ws, size_t ws_bytes, void* stream) {

@@ -73,6 +73,11 @@ hipError_t launch_lora_reduce(const float* part, int nslice, int64_t n, float sc
 hipError_t launch_merge(const WeightView& w, const uint16_t* A, const uint16_t* B, int r, float s,
                         uint16_t* out, hipStream_t st);
 
+// AdamW step (see lora_adamw_step in the C ABI).
+hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* p_bf16, int64_t n,
+                        float lr, float beta1, float beta2, float eps, float weight_decay, int step,
+                        hipStream_t st);
+
 // LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
 // fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.
 size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);

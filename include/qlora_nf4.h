@@ -218,6 +218,26 @@ QN_API int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u,
                int64_t M, int64_t N, int64_t K, int32_t r, float alpha,
                float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * lora_adamw_step -- one AdamW step on a LoRA matrix (A or B), in place.
+ * [rkmt] §3.5, [czcl] §3.2: the adapter is trained with AdamW (32-bit
+ * states, learning rate 2e-4), the only trainable parameters being A and
+ * B.  Decoupled weight decay, per element in fp32:
+ *   p <- p (1 - lr wd);  m <- b1 m + (1 - b1) g;  v <- b2 v + (1 - b2) g^2;
+ *   p <- p - (lr / (1 - b1^step)) m / (sqrt(v) / sqrt(1 - b2^step) + eps)
+ * (the bias corrections computed on the host in fp64).
+ *   p, m, v  device fp32[n], updated in place; g device fp32[n] (dA or dB
+ *            from lora_grads).  16-byte aligned.
+ *   p_bf16   device bf16[n] out (the new p rounded to bf16, the operand of
+ *            the next forward), 8-byte aligned, or NULL.
+ *   step     1 for the first step.  lr >= 0, 0 <= b1, b2 < 1, eps > 0,
+ *            weight_decay >= 0, else QN_ERR_SHAPE.
+ * The paged optimizer of the pages (host unified memory) is not part of it.
+ */
+QN_API int lora_adamw_step(float* p, const float* g, float* m, float* v, qn_bf16* p_bf16,
+                           int64_t n, float lr, float beta1, float beta2, float eps,
+                           float weight_decay, int32_t step, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

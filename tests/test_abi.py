@@ -149,3 +149,22 @@ def test_merge_argument_errors(lib):
     assert merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, None, None) == qn.QN_ERR_NULL
     assert merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, ODD, None) == qn.QN_ERR_ALIGN
     assert merge(None, FAKE, FAKE, 8, 16.0, FAKE, None) == qn.QN_ERR_NULL
+
+
+def test_adamw_argument_errors(lib):
+    step = lib.lora_adamw_step
+    args = dict(lr=2e-4, b1=0.9, b2=0.999, eps=1e-8, wd=0.0)
+
+    def call(p=FAKE, g=FAKE, m=FAKE, v=FAKE, pb=None, n=64, step_=1, **kw):
+        a = dict(args, **kw)
+        return step(p, g, m, v, pb, n, a["lr"], a["b1"], a["b2"], a["eps"], a["wd"], step_, None)
+
+    assert call(n=-1) == qn.QN_ERR_SHAPE
+    assert call(step_=0) == qn.QN_ERR_SHAPE
+    assert call(b1=1.0) == qn.QN_ERR_SHAPE
+    assert call(eps=0.0) == qn.QN_ERR_SHAPE
+    assert call(lr=-1.0) == qn.QN_ERR_SHAPE
+    assert call(g=None) == qn.QN_ERR_NULL
+    assert call(m=ODD) == qn.QN_ERR_ALIGN
+    assert call(pb=ODD) == qn.QN_ERR_ALIGN
+    assert call(p=None, g=None, m=None, v=None, n=0) == qn.QN_OK
