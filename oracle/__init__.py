@@ -13,6 +13,9 @@ Modules
   linear  -- the "4-bit storage, 16-bit compute" linear layer with a LoRA
              bypass: forward, backward to the input, LoRA gradients (fp64).
   memory  -- storage accounting (bits per parameter, LoRA parameter counts).
+  optim   -- the AdamW step on the LoRA matrices (fp64).
+  dropout -- LoRA dropout on the adapter branch: the counter-based mask
+             (Philox4x64-10) and the dropped forward, backward (fp64).
 
 Every function names the page and section it follows.  Pages are cited by
 title (site in brackets):
@@ -28,4 +31,4 @@ table printed in the original publication, which none of the pages carries
 (parity unpinned for that comparison only).
 """
 
-from . import nf4, linear, memory  # noqa: F401
+from . import nf4, linear, memory, optim, dropout  # noqa: F401
