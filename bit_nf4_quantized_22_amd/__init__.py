@@ -26,7 +26,8 @@ BLOCKSIZE, GROUP = 64, 256
 
 EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
-           "lora_grads", "qlora_merge", "lora_adamw_step")
+           "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
+           "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout")
 
 
 class QnError(RuntimeError):
@@ -54,8 +55,8 @@ def load_library():
         raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
                            "(run python -m bit_nf4_quantized_22_amd.build)")
     lib = ctypes.CDLL(LIB_PATH)
-    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
-                             ctypes.c_float, ctypes.c_size_t)
+    vp, i32, i64, f32, sz, u64 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                  ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64)
     wp = ctypes.POINTER(qn_weight)
     sig = {
         "qn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -71,6 +72,11 @@ def load_library():
         "qlora_merge": (ctypes.c_int, [wp, vp, vp, i32, f32, vp, vp]),
         "lora_adamw_step": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32,
                                            vp]),
+        "lora_dropout": (ctypes.c_int, [vp, i64, i64, f32, u64, vp, vp]),
+        "qlora_linear_fwd_dropout": (ctypes.c_int, [wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp,
+                                                    sz, vp]),
+        "qlora_linear_bwd_dx_dropout": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, f32, u64, vp,
+                                                       vp, vp, sz, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -221,10 +227,21 @@ def _workspace(op, M, N, K, r, ws, device):
 
 def qlora_linear_fwd(qw, x, A, B, r, alpha, y=None, u_out=None, ws=None, stream=None):
     """y = x W^T + (alpha/r) (x A^T) B^T  (bf16 in/out)."""
+    return _fwd(qw, x, None, A, B, r, alpha, y, u_out, ws, stream)
+
+
+def qlora_linear_fwd_dropout(qw, x, x_drop, A, B, r, alpha, y=None, u_out=None, ws=None,
+                             stream=None):
+    """y = x W^T + (alpha/r) (x_drop A^T) B^T, x_drop from lora_dropout."""
+    return _fwd(qw, x, x_drop, A, B, r, alpha, y, u_out, ws, stream)
+
+
+def _fwd(qw, x, x_drop, A, B, r, alpha, y, u_out, ws, stream):
     torch = _torch()
     lib = load_library()
     M = x.shape[0]
     _dev(x, torch.bfloat16, M * qw.K, "x")
+    _dev(x_drop, torch.bfloat16, M * qw.K, "x_drop")
     if r:
         _dev(A, torch.bfloat16, r * qw.K, "A")
         _dev(B, torch.bfloat16, qw.N * r, "B")
@@ -234,14 +251,30 @@ def qlora_linear_fwd(qw, x, A, B, r, alpha, y=None, u_out=None, ws=None, stream=
     _dev(u_out, torch.bfloat16, M * r, "u_out")
     ws, wsb = _workspace(QN_OP_FWD, M, qw.N, qw.K, r, ws, x.device)
     cw = qw.c_struct()
-    _check("qlora_linear_fwd", lib.qlora_linear_fwd(
-        ctypes.byref(cw), _ptr(x), M, _ptr(A) if r else None, _ptr(B) if r else None, r,
-        float(alpha), _ptr(y), _ptr(u_out), _ptr(ws), wsb, _stream(stream)))
+    a, b = (_ptr(A), _ptr(B)) if r else (None, None)
+    if x_drop is None:
+        _check("qlora_linear_fwd", lib.qlora_linear_fwd(
+            ctypes.byref(cw), _ptr(x), M, a, b, r, float(alpha), _ptr(y), _ptr(u_out), _ptr(ws),
+            wsb, _stream(stream)))
+    else:
+        _check("qlora_linear_fwd_dropout", lib.qlora_linear_fwd_dropout(
+            ctypes.byref(cw), _ptr(x), _ptr(x_drop), M, a, b, r, float(alpha), _ptr(y),
+            _ptr(u_out), _ptr(ws), wsb, _stream(stream)))
     return y
 
 
 def qlora_linear_bwd_dx(qw, dy, A, B, r, alpha, dx=None, t_out=None, ws=None, stream=None):
     """dx = dy W + (alpha/r) (dy B) A  (bf16 in/out)."""
+    return _bwd(qw, dy, A, B, r, alpha, None, 0, dx, t_out, ws, stream)
+
+
+def qlora_linear_bwd_dx_dropout(qw, dy, A, B, r, alpha, p, seed, dx=None, t_out=None, ws=None,
+                                stream=None):
+    """dx = dy W + keep/(1-p) * ((alpha/r) (dy B) A), the mask of lora_dropout(p, seed)."""
+    return _bwd(qw, dy, A, B, r, alpha, p, seed, dx, t_out, ws, stream)
+
+
+def _bwd(qw, dy, A, B, r, alpha, p, seed, dx, t_out, ws, stream):
     torch = _torch()
     lib = load_library()
     M = dy.shape[0]
@@ -255,10 +288,30 @@ def qlora_linear_bwd_dx(qw, dy, A, B, r, alpha, dx=None, t_out=None, ws=None, st
     _dev(t_out, torch.bfloat16, M * r, "t_out")
     ws, wsb = _workspace(QN_OP_BWD_DX, M, qw.N, qw.K, r, ws, dy.device)
     cw = qw.c_struct()
-    _check("qlora_linear_bwd_dx", lib.qlora_linear_bwd_dx(
-        ctypes.byref(cw), _ptr(dy), M, _ptr(A) if r else None, _ptr(B) if r else None, r,
-        float(alpha), _ptr(dx), _ptr(t_out), _ptr(ws), wsb, _stream(stream)))
+    a, b = (_ptr(A), _ptr(B)) if r else (None, None)
+    if p is None:
+        _check("qlora_linear_bwd_dx", lib.qlora_linear_bwd_dx(
+            ctypes.byref(cw), _ptr(dy), M, a, b, r, float(alpha), _ptr(dx), _ptr(t_out),
+            _ptr(ws), wsb, _stream(stream)))
+    else:
+        _check("qlora_linear_bwd_dx_dropout", lib.qlora_linear_bwd_dx_dropout(
+            ctypes.byref(cw), _ptr(dy), M, a, b, r, float(alpha), float(p), int(seed), _ptr(dx),
+            _ptr(t_out), _ptr(ws), wsb, _stream(stream)))
     return dx
+
+
+def lora_dropout(x, p, seed, out=None, stream=None):
+    """The LoRA branch's dropped input bf16[M, K]: x * keep / (1 - p), Philox mask."""
+    torch = _torch()
+    lib = load_library()
+    M, K = x.shape
+    _dev(x, torch.bfloat16, M * K, "x")
+    if out is None:
+        out = torch.empty_like(x)
+    _dev(out, torch.bfloat16, M * K, "out")
+    _check("lora_dropout", lib.lora_dropout(_ptr(x), M, K, float(p), int(seed), _ptr(out),
+                                            _stream(stream)))
+    return out
 
 
 def lora_grads(x, dy, A, B, r, alpha, u=None, t=None, dA=None, dB=None, ws=None, stream=None):

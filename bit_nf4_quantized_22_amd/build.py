@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libqlora_nf4.so")
 
 SOURCES = ["qn_tables.cpp", "qn_api.cpp", "qn_quant.hip", "qn_gemv.hip", "qn_gemm.hip",
-           "qn_grads.hip", "qn_merge.hip", "qn_optim.hip"]
+           "qn_grads.hip", "qn_merge.hip", "qn_optim.hip", "qn_dropout.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-fvisibility=hidden",

@@ -91,6 +91,91 @@ size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
          round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
 }
 
+// Forward with the LoRA-down input xa (x itself, or the dropped x).
+int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M, const qn_bf16* A,
+             const qn_bf16* B, int32_t r, float alpha, qn_bf16* y, qn_bf16* u_out, void* ws,
+             size_t ws_bytes, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, true);
+  if (st != QN_OK) return st;
+  if (M < 0 || r < 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (M == 0 || w->N == 0) return QN_OK;
+  if (!x || !xa || !y || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(xa, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2))) ||
+      (u_out && !aligned(u_out, 2)))
+    return QN_ERR_ALIGN;
+  const size_t need = fwd_ws(M, r);
+  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  // u = x A^T as fp32 partial sums over L-slices, added up (in slice order)
+  // by the GEMV or GEMM that applies the LoRA-up term
+  float* u32 = nullptr;
+  const bool decode = M <= kGemvMaxM;
+  const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K))
+                        : qn::skinny_wide_splits(M, w->K);
+  if (r > 0) {
+    u32 = static_cast<float*>(ws);
+    if (qn::launch_skinny(xa, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s) != hipSuccess)
+      return QN_ERR_HIP;
+  }
+  if (decode)
+    return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, ks, B, r, scale, y,
+                                      r > 0 ? u_out : nullptr, s));
+  uint16_t* us = nullptr;
+  if (r > 0) {
+    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(M, r));
+    if (qn::launch_lora_reduce(u32, ks, M * r, scale, us, u_out, s) != hipSuccess) return QN_ERR_HIP;
+  }
+  return hip_status(qn::launch_gemm_fwd(v, x, M, us, B, r, y, s));
+}
+
+// Backward to the input; with drop, the LoRA term is masked by the dropout
+// of the adapter's input (base GEMM alone, then dx += D * (s t A)).
+int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A, const qn_bf16* B,
+             int32_t r, float alpha, const float* drop_p, uint64_t seed, qn_bf16* dx,
+             qn_bf16* t_out, void* ws, size_t ws_bytes, void* stream) {
+  qn::WeightView v;
+  int st = check_weight(w, v, true);
+  if (st != QN_OK) return st;
+  if (M < 0 || r < 0) return QN_ERR_SHAPE;
+  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
+  if (M == 0 || w->K == 0) return QN_OK;
+  if (!dy || !dx || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
+      (t_out && !aligned(t_out, 2)))
+    return QN_ERR_ALIGN;
+  const size_t need = bwd_ws(M, w->N, r);
+  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
+  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
+  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
+  // t = dy B (through B^T, so both operands are row-major) as fp32 partial
+  // sums over N-slices, added up by the GEMM
+  uint16_t* ts = nullptr;
+  const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
+  const int ks = qn::skinny_wide_splits(mp, w->N);
+  if (r > 0) {
+    float* t32 = static_cast<float*>(ws);
+    ts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r));
+    uint16_t* bt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r) +
+                                               lora_bf16_bytes(M, r));
+    if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
+    if (qn::launch_skinny(dy, M, w->N, bt, r, scale, t32, nullptr, nullptr, ks, s) != hipSuccess)
+      return QN_ERR_HIP;
+    if (qn::launch_lora_reduce(t32, ks, M * r, scale, ts, t_out, s) != hipSuccess) return QN_ERR_HIP;
+  }
+  if (!drop_p || r == 0) return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
+  if (qn::launch_gemm_bwd(v, dy, M, nullptr, nullptr, 0, dx, s) != hipSuccess) return QN_ERR_HIP;
+  return hip_status(qn::launch_dx_lora_dropout(dx, ts, A, M, w->K, r, *drop_p, seed, s));
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,81 +253,38 @@ size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
 int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_bf16* A,
                      const qn_bf16* B, int32_t r, float alpha, qn_bf16* y, qn_bf16* u_out,
                      void* ws, size_t ws_bytes, void* stream) {
-  qn::WeightView v;
-  int st = check_weight(w, v, true);
-  if (st != QN_OK) return st;
-  if (M < 0 || r < 0) return QN_ERR_SHAPE;
-  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
-  if (M == 0 || w->N == 0) return QN_OK;
-  if (!x || !y || (r > 0 && (!A || !B))) return QN_ERR_NULL;
-  if (!aligned(x, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2))) ||
-      (u_out && !aligned(u_out, 2)))
-    return QN_ERR_ALIGN;
-  const size_t need = fwd_ws(M, r);
-  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
-  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
-  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
-  hipStream_t s = as_stream(stream);
-  (void)hipGetLastError();
-  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  // u = x A^T as fp32 partial sums over L-slices, added up (in slice order)
-  // by the GEMV or GEMM that applies the LoRA-up term
-  float* u32 = nullptr;
-  const bool decode = M <= kGemvMaxM;
-  const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K))
-                        : qn::skinny_wide_splits(M, w->K);
-  if (r > 0) {
-    u32 = static_cast<float*>(ws);
-    if (qn::launch_skinny(x, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s) != hipSuccess)
-      return QN_ERR_HIP;
-  }
-  if (decode)
-    return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, ks, B, r, scale, y,
-                                      r > 0 ? u_out : nullptr, s));
-  uint16_t* us = nullptr;
-  if (r > 0) {
-    us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(M, r));
-    if (qn::launch_lora_reduce(u32, ks, M * r, scale, us, u_out, s) != hipSuccess) return QN_ERR_HIP;
-  }
-  return hip_status(qn::launch_gemm_fwd(v, x, M, us, B, r, y, s));
+  return fwd_impl(w, x, x, M, A, B, r, alpha, y, u_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_dropout(const qn_weight* w, const qn_bf16* x, const qn_bf16* x_drop,
+                             int64_t M, const qn_bf16* A, const qn_bf16* B, int32_t r,
+                             float alpha, qn_bf16* y, qn_bf16* u_out, void* ws, size_t ws_bytes,
+                             void* stream) {
+  return fwd_impl(w, x, x_drop, M, A, B, r, alpha, y, u_out, ws, ws_bytes, stream);
 }
 
 int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
                         const qn_bf16* B, int32_t r, float alpha, qn_bf16* dx, qn_bf16* t_out,
                         void* ws, size_t ws_bytes, void* stream) {
-  qn::WeightView v;
-  int st = check_weight(w, v, true);
-  if (st != QN_OK) return st;
-  if (M < 0 || r < 0) return QN_ERR_SHAPE;
-  if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
-  if (M == 0 || w->K == 0) return QN_OK;
-  if (!dy || !dx || (r > 0 && (!A || !B))) return QN_ERR_NULL;
-  if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
-      (t_out && !aligned(t_out, 2)))
-    return QN_ERR_ALIGN;
-  const size_t need = bwd_ws(M, w->N, r);
-  if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
-  if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
-  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
-  hipStream_t s = as_stream(stream);
+  return bwd_impl(w, dy, M, A, B, r, alpha, nullptr, 0, dx, t_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_bwd_dx_dropout(const qn_weight* w, const qn_bf16* dy, int64_t M,
+                                const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,
+                                float p, uint64_t seed, qn_bf16* dx, qn_bf16* t_out, void* ws,
+                                size_t ws_bytes, void* stream) {
+  if (!(p >= 0.0f && p < 1.0f)) return QN_ERR_SHAPE;
+  return bwd_impl(w, dy, M, A, B, r, alpha, &p, seed, dx, t_out, ws, ws_bytes, stream);
+}
+
+int lora_dropout(const qn_bf16* x, int64_t M, int64_t K, float p, uint64_t seed, qn_bf16* x_drop,
+                 void* stream) {
+  if (M < 0 || K < 0 || K % 8 != 0 || !(p >= 0.0f && p < 1.0f)) return QN_ERR_SHAPE;
+  if (M == 0 || K == 0) return QN_OK;
+  if (!x || !x_drop) return QN_ERR_NULL;
+  if (!aligned(x, 16) || !aligned(x_drop, 16)) return QN_ERR_ALIGN;
   (void)hipGetLastError();
-  const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  // t = dy B (through B^T, so both operands are row-major) as fp32 partial
-  // sums over N-slices, added up by the GEMM
-  uint16_t* ts = nullptr;
-  const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
-  const int ks = qn::skinny_wide_splits(mp, w->N);
-  if (r > 0) {
-    float* t32 = static_cast<float*>(ws);
-    ts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r));
-    uint16_t* bt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r) +
-                                               lora_bf16_bytes(M, r));
-    if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
-    if (qn::launch_skinny(dy, M, w->N, bt, r, scale, t32, nullptr, nullptr, ks, s) != hipSuccess)
-      return QN_ERR_HIP;
-    if (qn::launch_lora_reduce(t32, ks, M * r, scale, ts, t_out, s) != hipSuccess) return QN_ERR_HIP;
-  }
-  return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
+  return hip_status(qn::launch_dropout(x, M, K, p, seed, x_drop, as_stream(stream)));
 }
 
 int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,

@@ -78,6 +78,21 @@ hipError_t launch_adamw(float* p, const float* g, float* m, float* v, uint16_t* 
                         float lr, float beta1, float beta2, float eps, float weight_decay, int step,
                         hipStream_t st);
 
+// LoRA dropout on the adapter branch (see lora_dropout in the C ABI):
+// threshold = floor(p 2^32) on the 32-bit Philox halves, inv_keep =
+// fl32(1 / (1 - p)), both from fp64 on the host.
+struct DropoutParams {
+  uint32_t threshold;
+  float inv_keep;
+};
+DropoutParams dropout_params(float p);
+// out[M, K] = x * keep / (1 - p) in bf16 (dropped elements +0); K % 8 == 0.
+hipError_t launch_dropout(const uint16_t* x, int64_t M, int64_t K, float p, uint64_t seed,
+                          uint16_t* out, hipStream_t st);
+// dx[M, K] += keep * (ts A) / (1 - p), ts = bf16(s t) [M, r], A [r, K].
+hipError_t launch_dx_lora_dropout(uint16_t* dx, const uint16_t* ts, const uint16_t* A, int64_t M,
+                                  int64_t K, int r, float p, uint64_t seed, hipStream_t st);
+
 // LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
 // fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.
 size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);

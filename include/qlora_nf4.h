@@ -219,6 +219,51 @@ QN_API int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u,
                float* dA, float* dB, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * lora_dropout -- the dropped input of the LoRA branch, x * keep / (1 - p).
+ * [rkmt] §3.3 gives the LoRA layer a dropout rate (0.1; [czcl] §3.2 and
+ * [kwkr] §4 use 0.05); it acts on the adapter's input only, the frozen
+ * path sees x.  The keep mask is a pure function of (seed, m, k), so the
+ * backward regenerates it: element (m, k) uses the Philox4x64-10 block
+ * (Salmon et al., SC 2011) at counter (k, m / 8, 0, 0), key (seed, 0); row
+ * m % 8 reads the 32-bit half (m % 8) % 2 (low first) of 64-bit word
+ * (m % 8) / 2 and is kept iff it is >= floor(p * 2^32).
+ *   x       device bf16[M, K], 16-byte aligned; K % 8 == 0.
+ *   x_drop  device bf16[M, K] out, 16-byte aligned, not overlapping x.
+ *           Kept: bf16(fl32(x * fl32(1 / (1 - p)))); dropped: +0.
+ *   p       0 <= p < 1 (else QN_ERR_SHAPE); p = 0 copies x bit for bit.
+ * Feed x_drop to qlora_linear_fwd_dropout and, as its x, to lora_grads.
+ * Use a distinct seed per layer and step.
+ */
+QN_API int lora_dropout(const qn_bf16* x, int64_t M, int64_t K, float p, uint64_t seed,
+                        qn_bf16* x_drop, void* stream);
+
+/*
+ * qlora_linear_fwd_dropout -- y = x * dequant(W)^T + (alpha/r) *
+ * (x_drop * A^T) * B^T: the forward with LoRA dropout ([rkmt] §3.3), the
+ * base product on x and the adapter on x_drop (from lora_dropout).
+ * Arguments, workspace (QN_OP_FWD) and errors as qlora_linear_fwd; x_drop
+ * is device bf16[M, K], 16-byte aligned; u_out receives x_drop * A^T.
+ */
+QN_API int qlora_linear_fwd_dropout(const qn_weight* w, const qn_bf16* x,
+                                    const qn_bf16* x_drop, int64_t M, const qn_bf16* A,
+                                    const qn_bf16* B, int32_t r, float alpha, qn_bf16* y,
+                                    qn_bf16* u_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * qlora_linear_bwd_dx_dropout -- dx = dy * dequant(W) + D * ((alpha/r) *
+ * (dy * B) * A), D = keep / (1 - p) with the mask of lora_dropout for the
+ * same (p, seed) regenerated in place: the chain rule through the dropped
+ * adapter input ([rkmt] §3.3; [kwkr] §2.3).  The LoRA term is added to the
+ * bf16 base product in a second pass, so dx is rounded to bf16 twice.
+ * Arguments, workspace (QN_OP_BWD_DX) and errors as qlora_linear_bwd_dx;
+ * p outside [0, 1) is QN_ERR_SHAPE.
+ */
+QN_API int qlora_linear_bwd_dx_dropout(const qn_weight* w, const qn_bf16* dy, int64_t M,
+                                       const qn_bf16* A, const qn_bf16* B, int32_t r,
+                                       float alpha, float p, uint64_t seed, qn_bf16* dx,
+                                       qn_bf16* t_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * lora_adamw_step -- one AdamW step on a LoRA matrix (A or B), in place.
  * [rkmt] §3.5, [czcl] §3.2: the adapter is trained with AdamW (32-bit
  * states, learning rate 2e-4), the only trainable parameters being A and

@@ -168,3 +168,32 @@ def test_adamw_argument_errors(lib):
     assert call(m=ODD) == qn.QN_ERR_ALIGN
     assert call(pb=ODD) == qn.QN_ERR_ALIGN
     assert call(p=None, g=None, m=None, v=None, n=0) == qn.QN_OK
+
+
+def test_dropout_argument_errors(lib):
+    drop = lib.lora_dropout
+    assert drop(FAKE, 16, 60, 0.1, 1, FAKE, None) == qn.QN_ERR_SHAPE      # K % 8
+    assert drop(FAKE, 16, 64, 1.0, 1, FAKE, None) == qn.QN_ERR_SHAPE      # p = 1
+    assert drop(FAKE, 16, 64, -0.1, 1, FAKE, None) == qn.QN_ERR_SHAPE
+    assert drop(FAKE, -1, 64, 0.1, 1, FAKE, None) == qn.QN_ERR_SHAPE
+    assert drop(None, 16, 64, 0.1, 1, FAKE, None) == qn.QN_ERR_NULL
+    assert drop(FAKE, 16, 64, 0.1, 1, ODD, None) == qn.QN_ERR_ALIGN
+    assert drop(None, 0, 64, 0.1, 1, None, None) == qn.QN_OK
+    assert drop(FAKE, 16, 64, 0.1, 2**64 - 1, ODD, None) == qn.QN_ERR_ALIGN  # full 64-bit seed
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256)
+    ws_need = qn.qn_workspace_bytes(qn.QN_OP_FWD, 32, 128, 128, 8)
+    fwd = lib.qlora_linear_fwd_dropout
+    assert fwd(ctypes.byref(w), FAKE, None, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_need,
+               None) == qn.QN_ERR_NULL
+    assert fwd(ctypes.byref(w), FAKE, ODD, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, ws_need,
+               None) == qn.QN_ERR_ALIGN
+    assert fwd(ctypes.byref(w), FAKE, FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None, FAKE, 0,
+               None) == qn.QN_ERR_WORKSPACE
+    bwd = lib.qlora_linear_bwd_dx_dropout
+    ws_b = qn.qn_workspace_bytes(qn.QN_OP_BWD_DX, 32, 128, 128, 8)
+    assert bwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, 1.0, 1, FAKE, None, FAKE, ws_b,
+               None) == qn.QN_ERR_SHAPE
+    assert bwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, FAKE, None, FAKE, 0,
+               None) == qn.QN_ERR_WORKSPACE
+    assert bwd(ctypes.byref(w), None, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, FAKE, None, FAKE, ws_b,
+               None) == qn.QN_ERR_NULL
