@@ -28,6 +28,11 @@ beyond the Infinity Cache) quantised in turn 10 times over.
 "adamw_7b_lora" times lora_adamw_step over all 40 M LoRA parameters of a
 7B model at r = 16 (seven projections x 32 layers).
 
+"dropout" times LoRA dropout (p = 0.05) on the same two training-step
+linears: lora_dropout of x (2048 x 4096 or 2048 x 11008 bf16, read once and
+written once) and the forward / backward-to-input calls with dropout,
+against the same calls without it.
+
 "unfused_context" times, as context only, the unfused way of doing the
 same base products: nf4_dequant to bf16 in HBM, then torch's bf16 GEMM.
 
@@ -223,6 +228,51 @@ def adamw_7b_lora(qn, torch, dev, synth, steps=10):
     torch.cuda.empty_cache()
     return {"params": n, "ms_per_step": round(ms, 4), "GBps": round(gbps, 1),
             "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+
+
+def dropout_cost(qn, torch, layers, reps=10, p=0.05, seed=7):
+    """lora_dropout GB/s and the time the dropout variants add to fwd + bwd."""
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    xd = [torch.empty_like(L["x"]) for L in layers]
+
+    def drop():
+        for L, o in zip(layers, xd):
+            qn.lora_dropout(L["x"], p, seed, out=o)
+
+    def plain():
+        for L in layers:
+            qn.qlora_linear_fwd(L["qw"], L["x"], L["A"], L["B"], RANK, ALPHA, y=L["y"],
+                                u_out=L["u"], ws=L["ws"])
+            qn.qlora_linear_bwd_dx(L["qw"], L["dy"], L["A"], L["B"], RANK, ALPHA, dx=L["dx"],
+                                   t_out=L["t"], ws=L["ws"])
+
+    def dropped():
+        for L, o in zip(layers, xd):
+            qn.qlora_linear_fwd_dropout(L["qw"], L["x"], o, L["A"], L["B"], RANK, ALPHA,
+                                        y=L["y"], u_out=L["u"], ws=L["ws"])
+            qn.qlora_linear_bwd_dx_dropout(L["qw"], L["dy"], L["A"], L["B"], RANK, ALPHA, p, seed,
+                                           dx=L["dx"], t_out=L["t"], ws=L["ws"])
+
+    ms_drop = timed(drop)
+    ms_plain = timed(plain)
+    ms_dropped = timed(dropped)
+    nbytes = sum(2 * 2 * M_TRAIN * L["K"] for L in layers)
+    gbps = nbytes / (ms_drop * 1e-3) / 1e9
+    return {"p": p, "lora_dropout_ms": round(ms_drop, 4), "lora_dropout_GBps": round(gbps, 1),
+            "lora_dropout_frac_hbm": round(gbps / PEAK_HBM_GBPS, 4),
+            "fwd_bwd_ms": round(ms_plain, 4), "fwd_bwd_dropout_ms": round(ms_dropped, 4),
+            "added_ms_incl_lora_dropout": round(ms_dropped + ms_drop - ms_plain, 4)}
 
 
 def quantise_65b(qn, torch, dev, synth):
@@ -473,6 +523,7 @@ def main():
     out["unfused_context"] = unfused_context(qn, torch, layers)
     out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
     out["adamw_7b_lora"] = adamw_7b_lora(qn, torch, dev, synth)
+    out["dropout"] = dropout_cost(qn, torch, layers)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(workloads)
     print(json.dumps(out))

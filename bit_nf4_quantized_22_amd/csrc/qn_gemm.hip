@@ -243,6 +243,25 @@ __device__ __forceinline__ void load_frags(const uint16_t* __restrict__ sA,
     f.b[j] = *reinterpret_cast<const uint4*>(sB + (wn * (kBN / 2) + j * 32 + li) * kLD + kk * 16 + 8 * lg);
 }
 
+// Rank <= 16 LoRA tiles staged at the start: activation [kBM][16] and weight
+// [kBN][16], rows of 32 bytes (a wave's 16-byte fragment reads cover 1 KB
+// contiguously: no bank conflicts).
+constexpr int kLoraEarly = 16;
+constexpr int kLoraPer = (kBM + kBN) * kLoraEarly / kThreads;  // elements per thread
+
+__device__ __forceinline__ void load_frags_lora(const uint16_t* __restrict__ sLA,
+                                                const uint16_t* __restrict__ sLW, Frags& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int li = lane & 31, lg = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < kTM; ++i)
+    f.a[i] = *reinterpret_cast<const uint4*>(sLA + (wm * (kBM / 2) + i * 32 + li) * kLoraEarly + 8 * lg);
+#pragma unroll
+  for (int j = 0; j < kTN; ++j)
+    f.b[j] = *reinterpret_cast<const uint4*>(sLW + (wn * (kBN / 2) + j * 32 + li) * kLoraEarly + 8 * lg);
+}
+
 __device__ __forceinline__ void mma_frags(const Frags& f, f32x16_t (&acc)[kTM][kTN]) {
 #pragma unroll
   for (int i = 0; i < kTM; ++i)
@@ -304,6 +323,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   __shared__ __attribute__((aligned(16))) uint16_t sA2[kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLD];
   __shared__ __attribute__((aligned(16))) float scode[16 * 64];  // q[c] for lane l at [64 c + l]
+  __shared__ __attribute__((aligned(16))) uint16_t sLA[kBM * kLoraEarly];
+  __shared__ __attribute__((aligned(16))) uint16_t sLW[kBN * kLoraEarly];
   const int t = threadIdx.x;
   {
     const CodeRegs R = code_regs(P);
@@ -327,6 +348,58 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
+  // LoRA operands of rank <= 16: loaded here, from clamped in-bounds
+  // addresses, and written to sLA / sLW after each role has issued its
+  // prologue loads, so their latency overlaps the pipeline start.  Element
+  // c < kBM * 16 is lact[m0 + c / 16][c % 16]; the rest is the weight side:
+  // B[c0 + n][j] (forward) or A[j][c0 + kcol] (backward).
+  const bool early = g.r > 0 && g.r <= kLoraEarly;
+  uint32_t lv[kLoraPer];
+  uint32_t lok = 0;
+  if (early) {
+#pragma unroll
+    for (int i = 0; i < kLoraPer; ++i) {
+      const int ci = i * kThreads;  // thread-independent: which tile
+      const int c = ci + t;
+      if (ci < kBM * kLoraEarly) {
+        const int row = c / kLoraEarly, col = c % kLoraEarly;
+        const int64_t m = m0 + row;
+        lok |= static_cast<uint32_t>(m < g.M && col < g.r) << i;
+        lv[i] = g.lact[(m < g.M ? m : g.M - 1) * g.r + (col < g.r ? col : g.r - 1)];
+      } else {
+        const int e = c - kBM * kLoraEarly;
+        if constexpr (kBwd) {
+          const int j = e / kBN, kcol = e % kBN;
+          lok |= static_cast<uint32_t>(j < g.r && c0 + kcol < g.K) << i;
+          lv[i] = g.lw[static_cast<int64_t>(j < g.r ? j : g.r - 1) * g.K +
+                       (c0 + kcol < g.K ? c0 + kcol : g.K - 1)];
+        } else {
+          const int n = e / kLoraEarly, j = e % kLoraEarly;
+          lok |= static_cast<uint32_t>(c0 + n < g.N && j < g.r) << i;
+          lv[i] = g.lw[(c0 + n < g.N ? c0 + n : g.N - 1) * g.r + (j < g.r ? j : g.r - 1)];
+        }
+      }
+    }
+  }
+  auto store_lora = [&]() {
+    if (!early) return;
+#pragma unroll
+    for (int i = 0; i < kLoraPer; ++i) {
+      const int ci = i * kThreads;
+      const int c = ci + t;
+      const uint16_t val = (lok >> i) & 1u ? static_cast<uint16_t>(lv[i]) : uint16_t{0};
+      if (ci < kBM * kLoraEarly) {
+        sLA[c] = val;
+      } else {
+        const int e = c - kBM * kLoraEarly;
+        if constexpr (kBwd)
+          sLW[(e % kBN) * kLoraEarly + e / kBN] = val;
+        else
+          sLW[e] = val;
+      }
+    }
+  };
+
   // Waves 0-3 run the MFMAs and fetch the activation tiles by DMA; waves
   // 4-11 load and dequantise the weight.  Per K step k: the MFMA waves
   // consume activation buffer k % 3 and weight buffer k % 2, and start the
@@ -340,7 +413,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     load_step<kBwd, kDQ>(g, c0, 0, p0, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 1 ? 1 : nk - 1, p1, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 2 ? 2 : nk - 1, p2, pt);
-    __syncthreads();  // code table visible
+    store_lora();
+    __syncthreads();  // code table (and the LoRA tiles) visible
     store_step<kBwd>(p0, chunk_scale<kDQ>(p0), scode, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
@@ -367,6 +441,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     const uint16_t* act_tile = g.act + m0 * L;
     adma_issue(ad, act_tile, 0, sA0);
     adma_issue(ad, act_tile, nk > 1 ? 1 : nk - 1, sA1);
+    store_lora();
     __syncthreads();
     adma_wait_one_step();  // step 0 landed
     __syncthreads();
@@ -389,31 +464,72 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   }
   __syncthreads();
 
-  // LoRA contraction of depth r, kBK at a time, through sA0 and sB[0].
-  for (int j0 = 0; j0 < g.r; j0 += kBK) {
-    for (int c = t; c < kBM * kBK; c += kThreads) {
-      const int row = c / kBK, col = c % kBK;
-      const int64_t m = m0 + row;
-      uint16_t v = 0;
-      if (m < g.M && j0 + col < g.r) v = g.lact[m * g.r + j0 + col];
-      sA0[row * kBK + (((col >> 3) ^ swz(row)) << 3) + (col & 7)] = v;
+  // LoRA contraction of depth r, kBK at a time, through sA0 and sB[0].  Only
+  // the dp = ceil16(depth) columns the MFMAs read are filled (zero past r).
+  // The elements of both tiles form one list, taken 16 per thread at a time:
+  // all 16 loads are issued before the first LDS store, so r <= 16 costs one
+  // memory round trip (12 elements per thread) and r = 64 three.
+  // Consecutive threads read consecutive elements of a row of lact, B or A.
+  constexpr int kBatch = 16;
+  if (early) {
+    if (t < 64 * kMmaWaves) {
+      Frags f;
+      load_frags_lora(sLA, sLW, f);
+      mma_frags(f, acc);
     }
-    for (int c = t; c < kBN * kBK; c += kThreads) {
-      uint16_t v = 0;
-      if constexpr (kBwd) {  // sB[kcol][j] = A[j0 + j][c0 + kcol]
-        const int kcol = c % kBN, j = c / kBN;
-        if (j0 + j < g.r && c0 + kcol < g.K) v = g.lw[static_cast<int64_t>(j0 + j) * g.K + c0 + kcol];
-        sB[0][kcol * kLD + j] = v;
-      } else {               // sB[n][j] = B[c0 + n][j0 + j]
-        const int n = c / kBK, j = c % kBK;
-        if (c0 + n < g.N && j0 + j < g.r) v = g.lw[(c0 + n) * g.r + j0 + j];
-        sB[0][n * kLD + j] = v;
+  }
+  for (int j0 = 0; !early && j0 < g.r; j0 += kBK) {
+    const int depth = g.r - j0 < kBK ? g.r - j0 : kBK;
+    const int dp = (depth + 15) & ~15;
+    const int na = kBM * dp, ntot = na + kBN * dp;  // both multiples of kThreads
+    for (int base = 0; base < ntot; base += kBatch * kThreads) {
+      // loads from clamped, in-bounds addresses; invalid elements are zeroed
+      // at the LDS store (no write to a register with a load in flight)
+      uint32_t v[kBatch];
+      uint32_t ok = 0;
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int ci = base + i * kThreads;  // thread-independent: which tile
+        const int c = ci + t;
+        if (ci < na) {
+          const int row = c / dp, col = c % dp;
+          const int64_t m = m0 + row;
+          ok |= static_cast<uint32_t>(m < g.M && col < depth) << i;
+          v[i] = g.lact[(m < g.M ? m : g.M - 1) * g.r + j0 + (col < depth ? col : depth - 1)];
+        } else if (ci < ntot) {
+          const int e = c - na;
+          if constexpr (kBwd) {  // A[j0 + j][c0 + kcol]
+            const int j = e / kBN, kcol = e % kBN;
+            ok |= static_cast<uint32_t>(j < depth && c0 + kcol < g.K) << i;
+            v[i] = g.lw[static_cast<int64_t>(j0 + (j < depth ? j : depth - 1)) * g.K +
+                        (c0 + kcol < g.K ? c0 + kcol : g.K - 1)];
+          } else {               // B[c0 + n][j0 + j]
+            const int n = e / dp, j = e % dp;
+            ok |= static_cast<uint32_t>(c0 + n < g.N && j < depth) << i;
+            v[i] = g.lw[(c0 + n < g.N ? c0 + n : g.N - 1) * g.r + j0 + (j < depth ? j : depth - 1)];
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int ci = base + i * kThreads;
+        const int c = ci + t;
+        const uint16_t val = (ok >> i) & 1u ? static_cast<uint16_t>(v[i]) : uint16_t{0};
+        if (ci < na) {
+          const int row = c / dp, col = c % dp;
+          sA0[row * kBK + (((col >> 3) ^ swz(row)) << 3) + (col & 7)] = val;
+        } else if (ci < ntot) {
+          const int e = c - na;
+          if constexpr (kBwd)  // sB[kcol][j]
+            sB[0][(e % kBN) * kLD + e / kBN] = val;
+          else                 // sB[n][j]
+            sB[0][(e / dp) * kLD + e % dp] = val;
+        }
       }
     }
     __syncthreads();
-    const int depth = g.r - j0 < kBK ? g.r - j0 : kBK;
     if (t < 64 * kMmaWaves)
-      for (int kk = 0; kk < (depth + 15) >> 4; ++kk) mma_k16(sA0, sB[0], kk, acc);
+      for (int kk = 0; kk < dp >> 4; ++kk) mma_k16(sA0, sB[0], kk, acc);
     __syncthreads();
   }
   if (t >= 64 * kMmaWaves) return;
