@@ -16,6 +16,8 @@ Modules
   optim   -- the AdamW step on the LoRA matrices (fp64).
   dropout -- LoRA dropout on the adapter branch: the counter-based mask
              (Philox4x64-10) and the dropped forward, backward (fp64).
+  codebooks -- the FP4 weight table, the FP8 (E4M3) level-2 code and the
+             uniform INT4 strawman of the error study.
 
 Every function names the page and section it follows.  Pages are cited by
 title (site in brackets):
@@ -31,4 +33,4 @@ table printed in the original publication, which none of the pages carries
 (parity unpinned for that comparison only).
 """
 
-from . import nf4, linear, memory, optim, dropout  # noqa: F401
+from . import nf4, linear, memory, optim, dropout, codebooks  # noqa: F401
