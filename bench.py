@@ -264,9 +264,9 @@ def dropout_cost(qn, torch, layers, reps=10, p=0.05, seed=7):
             qn.qlora_linear_bwd_dx_dropout(L["qw"], L["dy"], L["A"], L["B"], RANK, ALPHA, p, seed,
                                            dx=L["dx"], t_out=L["t"], ws=L["ws"])
 
-    ms_drop = timed(drop)
-    ms_plain = timed(plain)
-    ms_dropped = timed(dropped)
+    # interleaved rounds, medians: the clock drifts between back-to-back runs
+    rounds = [(timed(drop), timed(plain), timed(dropped)) for _ in range(5)]
+    ms_drop, ms_plain, ms_dropped = (float(np.median([r[i] for r in rounds])) for i in range(3))
     nbytes = sum(2 * 2 * M_TRAIN * L["K"] for L in layers)
     gbps = nbytes / (ms_drop * 1e-3) / 1e9
     return {"p": p, "lora_dropout_ms": round(ms_drop, 4), "lora_dropout_GBps": round(gbps, 1),

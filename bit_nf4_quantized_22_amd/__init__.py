@@ -27,7 +27,8 @@ BLOCKSIZE, GROUP = 64, 256
 EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
-           "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout")
+           "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
+           "fp4_quantize", "dq_quantize_scales_fp8")
 
 
 class QnError(RuntimeError):
@@ -40,7 +41,8 @@ class qn_weight(ctypes.Structure):
     _fields_ = [("packed", ctypes.c_void_p), ("qscale", ctypes.c_void_p),
                 ("gscale", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64),
-                ("blocksize", ctypes.c_int32), ("group", ctypes.c_int32)]
+                ("blocksize", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("quant_type", ctypes.c_int32), ("scale_type", ctypes.c_int32)]
 
 
 _lib = None
@@ -61,8 +63,11 @@ def load_library():
     sig = {
         "qn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "nf4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
+        "fp4_codebook": (ctypes.c_int, [ctypes.POINTER(ctypes.c_float)]),
         "nf4_quantize": (ctypes.c_int, [vp, i32, i64, i32, vp, vp, vp]),
+        "fp4_quantize": (ctypes.c_int, [vp, i32, i64, i32, vp, vp, vp]),
         "dq_quantize_scales": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+        "dq_quantize_scales_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
         "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -118,23 +123,33 @@ def _dev(t, dtype, numel=None, name="tensor"):
     return t
 
 
+QN_NF4, QN_FP4 = 0, 1
+QN_SCALE_U8, QN_SCALE_FP8 = 0, 1
+_QUANT_TYPES = {"nf4": QN_NF4, "fp4": QN_FP4}
+_SCALE_TYPES = {"u8": QN_SCALE_U8, "fp8": QN_SCALE_FP8}
+
+
 class QuantWeight:
-    """Device tensors of an NF4 weight W[N, K] (+ double-quantised constants).
+    """Device tensors of a 4-bit weight W[N, K] (+ double-quantised constants).
 
     packed uint8[N*K/2]; qscale uint8[N*K/64] and gscale fp32[ceil(N*K/64/256)]
-    when double-quantised, else absmax fp32[N*K/64].
+    when double-quantised, else absmax fp32[N*K/64].  quant_type "nf4" or
+    "fp4" (the code table), scale_type "u8" or "fp8" (the level-2 code).
     """
 
-    def __init__(self, packed, N, K, qscale=None, gscale=None, absmax=None):
+    def __init__(self, packed, N, K, qscale=None, gscale=None, absmax=None, quant_type="nf4",
+                 scale_type="u8"):
         self.packed, self.qscale, self.gscale, self.absmax = packed, qscale, gscale, absmax
         self.N, self.K = int(N), int(K)
+        self.quant_type, self.scale_type = quant_type, scale_type
 
     def c_struct(self):
         return qn_weight(self.packed.data_ptr(),
                          None if self.qscale is None else self.qscale.data_ptr(),
                          None if self.gscale is None else self.gscale.data_ptr(),
                          None if self.absmax is None else self.absmax.data_ptr(),
-                         self.N, self.K, BLOCKSIZE, GROUP)
+                         self.N, self.K, BLOCKSIZE, GROUP, _QUANT_TYPES[self.quant_type],
+                         _SCALE_TYPES[self.scale_type])
 
 
 def nf4_codebook():
@@ -144,11 +159,27 @@ def nf4_codebook():
     return list(out)
 
 
+def fp4_codebook():
+    """The 16 fp32 FP4 code points (host call), as a list of floats."""
+    out = (ctypes.c_float * 16)()
+    _check("fp4_codebook", load_library().fp4_codebook(out))
+    return list(out)
+
+
 def nf4_quantize(w, packed=None, absmax=None, stream=None):
     """Blockwise NF4 quantisation of a fp32 or bf16 device tensor (flattened).
 
     Returns (packed uint8[numel/2], absmax fp32[ceil(numel/64)]).
     """
+    return _quantize("nf4_quantize", w, packed, absmax, stream)
+
+
+def fp4_quantize(w, packed=None, absmax=None, stream=None):
+    """nf4_quantize with the FP4 code table."""
+    return _quantize("fp4_quantize", w, packed, absmax, stream)
+
+
+def _quantize(fn, w, packed, absmax, stream):
     torch = _torch()
     lib = load_library()
     if w.dtype == torch.float32:
@@ -156,7 +187,7 @@ def nf4_quantize(w, packed=None, absmax=None, stream=None):
     elif w.dtype == torch.bfloat16:
         dt = QN_BF16
     else:
-        raise ValueError("nf4_quantize: weights must be float32 or bfloat16")
+        raise ValueError(f"{fn}: weights must be float32 or bfloat16")
     _dev(w, w.dtype, name="w")
     n = w.numel()
     nb = -(-n // BLOCKSIZE)
@@ -166,13 +197,14 @@ def nf4_quantize(w, packed=None, absmax=None, stream=None):
         absmax = torch.empty(nb, dtype=torch.float32, device=w.device)
     _dev(packed, torch.uint8, n // 2, "packed")
     _dev(absmax, torch.float32, nb, "absmax")
-    _check("nf4_quantize", lib.nf4_quantize(_ptr(w), dt, n, BLOCKSIZE, _ptr(packed),
-                                            _ptr(absmax), _stream(stream)))
+    _check(fn, getattr(lib, fn)(_ptr(w), dt, n, BLOCKSIZE, _ptr(packed), _ptr(absmax),
+                                _stream(stream)))
     return packed, absmax
 
 
-def dq_quantize_scales(absmax, qscale=None, gscale=None, stream=None):
-    """Double quantisation: returns (qscale uint8[nb], gscale fp32[ceil(nb/256)])."""
+def dq_quantize_scales(absmax, qscale=None, gscale=None, stream=None, fp8=False):
+    """Double quantisation: returns (qscale uint8[nb], gscale fp32[ceil(nb/256)]);
+    fp8 selects the E4M3 level-2 code (dq_quantize_scales_fp8)."""
     torch = _torch()
     lib = load_library()
     _dev(absmax, torch.float32, name="absmax")
@@ -184,19 +216,27 @@ def dq_quantize_scales(absmax, qscale=None, gscale=None, stream=None):
         gscale = torch.empty(ng, dtype=torch.float32, device=absmax.device)
     _dev(qscale, torch.uint8, nb, "qscale")
     _dev(gscale, torch.float32, ng, "gscale")
-    _check("dq_quantize_scales", lib.dq_quantize_scales(_ptr(absmax), nb, GROUP, _ptr(qscale),
-                                                        _ptr(gscale), _stream(stream)))
+    fn = "dq_quantize_scales_fp8" if fp8 else "dq_quantize_scales"
+    _check(fn, getattr(lib, fn)(_ptr(absmax), nb, GROUP, _ptr(qscale), _ptr(gscale),
+                                _stream(stream)))
     return qscale, gscale
 
 
-def quantize_weight(w, double_quant=True, stream=None):
-    """nf4_quantize (+ dq_quantize_scales) of a [N, K] tensor -> QuantWeight."""
+def quantize_weight(w, double_quant=True, stream=None, quant_type="nf4", scale_type="u8"):
+    """4-bit quantisation (+ double quantisation) of a [N, K] tensor -> QuantWeight.
+
+    quant_type "nf4" (nf4_quantize) or "fp4" (fp4_quantize); scale_type "u8"
+    (dq_quantize_scales) or "fp8" (dq_quantize_scales_fp8)."""
+    if quant_type not in _QUANT_TYPES or scale_type not in _SCALE_TYPES:
+        raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8' or 'fp8'")
     N, K = w.shape
-    packed, absmax = nf4_quantize(w, stream=stream)
+    quant = fp4_quantize if quant_type == "fp4" else nf4_quantize
+    packed, absmax = quant(w, stream=stream)
     if not double_quant:
-        return QuantWeight(packed, N, K, absmax=absmax)
-    qscale, gscale = dq_quantize_scales(absmax, stream=stream)
-    return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale)
+        return QuantWeight(packed, N, K, absmax=absmax, quant_type=quant_type)
+    qscale, gscale = dq_quantize_scales(absmax, stream=stream, fp8=scale_type == "fp8")
+    return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
+                       scale_type=scale_type)
 
 
 def nf4_dequant(qw, out_dtype=None, out=None, stream=None):

@@ -31,6 +31,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? QN_OK : QN_ERR_HIP; }
 int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   if (!w || !w->packed) return QN_ERR_NULL;
   if (w->blocksize != kBlock || w->group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (w->quant_type != QN_NF4 && w->quant_type != QN_FP4) return QN_ERR_UNSUPPORTED;
+  if (w->scale_type != QN_SCALE_U8 && w->scale_type != QN_SCALE_FP8) return QN_ERR_UNSUPPORTED;
+  if (!qn::tables(w->quant_type)) return QN_ERR_UNSUPPORTED;
   if (w->N < 0 || w->K < 0) return QN_ERR_SHAPE;
   if (linear && (w->N <= 0 || w->K <= 0 || w->N % 64 != 0 || w->K % 64 != 0)) return QN_ERR_SHAPE;
   if (w->qscale) {
@@ -47,6 +50,8 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   v.absmax = w->qscale ? nullptr : w->absmax;
   v.N = w->N;
   v.K = w->K;
+  v.quant_type = w->quant_type == QN_FP4 ? qn::kQuantFP4 : qn::kQuantNF4;
+  v.fp8 = w->qscale && w->scale_type == QN_SCALE_FP8 ? 1 : 0;
   return QN_OK;
 }
 
@@ -89,6 +94,39 @@ size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
   return 2 * round_up(mr * 4, 256) + bt_bytes(N, r) +
          round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
+}
+
+int codebook(int qt, float out[16]) {
+  if (!out) return QN_ERR_NULL;
+  const qn::Tables* t = qn::tables(qt);
+  if (!t) return QN_ERR_UNSUPPORTED;
+  std::memcpy(out, t->q32, sizeof(t->q32));
+  return QN_OK;
+}
+
+int quantize(int qt, const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+             uint8_t* packed, float* absmax, void* stream) {
+  if (blocksize != kBlock) return QN_ERR_UNSUPPORTED;
+  if (dtype != QN_F32 && dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
+  if (numel < 0 || (numel & 1)) return QN_ERR_SHAPE;
+  if (numel == 0) return QN_OK;
+  if (!w || !packed || !absmax) return QN_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return QN_ERR_ALIGN;
+  if (!qn::tables(qt)) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(
+      qn::launch_quantize(w, dtype == QN_BF16, numel, qt, packed, absmax, as_stream(stream)));
+}
+
+int dq(bool fp8, const float* absmax, int64_t nblocks, int32_t group, uint8_t* qscale,
+       float* gscale, void* stream) {
+  if (group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (nblocks < 0) return QN_ERR_SHAPE;
+  if (nblocks == 0) return QN_OK;
+  if (!absmax || !qscale || !gscale) return QN_ERR_NULL;
+  if (!aligned(absmax, 4) || !aligned(gscale, 4)) return QN_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_dq(absmax, nblocks, fp8, qscale, gscale, as_stream(stream)));
 }
 
 // Forward with the LoRA-down input xa (x itself, or the dropped x).
@@ -193,37 +231,28 @@ const char* qn_status_string(int status) {
   }
 }
 
-int nf4_codebook(float out[16]) {
-  if (!out) return QN_ERR_NULL;
-  const qn::Tables* t = qn::tables();
-  if (!t) return QN_ERR_UNSUPPORTED;
-  std::memcpy(out, t->q32, sizeof(t->q32));
-  return QN_OK;
-}
+int nf4_codebook(float out[16]) { return codebook(qn::kQuantNF4, out); }
+
+int fp4_codebook(float out[16]) { return codebook(qn::kQuantFP4, out); }
 
 int nf4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
                  uint8_t* packed, float* absmax, void* stream) {
-  if (blocksize != kBlock) return QN_ERR_UNSUPPORTED;
-  if (dtype != QN_F32 && dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
-  if (numel < 0 || (numel & 1)) return QN_ERR_SHAPE;
-  if (numel == 0) return QN_OK;
-  if (!w || !packed || !absmax) return QN_ERR_NULL;
-  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(absmax, 4)) return QN_ERR_ALIGN;
-  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
-  (void)hipGetLastError();
-  return hip_status(qn::launch_quantize(w, dtype == QN_BF16, numel, packed, absmax, as_stream(stream)));
+  return quantize(qn::kQuantNF4, w, dtype, numel, blocksize, packed, absmax, stream);
+}
+
+int fp4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+                 uint8_t* packed, float* absmax, void* stream) {
+  return quantize(qn::kQuantFP4, w, dtype, numel, blocksize, packed, absmax, stream);
 }
 
 int dq_quantize_scales(const float* absmax, int64_t nblocks, int32_t group, uint8_t* qscale,
                        float* gscale, void* stream) {
-  if (group != kGroup) return QN_ERR_UNSUPPORTED;
-  if (nblocks < 0) return QN_ERR_SHAPE;
-  if (nblocks == 0) return QN_OK;
-  if (!absmax || !qscale || !gscale) return QN_ERR_NULL;
-  if (!aligned(absmax, 4) || !aligned(gscale, 4)) return QN_ERR_ALIGN;
-  if (!qn::tables()) return QN_ERR_UNSUPPORTED;
-  (void)hipGetLastError();
-  return hip_status(qn::launch_dq(absmax, nblocks, qscale, gscale, as_stream(stream)));
+  return dq(false, absmax, nblocks, group, qscale, gscale, stream);
+}
+
+int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t group,
+                           uint8_t* qscale, float* gscale, void* stream) {
+  return dq(true, absmax, nblocks, group, qscale, gscale, stream);
 }
 
 int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* stream) {

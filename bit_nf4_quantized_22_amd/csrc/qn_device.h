@@ -30,12 +30,36 @@ __device__ __forceinline__ float l8_value(uint32_t q) {
   return __fdiv_rn(static_cast<float>(q), 255.0f);
 }
 
+// Value of a non-negative E4M3 code q < 0x7F (4 exponent bits, bias 7, 3
+// mantissa bits; subnormals m 2^-9), exact in fp32.
+__device__ __forceinline__ float e4m3_value(uint32_t q) {
+  const uint32_t e = q >> 3, m = q & 7u;
+  return e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : static_cast<float>(m) * 0x1p-9f;
+}
+
+// Nearest E4M3 code of v in [0, 1], ties to the even code: below 2^-6 the
+// subnormal k 2^-9 with k = rne(512 v) (exact scaling; k = 8 is the first
+// normal code), above it the fp32 significand rounded to 3 bits.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+  if (v < 0x1p-6f) return static_cast<uint32_t>(__builtin_rintf(v * 512.0f));
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t m = b & 0x7FFFFFu, rem = m & 0xFFFFFu;
+  const uint32_t code = (((b >> 23) - 120u) << 3) | (m >> 20);
+  return code + ((rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u);
+}
+
+// Level-2 value of code q: the uint8 grid fl32(q / 255), or the E4M3 number.
+__device__ __forceinline__ float l2_value(uint32_t q, int fp8) {
+  return fp8 ? e4m3_value(q) : l8_value(q);
+}
+
 // Block constant c' of block `bi` of a quantised weight: double-dequantised
-// fl32(L8[q8] * c2) when qscale != nullptr, else the stored fp32 absmax.
+// fl32(L2[q8] * c2) when qscale != nullptr, else the stored fp32 absmax.
 __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ qscale,
                                              const float* __restrict__ gscale,
-                                             const float* __restrict__ absmax, int64_t bi) {
-  if (qscale) return __fmul_rn(l8_value(qscale[bi]), gscale[bi >> 8]);
+                                             const float* __restrict__ absmax, int64_t bi,
+                                             int fp8) {
+  if (qscale) return __fmul_rn(l2_value(qscale[bi], fp8), gscale[bi >> 8]);
   return absmax[bi];
 }
 
@@ -56,9 +80,11 @@ __device__ __forceinline__ float wave_sum(float v) {
 // every workgroup); each kernel builds its LDS tables from a few scalars
 // read with wave-uniform indices.
 
-// The 16 NF4 code values (fp32, ascending).
+// The 16 code values of the weight's table (fp32, ascending) and the kind
+// of its level-2 code (0: uint8 grid, 1: E4M3).
 struct CodeParams {
   float q[16];
+  int fp8;
 };
 
 // The 16 code values spread over lanes 0..15 of one VGPR (v_writelane of

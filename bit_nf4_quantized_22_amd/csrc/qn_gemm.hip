@@ -124,8 +124,8 @@ __device__ __forceinline__ void load_step(const GemmArgs& g, int64_t c0, int kt,
 
 // Block constant of a prefetched weight chunk.
 template <bool kDQ>
-__device__ __forceinline__ float chunk_scale(const Prefetch& pf) {
-  return kDQ ? __fmul_rn(l8_value(pf.q8), pf.c) : pf.c;
+__device__ __forceinline__ float chunk_scale(const Prefetch& pf, int fp8) {
+  return kDQ ? __fmul_rn(l2_value(pf.q8, fp8), pf.c) : pf.c;
 }
 
 // Dequantise one K step of weight codes into the LDS weight tile.  All
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     load_step<kBwd, kDQ>(g, c0, nk > 2 ? 2 : nk - 1, p2, pt);
     store_lora();
     __syncthreads();  // code table (and the LoRA tiles) visible
-    store_step<kBwd>(p0, chunk_scale<kDQ>(p0), scode, sB[0], pt);
+    store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.fp8), scode, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
       const int kl = k + 3 < nk ? k + 3 : nk - 1;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
       // the barrier, so the compiler cannot hoist their address arithmetic
       // next to the loads it has just issued and wait for those.
       asm volatile("" : "+v"(dec.w), "+v"(dec.q8), "+v"(dec.c));
-      const float cs = chunk_scale<kDQ>(dec);
+      const float cs = chunk_scale<kDQ>(dec, P.fp8);
       load_step<kBwd, kDQ>(g, c0, kl, ld, pt);
       store_step<kBwd>(dec, cs, scode, sB[(k & 1) ^ 1], pt);
       __syncthreads();
@@ -556,12 +556,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   }
 }
 
-CodeParams code_params() {
-  const Tables* t = tables();
-  CodeParams P;
-  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
-  return P;
-}
 
 }  // namespace
 
@@ -572,9 +566,9 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, x, us, B, r, y};
   const dim3 grid(static_cast<uint32_t>(((w.N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
-    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(kThreads), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(kThreads), 0, st, g, code_params(w));
   else
-    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(kThreads), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<false, false>), grid, dim3(kThreads), 0, st, g, code_params(w));
   return hipGetLastError();
 }
 
@@ -585,9 +579,9 @@ hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
   GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, dy, ts, A, r, dx};
   const dim3 grid(static_cast<uint32_t>(((w.K + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
-    hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(kThreads), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(kThreads), 0, st, g, code_params(w));
   else
-    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(kThreads), 0, st, g, code_params());
+    hipLaunchKernelGGL((gemm_kernel<true, false>), grid, dim3(kThreads), 0, st, g, code_params(w));
   return hipGetLastError();
 }
 

@@ -330,7 +330,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
             code_value_uniform(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
         reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
       }
-      for (int i = tid; i < 256; i += kThreads) sl8[i] = l8_value(static_cast<uint32_t>(i));
+      for (int i = tid; i < 256; i += kThreads) sl8[i] = l2_value(static_cast<uint32_t>(i), P.fp8);
       if constexpr (kXL)
         for (int i = tid; i < kS * 8 + 8; i += kThreads) sxz[i] = make_uint4(0, 0, 0, 0);
       __syncthreads();
@@ -629,9 +629,7 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
                        const uint16_t* B, int r, float s, uint16_t* y, uint16_t* u_out,
                        hipStream_t st) {
   if (M == 0 || w.N == 0) return hipSuccess;
-  const Tables* t = tables();
-  CodeParams P;
-  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
+  const CodeParams P = code_params(w);
   GemvArgs a;
   a.packed = w.packed;
   a.qscale = w.qscale;

@@ -8,18 +8,25 @@
 
 namespace qn {
 
+struct CodeParams;  // qn_device.h
+
 struct WeightView {
   const uint8_t* packed;
   const uint8_t* qscale;  // nullptr: not double-quantised
   const float* gscale;
   const float* absmax;
   int64_t N, K;
+  int quant_type;  // kQuantNF4 or kQuantFP4 (the code table)
+  int fp8;         // level-2 code: 0 uint8 grid, 1 E4M3
 };
 
-hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* packed,
-                           float* absmax, hipStream_t s);
-hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
-                     hipStream_t s);
+// Code values and level-2 kind of a weight, for the kernels.
+CodeParams code_params(const WeightView& w);
+
+hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, int quant_type,
+                           uint8_t* packed, float* absmax, hipStream_t s);
+hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qscale,
+                     float* gscale, hipStream_t s);
 hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s);
 
 // out[M, r] = in[M, L] * P^T, P row-major [r, L] (in and P 16-byte

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
 #pragma unroll
     for (int i = 0; i < kRowBatch; ++i) {
       const int64_t n = n0 + rb + i;
-      const float cs = kDQ ? __fmul_rn(l8_value(q8[i]), c2[i]) : c2[i];
+      const float cs = kDQ ? __fmul_rn(l2_value(q8[i], P.fp8), c2[i]) : c2[i];
       const float w = __fmul_rn(scode[(byte[i] >> shift) & 15], cs);
       float merged = w;
       if constexpr (kR > 0) {
@@ -137,9 +137,7 @@ void merge_launch(const WeightView& w, const uint16_t* A, const uint16_t* B, int
 hipError_t launch_merge(const WeightView& w, const uint16_t* A, const uint16_t* B, int r, float s,
                         uint16_t* out, hipStream_t st) {
   if (w.N == 0 || w.K == 0) return hipSuccess;
-  const Tables* t = tables();
-  CodeParams P;
-  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
+  const CodeParams P = code_params(w);
   if (r == 0) merge_launch<0>(w, A, B, r, s, out, P, st);  // frozen weight: A, B unused
   else if (r <= 16) merge_launch<16>(w, A, B, r, s, out, P, st);
   else if (r <= 32) merge_launch<32>(w, A, B, r, s, out, P, st);

@@ -155,7 +155,10 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
   }
 }
 
-// One workgroup of 256 lanes per group of 256 block constants.
+// One workgroup of 256 lanes per group of 256 block constants.  The code of
+// v = fl32(c / c2) is the nearest level of the uint8 grid fl32(q / 255), or
+// (kFP8) the nearest E4M3 number ([kwkr] §3.1 names fp8 for the constants).
+template <bool kFP8>
 __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restrict__ absmax,
                                                           int64_t nblocks,
                                                           uint8_t* __restrict__ qscale,
@@ -185,9 +188,13 @@ __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restric
     int q = 0;
     if (c2 > 0.0f) {
       const float v = c / c2;  // IEEE division
-      q = static_cast<int>(fminf(fmaxf(fmaf(v, 255.0f, 0.5f), 0.0f), 255.0f));
-      while (q < 255 && v > sthr[q]) ++q;
-      while (q > 0 && !(v > sthr[q - 1])) --q;
+      if constexpr (kFP8) {
+        q = static_cast<int>(e4m3_code(v));
+      } else {
+        q = static_cast<int>(fminf(fmaxf(fmaf(v, 255.0f, 0.5f), 0.0f), 255.0f));
+        while (q < 255 && v > sthr[q]) ++q;
+        while (q > 0 && !(v > sthr[q - 1])) --q;
+      }
     }
     qscale[i] = static_cast<uint8_t>(q);
   }
@@ -204,7 +211,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
   __syncthreads();
   const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 32;
   if (e0 >= numel) return;
-  const float cs = block_scale(qscale, gscale, absmax, e0 >> 6);
+  const float cs = block_scale(qscale, gscale, absmax, e0 >> 6, P.fp8);
   const uint4 pk = *reinterpret_cast<const uint4*>(packed + e0 / 2);
   const uint32_t words[4] = {pk.x, pk.y, pk.z, pk.w};
   float v[32];
@@ -234,10 +241,18 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
 
 }  // namespace
 
-hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* packed,
-                           float* absmax, hipStream_t s) {
+CodeParams code_params(const WeightView& w) {
+  const Tables* t = tables(w.quant_type);
+  CodeParams P;
+  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
+  P.fp8 = w.fp8;
+  return P;
+}
+
+hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, int quant_type,
+                           uint8_t* packed, float* absmax, hipStream_t s) {
   if (numel == 0) return hipSuccess;
-  const Tables* t = tables();
+  const Tables* t = tables(quant_type);
   QuantParams P;
   P.scale = t->bucket_scale;
   P.nbuckets = static_cast<uint32_t>(t->nbuckets);
@@ -252,21 +267,23 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, uint8_t* pac
   return hipGetLastError();
 }
 
-hipError_t launch_dq(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
-                     hipStream_t s) {
+hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qscale,
+                     float* gscale, hipStream_t s) {
   if (nblocks == 0) return hipSuccess;
   const int64_t groups = (nblocks + 255) / 256;
-  hipLaunchKernelGGL(dq_quantize_kernel, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s,
-                     absmax, nblocks, qscale, gscale);
+  if (fp8)
+    hipLaunchKernelGGL(dq_quantize_kernel<true>, dim3(static_cast<uint32_t>(groups)), dim3(256), 0,
+                       s, absmax, nblocks, qscale, gscale);
+  else
+    hipLaunchKernelGGL(dq_quantize_kernel<false>, dim3(static_cast<uint32_t>(groups)), dim3(256),
+                       0, s, absmax, nblocks, qscale, gscale);
   return hipGetLastError();
 }
 
 hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s) {
   const int64_t numel = w.N * w.K;
   if (numel == 0) return hipSuccess;
-  const Tables* t = tables();
-  CodeParams P;
-  for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
+  const CodeParams P = code_params(w);
   const int64_t groups = (numel / 32 + 255) / 256;
   if (out_bf16)
     hipLaunchKernelGGL(nf4_dequant_kernel<true>, dim3(static_cast<uint32_t>(groups)), dim3(256),

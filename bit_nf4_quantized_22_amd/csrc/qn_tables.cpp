@@ -1,5 +1,5 @@
-// Host construction of the read-only tables: NF4 code points, the exact
-// fp32 decision thresholds of the nearest-code search, the 8-bit level
+// Host construction of the read-only tables: code points (NF4 or FP4), the
+// exact fp32 decision thresholds of the nearest-code search, the 8-bit level
 // table of the double quantisation, and the byte-pair decode tables.
 //
 // NF4 code points: [kwkr "QLoRA原理深入" §2.2] standard-normal quantiles as
@@ -9,6 +9,13 @@
 // side, 7 on the negative side, plus 0, divided by the quantile at P, with
 // P = 1 - (1/32 + 1/30)/2 (the truncation point is not given on the pages;
 // this is the value chosen).
+//
+// FP4 code points: [kwkr "QLoRA原理深入" §4.1] names fp4 as the alternative
+// type (made for floating-point distributions, worse than NF4 for weights)
+// without giving its format.  Taken as E2M1 (sign, 2 exponent bits, 1
+// mantissa bit: magnitudes 0, 1/2, 1, 3/2, 2, 3, 4, 6) divided by 6, so the
+// block absmax maps to the largest code; its 15 values fill 16 ascending
+// entries with 0 at indices 7 and 8.
 
 #include "qn_tables.h"
 
@@ -86,8 +93,11 @@ bool build_buckets(Tables& t) {
   // Every threshold must sit at least `margin` inside its bucket (the
   // kernel's fast path compares an approximate quotient, see quantiser).
   const float margin = std::ldexp(1.0f, -19);
-  static const float scales[] = {32.f, 31.f, 33.f, 30.f, 34.f, 29.f, 35.f,
-                                 28.f, 36.f, 27.f, 37.f, 40.f, 44.f, 48.f};
+  // Integer scales put v = 0 on a bucket edge; FP4 has a threshold there,
+  // so half-integer scales follow.
+  static const float scales[] = {32.f, 31.f, 33.f, 30.f, 34.f, 29.f, 35.f, 28.f,
+                                 36.f, 27.f, 37.f, 40.f, 44.f, 48.f, 24.5f, 25.5f,
+                                 26.5f, 27.5f, 28.5f, 29.5f, 30.5f, 31.5f, 36.5f, 48.5f};
   for (float s : scales) {
     int nb = static_cast<int>(2 * s) + 1;
     if (nb > kMaxBuckets) continue;
@@ -116,15 +126,13 @@ bool build_buckets(Tables& t) {
   return false;
 }
 
-Tables g_tables;
-const Tables* g_ptr = nullptr;
+Tables g_tables[2];
+const Tables* g_ptr[2] = {nullptr, nullptr};
 std::once_flag g_once;
 
-void build() {
-  Tables& t = g_tables;
-  // code points, fp64, ascending
+// NF4 code points, fp64, ascending.
+void nf4_points(double q[16]) {
   const double pmax = 929.0 / 960.0;  // 1 - (1/32 + 1/30) / 2, exact ratio
-  double q[16];
   const double top = inv_norm_cdf(pmax);
   for (int j = 1; j <= 7; ++j)  // negative side: probabilities 1/2 + 449 j / 6720
     q[7 - j] = -inv_norm_cdf((3360.0 + 449.0 * j) / 6720.0) / top;
@@ -133,6 +141,19 @@ void build() {
     q[7 + j] = inv_norm_cdf((3840.0 + 449.0 * j) / 7680.0) / top;
   // Both ends evaluate the quantile at exactly P (6503/6720 = 7432/7680 =
   // 929/960), so they come out as exactly -1 and +1; checked below.
+}
+
+// FP4 code points: E2M1 magnitudes / 6, negatives mirrored, 0 twice.
+void fp4_points(double q[16]) {
+  static const double mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+  for (int i = 0; i < 8; ++i) {
+    q[8 + i] = mag[i] / 6.0;
+    q[7 - i] = -mag[i] / 6.0;
+  }
+  q[7] = 0.0;  // +0, not -0
+}
+
+bool build_one(Tables& t, const double q[16], bool twin_zero) {
   for (int i = 0; i < 16; ++i) t.q32[i] = static_cast<float>(q[i]);
   for (int i = 0; i < 15; ++i)
     t.thr[i] = round_down_f32((static_cast<double>(t.q32[i]) + t.q32[i + 1]) * 0.5);
@@ -147,18 +168,27 @@ void build() {
     t.pair_f32[2 * b + 1] = lo;
   }
   bool ok = build_buckets(t);
-  for (int i = 0; i < 15; ++i) ok = ok && t.q32[i] < t.q32[i + 1];
+  for (int i = 0; i < 15; ++i)
+    ok = ok && (t.q32[i] < t.q32[i + 1] || (twin_zero && i == 7 && t.q32[i] == t.q32[i + 1]));
   uint32_t zbits;
   std::memcpy(&zbits, &t.q32[7], 4);
   ok = ok && zbits == 0u && t.q32[0] == -1.0f && t.q32[15] == 1.0f;
-  g_ptr = ok ? &t : nullptr;
+  return ok;
+}
+
+void build() {
+  double q[16];
+  nf4_points(q);
+  if (build_one(g_tables[kQuantNF4], q, false)) g_ptr[kQuantNF4] = &g_tables[kQuantNF4];
+  fp4_points(q);
+  if (build_one(g_tables[kQuantFP4], q, true)) g_ptr[kQuantFP4] = &g_tables[kQuantFP4];
 }
 
 }  // namespace
 
-const Tables* tables() {
+const Tables* tables(int quant_type) {
   std::call_once(g_once, build);
-  return g_ptr;
+  return quant_type == kQuantNF4 || quant_type == kQuantFP4 ? g_ptr[quant_type] : nullptr;
 }
 
 }  // namespace qn

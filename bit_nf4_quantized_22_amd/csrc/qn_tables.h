@@ -17,8 +17,12 @@ struct QuantBucket {
   uint32_t base;  // codes below the bucket
 };
 
+// Code tables of the 4-bit weight: NF4, or FP4 (E2M1 / 6, zero twice).
+constexpr int kQuantNF4 = 0;
+constexpr int kQuantFP4 = 1;
+
 struct Tables {
-  float q32[16];         // NF4 code points, fp32, ascending
+  float q32[16];         // code points, fp32, ascending
   float thr[15];         // largest fp32 <= fp64 mid-point of q32[i], q32[i+1]
   float l8[256];         // level-2 code values fl32(q / 255)
   float thr8[255];       // largest fp32 <= fp64 mid-point of l8[j], l8[j+1]
@@ -29,9 +33,10 @@ struct Tables {
   float pair_f32[512];      // byte -> q32[hi nibble], q32[lo nibble]
 };
 
-// The tables, built on first call.  Returns nullptr only if construction
-// failed its own consistency checks (never expected).
-const Tables* tables();
+// The tables of a code type (kQuantNF4 or kQuantFP4), built on first call.
+// Returns nullptr for an unknown type or if construction failed its own
+// consistency checks (never expected).
+const Tables* tables(int quant_type = kQuantNF4);
 
 // fp64 inverse of the standard normal CDF (exposed for the codebook).
 double inv_norm_cdf(double p);

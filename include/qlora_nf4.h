@@ -66,6 +66,13 @@ extern "C" {
 
 typedef uint16_t qn_bf16; /* bf16 bit pattern */
 
+/* code table of the 4-bit weight (qn_weight.quant_type) */
+#define QN_NF4  0
+#define QN_FP4  1
+/* level-2 code of the block constants (qn_weight.scale_type) */
+#define QN_SCALE_U8   0
+#define QN_SCALE_FP8  1
+
 /*
  * A quantised weight W[N, K] (N = out_features, K = in_features).
  *   packed  uint8[N*K/2]: 4-bit codes of the row-major flattening of W, two
@@ -79,6 +86,12 @@ typedef uint16_t qn_bf16; /* bf16 bit pattern */
  *   blocksize must be 64 and group 256.  The linear ops (and lora_grads)
  *   need N and K to be positive multiples of 64, so a block never crosses a
  *   row; other sizes return QN_ERR_SHAPE.
+ *   quant_type  QN_NF4 (the NF4 table of nf4_codebook) or QN_FP4 (that of
+ *           fp4_codebook); the codes must come from the matching quantiser.
+ *   scale_type  QN_SCALE_U8 (qscale from dq_quantize_scales) or
+ *           QN_SCALE_FP8 (from dq_quantize_scales_fp8); ignored when
+ *           qscale == NULL.  Other values return QN_ERR_UNSUPPORTED.  A
+ *           zero-initialised struct means NF4 with the uint8 code.
  */
 typedef struct qn_weight {
   const uint8_t* packed;
@@ -89,6 +102,8 @@ typedef struct qn_weight {
   int64_t K;
   int32_t blocksize;
   int32_t group;
+  int32_t quant_type;
+  int32_t scale_type;
 } qn_weight;
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -136,6 +151,37 @@ QN_API int nf4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blo
  */
 QN_API int dq_quantize_scales(const float* absmax, int64_t nblocks, int32_t group,
                        uint8_t* qscale, float* gscale, void* stream);
+
+/*
+ * fp4_codebook -- HOST function.  Writes the 16 FP4 code points (ascending,
+ * fp32) to out[16].  [kwkr] §4.1 names fp4 as the alternative 4-bit type
+ * (made for floating-point distributions; worse than NF4 for weights)
+ * without a format: taken as E2M1 (magnitudes 0, 1/2, 1, 3/2, 2, 3, 4, 6)
+ * divided by 6, negatives mirrored, +0 at both out[7] and out[8]; each
+ * value is the fp32 nearest to the exact ratio.  QN_ERR_NULL if out is NULL.
+ */
+QN_API int fp4_codebook(float out[16]);
+
+/*
+ * fp4_quantize -- nf4_quantize with the FP4 table: same arguments, layout,
+ * block constants and errors; code = index of the nearest entry of
+ * fp4_codebook (ties to the lower index, so v <= 0 within the zero bin
+ * takes code 7 and v > 0 code 8, both +0).  Use quant_type = QN_FP4.
+ */
+QN_API int fp4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+                        uint8_t* packed, float* absmax, void* stream);
+
+/*
+ * dq_quantize_scales_fp8 -- dq_quantize_scales with an FP8 level-2 code.
+ * [kwkr] §3.1 compresses the fp32 block constants to fp8: here the ratio
+ * v = fl32(c / c2) in [0, 1] (c2 the group max, stored in gscale as for the
+ * uint8 code) is stored as the nearest E4M3 number (4 exponent bits, bias
+ * 7, 3 mantissa bits, subnormals below 2^-6), ties to the even code; the
+ * dequantised constant is fl32(value * c2).  Same arguments and errors as
+ * dq_quantize_scales; use scale_type = QN_SCALE_FP8.
+ */
+QN_API int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t group,
+                                  uint8_t* qscale, float* gscale, void* stream);
 
 /*
  * nf4_dequant -- materialise the weight.

@@ -197,3 +197,31 @@ def test_dropout_argument_errors(lib):
                None) == qn.QN_ERR_WORKSPACE
     assert bwd(ctypes.byref(w), None, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, FAKE, None, FAKE, ws_b,
                None) == qn.QN_ERR_NULL
+
+
+def test_fp4_codebook_bits_match_the_oracle(lib):
+    from oracle import codebooks
+    out = np.array(qn.fp4_codebook(), dtype=np.float32)
+    assert np.array_equal(out.view(np.uint32), codebooks.fp4_codebook().view(np.uint32))
+
+
+def test_code_type_argument_errors(lib):
+    assert lib.fp4_quantize(FAKE, qn.QN_BF16, 63, 64, FAKE, FAKE, None) == qn.QN_ERR_SHAPE
+    assert lib.fp4_quantize(FAKE, qn.QN_BF16, 64, 32, FAKE, FAKE, None) == qn.QN_ERR_UNSUPPORTED
+    assert lib.fp4_quantize(None, qn.QN_BF16, 64, 64, FAKE, FAKE, None) == qn.QN_ERR_NULL
+    assert lib.fp4_quantize(None, qn.QN_BF16, 0, 64, None, None, None) == qn.QN_OK
+    assert lib.dq_quantize_scales_fp8(FAKE, 10, 128, FAKE, FAKE, None) == qn.QN_ERR_UNSUPPORTED
+    assert lib.dq_quantize_scales_fp8(FAKE, -1, 256, FAKE, FAKE, None) == qn.QN_ERR_SHAPE
+    assert lib.dq_quantize_scales_fp8(FAKE, 10, 256, None, FAKE, None) == qn.QN_ERR_NULL
+    # unknown code types are rejected by every call that takes a weight
+    for qt, st in ((2, 0), (-1, 0), (0, 2), (1, 7)):
+        w = qn.qn_weight(0x100000, 0x100000, 0x100000, None, 128, 128, 64, 256, qt, st)
+        assert lib.nf4_dequant(ctypes.byref(w), qn.QN_BF16, FAKE, None) == qn.QN_ERR_UNSUPPORTED
+        assert lib.qlora_merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, FAKE, None) == \
+            qn.QN_ERR_UNSUPPORTED
+        ws = qn.qn_workspace_bytes(qn.QN_OP_FWD, 32, 128, 128, 8)
+        assert lib.qlora_linear_fwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, FAKE, None,
+                                    FAKE, ws, None) == qn.QN_ERR_UNSUPPORTED
+    # a zero-initialised type pair is NF4 with the uint8 code
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 64, 64, 64, 256)
+    assert (w.quant_type, w.scale_type) == (qn.QN_NF4, qn.QN_SCALE_U8)

@@ -1,0 +1,176 @@
+"""Codebook variants on the GPU against the oracle (oracle/codebooks.py): the
+FP4 weight table and the FP8 (E4M3) level-2 code.
+
+Bars: codes, block constants and level-2 codes bit-exact; dequantised
+weights bit-exact (fp32 and bf16); the linear ops and the merge with such
+weights within the same tolerances as with NF4 (relative Frobenius 1e-2).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import bit_nf4_quantized_22_amd as qn
+from oracle import codebooks, linear, nf4
+from tests.gpu_helpers import (bf16_dev, check, f32_dev, f64, rel_frob, run_layer_checks, synth,
+                               to_bits16, to_np, weight_dev, weight_f32)
+
+pytestmark = pytest.mark.gpu
+
+COMBOS = [("fp4", "u8"), ("fp4", "fp8"), ("fp4", None), ("nf4", "fp8")]
+
+
+def oracle_weight(W32, kind, scale):
+    packed, absmax = codebooks.quantize_4bit(W32, kind)
+    q8 = c2 = None
+    if scale == "u8":
+        q8, c2 = nf4.double_quantize(absmax)
+        scales = nf4.dequant_scales(q8, c2)
+    elif scale == "fp8":
+        q8, c2 = codebooks.double_quantize_fp8(absmax)
+        scales = codebooks.dequant_scales_fp8(q8, c2)
+    else:
+        scales = absmax
+    What = codebooks.dequantize_4bit(packed, scales, W32.size, kind).reshape(W32.shape)
+    return dict(packed=packed, absmax=absmax, q8=q8, c2=c2, What=What)
+
+
+def device_weight(W, dtype, kind, scale):
+    w = weight_dev(W, dtype)
+    N, K = W.shape
+    return qn.quantize_weight(w.reshape(N, K), double_quant=scale is not None, quant_type=kind,
+                              scale_type=scale or "u8")
+
+
+def assert_weight_equal(qw, ref):
+    torch.cuda.synchronize()
+    gp = qw.packed.cpu().numpy().ravel()
+    bad = np.nonzero(gp != ref["packed"].ravel())[0]
+    assert bad.size == 0, f"{bad.size} packed bytes differ, first at {bad[:5]}"
+    if ref["q8"] is not None:
+        gq = qw.qscale.cpu().numpy().ravel()
+        badq = np.nonzero(gq != ref["q8"].ravel())[0]
+        assert badq.size == 0, f"{badq.size} level-2 codes differ, first at {badq[:5]}"
+        assert np.array_equal(qw.gscale.cpu().numpy().view(np.uint32), ref["c2"].view(np.uint32))
+    else:
+        assert np.array_equal(qw.absmax.cpu().numpy().view(np.uint32),
+                              ref["absmax"].view(np.uint32))
+
+
+def _fp4_adversarial(nblocks=256, seed=0):
+    """Blocks whose normalised values sit on and next to every FP4 mid-point,
+    plus exact zeros of both signs."""
+    rng = np.random.default_rng(seed)
+    q = codebooks.fp4_codebook().astype(np.float64)
+    mids = (q[:-1] + q[1:]) / 2
+    out = np.zeros((nblocks, 64), np.float32)
+    for b in range(nblocks):
+        c = np.float32(rng.uniform(0.001, 0.3))
+        blk = np.empty(64, np.float32)
+        for i in range(64):
+            t = np.float32(mids[rng.integers(0, 15)] * float(c))
+            blk[i] = [t, np.nextafter(t, np.float32(-1)), np.nextafter(t, np.float32(1)),
+                      np.float32(0.0), np.float32(-0.0)][rng.integers(0, 5)]
+        blk[rng.integers(0, 64)] = c * (1 if b % 2 else -1)
+        out[b] = blk
+    return out
+
+
+@pytest.mark.parametrize("case", ["tiny_f32", "decode_bf16", "train_11008x4096", "adversarial",
+                                  "ragged"])
+@pytest.mark.parametrize("kind,scale", COMBOS)
+def test_quantised_weight_bit_exact(case, kind, scale):
+    if case == "tiny_f32":
+        W, dtype = synth.tiny_layer(0).W, "f32"
+    elif case == "decode_bf16":
+        W, dtype = synth.decode_layer(1, 4096, 4096, seed=2).W, "bf16"
+    elif case == "train_11008x4096":
+        W, dtype = synth.train_linear(11008, 4096, M=16, seed=3).W, "bf16"
+    elif case == "adversarial":
+        W, dtype = _fp4_adversarial().reshape(128, 128), "f32"
+    else:  # N*K a multiple of 64 but not of the 4096-weight workgroup, odd groups
+        W = synth.bf16_bits(np.random.default_rng(7).standard_normal((64 * 37, 64)).astype(
+            np.float32) * 0.02)
+        dtype = "bf16"
+    qw = device_weight(W, dtype, kind, scale)
+    ref = oracle_weight(weight_f32(W, dtype).reshape(W.shape), kind, scale)
+    assert_weight_equal(qw, ref)
+    for out_dtype in (torch.float32, torch.bfloat16):
+        got = qn.nf4_dequant(qw, out_dtype)
+        torch.cuda.synchronize()
+        if out_dtype == torch.float32:
+            assert np.array_equal(got.cpu().numpy().view(np.uint32), ref["What"].view(np.uint32))
+        else:
+            assert np.array_equal(to_bits16(got), nf4.f32_to_bf16_bits(ref["What"]))
+
+
+def test_fp8_level2_code_crafted_ratios():
+    """Group maxima of 1 make v = c exactly: E4M3 values, their mid-points
+    (ties to the even code), one ulp either side, subnormal ratios, zeros."""
+    vals = codebooks.e4m3_values()
+    vals = vals[vals <= 1.0]
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(0)),
+                          np.nextafter(mids, np.float32(2)), np.float32([0.0, 1e-30, 3e-3, 2e-3])])
+    pts = pts[(pts >= 0) & (pts <= 1)]
+    n = -(-pts.size // 255) * 255
+    c = np.zeros(n, np.float32)
+    c[:pts.size] = pts
+    c = c.reshape(-1, 255)
+    c = np.concatenate([np.ones((c.shape[0], 1), np.float32), c], axis=1).ravel()
+    c = np.concatenate([c, np.zeros(256, np.float32)])  # an all-zero group
+    q, g = qn.dq_quantize_scales(f32_dev(c), fp8=True)
+    torch.cuda.synchronize()
+    rq, rg = codebooks.double_quantize_fp8(c)
+    assert np.array_equal(g.cpu().numpy().view(np.uint32), rg.view(np.uint32))
+    bad = np.nonzero(q.cpu().numpy() != rq)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, e.g. c={c[bad[:4]]}"
+
+
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("fp4", None), ("nf4", "fp8")])
+@pytest.mark.parametrize("M", [1, 16, 40])
+def test_linear_layer_with_codebook(kind, scale, M):
+    wl = synth.tiny_layer(0)
+    if M > wl.M:
+        rng = np.random.default_rng(1000 + M)
+        wl["x"] = synth.bf16_bits(rng.standard_normal((M, wl.K)).astype(np.float32))
+        wl["dy"] = synth.bf16_bits(rng.standard_normal((M, wl.N)).astype(np.float32))
+    qw = device_weight(wl.W, wl.W_dtype, kind, scale)
+    ref = oracle_weight(weight_f32(wl.W, wl.W_dtype).reshape(wl.N, wl.K), kind, scale)
+    run_layer_checks(wl, M=M, qw=qw, ref=ref)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_decode_with_fp4_fp8(M):
+    wl = synth.decode_layer(M, 4096, 11008, seed=2)
+    qw = device_weight(wl.W, "bf16", "fp4", "fp8")
+    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), "fp4", "fp8")
+    y = qn.qlora_linear_fwd(qw, bf16_dev(wl.x), bf16_dev(wl.A), bf16_dev(wl.B), wl.r, wl.alpha)
+    torch.cuda.synchronize()
+    want = linear.linear_forward(f64(wl.x), ref["What"].astype(np.float64), f64(wl.A), f64(wl.B),
+                                 wl.alpha, wl.r)
+    check(f"decode fp4+fp8 M={M}", to_np(y), want)
+
+
+def test_training_shape_with_fp4_fp8():
+    wl = synth.train_linear(4096, 11008, M=2048, seed=3)
+    qw = device_weight(wl.W, "bf16", "fp4", "fp8")
+    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), "fp4", "fp8")
+    rows = np.sort(np.random.default_rng(0).choice(2048, 128, replace=False))
+    run_layer_checks(wl, rows=rows, qw=qw, ref=ref)
+
+
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("nf4", "fp8")])
+def test_merge_with_codebook(kind, scale):
+    wl = synth.decode_layer(1, 1024, 2048, seed=5, r=16, alpha=32.0)
+    qw = device_weight(wl.W, "bf16", kind, scale)
+    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), kind, scale)
+    A, B = bf16_dev(wl.A), bf16_dev(wl.B)
+    merged = qn.qlora_merge(qw, A, B, wl.r, wl.alpha)
+    frozen = qn.qlora_merge(qw, A, torch.zeros_like(B), wl.r, wl.alpha)
+    torch.cuda.synchronize()
+    want = linear.lora_merge(ref["What"].astype(np.float64), f64(wl.A), f64(wl.B), wl.alpha, wl.r)
+    e = rel_frob(synth.bf16_to_f32(to_bits16(merged)), want)
+    assert e <= 4e-3, e
+    # B = 0: the merge is the bf16 dequantised weight bit for bit
+    assert np.array_equal(to_bits16(frozen), nf4.f32_to_bf16_bits(ref["What"]))
