@@ -128,37 +128,50 @@ __device__ __forceinline__ float chunk_scale(const Prefetch& pf, int fp8) {
   return kDQ ? __fmul_rn(l2_value(pf.q8, fp8), pf.c) : pf.c;
 }
 
-// Dequantise one K step of weight codes into the LDS weight tile.  All
-// table lookups are issued first, so the in-order LDS return queue holds
-// only lookups while the arithmetic waits on them.
+// Dequantise one K step of weight codes into the LDS weight tile.  A
+// producer lane's 32 codes all belong to one 64-block, so it first forms
+// that block's 16 products bf16(fl32(Q[c] cs)) (the same rounding as
+// nf4_dequant) and then decodes every code with byte permutes from
+// registers: no code-table reads through LDS, whose bandwidth the MFMA
+// fragment reads and the activation DMAs already use.
 template <bool kBwd>
-__device__ __forceinline__ void store_step(const Prefetch& pf, float cs,
-                                           const float* __restrict__ scode,
+__device__ __forceinline__ void store_step(const Prefetch& pf, float cs, const CodeParams& P,
                                            uint16_t* __restrict__ sB, int t) {
-  // Byte b of a word holds element 2b (high nibble) and 2b+1 (low nibble).
-  // Code c of lane l sits at byte offset 256 c + 4 l of the 64-copy table,
-  // so a wave's 64 lookups hit 64 different banks; the offset is one v_perm
-  // of the code byte and 4 l.
-  const uint32_t lane4 = static_cast<uint32_t>(threadIdx.x & 63) << 2;
-  const char* tab = reinterpret_cast<const char*>(scode);
-  float q[kWords][8];
+  // tl[j] / th[j]: low / high bytes of the products of codes 4 j .. 4 j + 3
+  uint32_t tl[4], th[4];
 #pragma unroll
-  for (int i = 0; i < kWords; ++i) {
-    const uint32_t word = pf.w[i];
-    const uint32_t hi = (word >> 4) & 0x0F0F0F0Fu, lo = word & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint32_t sel = 0x0C0C0400u + (static_cast<uint32_t>(b) << 8);
-      q[i][2 * b] = *reinterpret_cast<const float*>(tab + __builtin_amdgcn_perm(hi, lane4, sel));
-      q[i][2 * b + 1] = *reinterpret_cast<const float*>(tab + __builtin_amdgcn_perm(lo, lane4, sel));
-    }
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t d0 = pack_bf16x2(__fmul_rn(P.q[4 * j], cs), __fmul_rn(P.q[4 * j + 1], cs));
+    const uint32_t d1 = pack_bf16x2(__fmul_rn(P.q[4 * j + 2], cs), __fmul_rn(P.q[4 * j + 3], cs));
+    tl[j] = __builtin_amdgcn_perm(d1, d0, 0x06040200u);
+    th[j] = __builtin_amdgcn_perm(d1, d0, 0x07050301u);
   }
+  // Bytes of c are four codes: look each up in both 8-entry halves (index
+  // c & 7), then keep byte k of the low or the high half by bit 3 of c.
+  auto look = [&](uint32_t c, uint32_t& lo8, uint32_t& hi8) {
+    const uint32_t s7 = c & 0x07070707u;
+    const uint32_t half = ((c >> 1) & 0x04040404u) | 0x03020100u;
+    lo8 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(tl[3], tl[2], s7),
+                                __builtin_amdgcn_perm(tl[1], tl[0], s7), half);
+    hi8 = __builtin_amdgcn_perm(__builtin_amdgcn_perm(th[3], th[2], s7),
+                                __builtin_amdgcn_perm(th[1], th[0], s7), half);
+  };
 #pragma unroll
   for (int i = 0; i < kWords; ++i) {
-    uint32_t d[4];
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      d[b] = pack_bf16x2(__fmul_rn(q[i][2 * b], cs), __fmul_rn(q[i][2 * b + 1], cs));
+    // byte b of a word holds element 2b (high nibble) and 2b+1 (low nibble)
+    const uint32_t word = pf.w[i];
+    uint32_t el, eh, ol, oh;
+    look((word >> 4) & 0x0F0F0F0Fu, el, eh);  // elements 0, 2, 4, 6
+    look(word & 0x0F0F0F0Fu, ol, oh);         // elements 1, 3, 5, 7
+    const uint32_t e0 = __builtin_amdgcn_perm(eh, el, 0x05010400u);  // bf16 pair: elements 0, 2
+    const uint32_t e1 = __builtin_amdgcn_perm(eh, el, 0x07030602u);  // 4, 6
+    const uint32_t o0 = __builtin_amdgcn_perm(oh, ol, 0x05010400u);  // 1, 3
+    const uint32_t o1 = __builtin_amdgcn_perm(oh, ol, 0x07030602u);  // 5, 7
+    uint32_t d[4];  // d[b]: elements 2b, 2b + 1
+    d[0] = __builtin_amdgcn_perm(o0, e0, 0x05040100u);
+    d[1] = __builtin_amdgcn_perm(o0, e0, 0x07060302u);
+    d[2] = __builtin_amdgcn_perm(o1, e1, 0x05040100u);
+    d[3] = __builtin_amdgcn_perm(o1, e1, 0x07060302u);
     if constexpr (kBwd) {
       const int row = t % kBK, qd = t / kBK;
 #pragma unroll
@@ -322,14 +335,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   __shared__ __attribute__((aligned(16))) uint16_t sA1[kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sA2[kBM * kBK];
   __shared__ __attribute__((aligned(16))) uint16_t sB[2][kBN * kLD];
-  __shared__ __attribute__((aligned(16))) float scode[16 * 64];  // q[c] for lane l at [64 c + l]
   __shared__ __attribute__((aligned(16))) uint16_t sLA[kBM * kLoraEarly];
   __shared__ __attribute__((aligned(16))) uint16_t sLW[kBN * kLoraEarly];
   const int t = threadIdx.x;
-  {
-    const CodeRegs R = code_regs(P);
-    for (int i = t; i < 16 * 64; i += blockDim.x) scode[i] = code_value(R, i >> 6);
-  }
 
   const int64_t ncols = kBwd ? g.K : g.N;
   const int64_t L = kBwd ? g.N : g.K;  // contraction length
@@ -414,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     load_step<kBwd, kDQ>(g, c0, nk > 1 ? 1 : nk - 1, p1, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 2 ? 2 : nk - 1, p2, pt);
     store_lora();
-    __syncthreads();  // code table (and the LoRA tiles) visible
-    store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.fp8), scode, sB[0], pt);
+    __syncthreads();  // the LoRA tiles visible
+    store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.fp8), P, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
       const int kl = k + 3 < nk ? k + 3 : nk - 1;
@@ -425,7 +433,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
       asm volatile("" : "+v"(dec.w), "+v"(dec.q8), "+v"(dec.c));
       const float cs = chunk_scale<kDQ>(dec, P.fp8);
       load_step<kBwd, kDQ>(g, c0, kl, ld, pt);
-      store_step<kBwd>(dec, cs, scode, sB[(k & 1) ^ 1], pt);
+      store_step<kBwd>(dec, cs, P, sB[(k & 1) ^ 1], pt);
       __syncthreads();
     };
     int k = 0;
