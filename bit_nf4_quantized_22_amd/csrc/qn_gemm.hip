@@ -173,11 +173,18 @@ __device__ __forceinline__ void store_step(const Prefetch& pf, float cs, const C
     d[2] = __builtin_amdgcn_perm(o1, e1, 0x05040100u);
     d[3] = __builtin_amdgcn_perm(o1, e1, 0x07060302u);
     if constexpr (kBwd) {
-      const int row = t % kBK, qd = t / kBK;
+      // Transposed tile sB[column][row]: lane l holds row l (rows are the
+      // contraction).  Adjacent lanes swap halves (one DPP move) so the even
+      // lane stores rows l, l+1 of column 2b and the odd lane those of
+      // column 2b + 1, as one 4-byte store each.
+      const int lane = t & 63, qd = t / kBK;
+      const uint32_t sel = (lane & 1) ? 0x03020706u : 0x05040100u;
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
-        sB[(kCodes * qd + 8 * i + 2 * b) * kLD + row] = static_cast<uint16_t>(d[b] & 0xFFFF);
-        sB[(kCodes * qd + 8 * i + 2 * b + 1) * kLD + row] = static_cast<uint16_t>(d[b] >> 16);
+        const uint32_t nb = static_cast<uint32_t>(
+            __builtin_amdgcn_mov_dpp(static_cast<int>(d[b]), 0xB1, 0xF, 0xF, false));  // lane l ^ 1
+        *reinterpret_cast<uint32_t*>(sB + (kCodes * qd + 8 * i + 2 * b + (lane & 1)) * kLD +
+                                     (lane & ~1)) = __builtin_amdgcn_perm(nb, d[b], sel);
       }
     } else {
       *reinterpret_cast<u32x4*>(sB + (t / kCodeThreads) * kLD + kCodes * (t % kCodeThreads) + 8 * i) =
