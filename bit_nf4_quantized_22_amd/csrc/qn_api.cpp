@@ -324,7 +324,7 @@ int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t 
   if (r < 0) return QN_ERR_SHAPE;
   if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
   if (!out || (r > 0 && (!A || !B))) return QN_ERR_NULL;
-  if (!aligned(out, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))) return QN_ERR_ALIGN;
+  if (!aligned(out, 16) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))) return QN_ERR_ALIGN;
   if (!qn::tables()) return QN_ERR_UNSUPPORTED;
   (void)hipGetLastError();
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;

@@ -1,20 +1,23 @@
-// LoRA merge (gfx950): out[n, k] = bf16(fl32(q[code] c') + fl32(s * sum_j B[n, j] A[j, k])),
-// s = alpha / r, the sum an fp32 fma chain over j = 0 .. r - 1.
+// LoRA merge (gfx950): out[n, k] = bf16(fl32(q[code] c') + fl32(s * (B A)[n, k])),
+// s = alpha / r, the rank-r product accumulated in fp32 by MFMA.
 //
 // [rkmt "QLORA技术解析" §2.1] for inference the adapter is folded into the
 // weight, W <- W + B A, so it costs no latency; [tgd "QLoRA微调" §7] a QLoRA
 // adapter is merged into a 16-bit weight, never into the 4-bit form.  The
-// weight here is the dequantised NF4 weight (the value the adapter was
+// weight here is the dequantised 4-bit weight (the value the adapter was
 // trained against), expanded on the fly: the merged bf16 weight is the only
 // 16-bit copy that is written.  Re-quantising it (nf4_quantize) gives a
 // merged 4-bit model.
 //
 // HBM-bound streaming kernel: per weight it reads half a byte of codes and
-// writes two bytes.  A workgroup of 256 threads owns 256 consecutive columns
-// and kRowsPerWG rows; each thread keeps the r values of A's column in
-// registers for all its rows, the workgroup's rows of B sit in LDS as fp32
-// (one broadcast read per value), and the loads of kRowBatch rows are
-// issued together, so the rank-r update costs r fp32 FMAs per weight.
+// writes two bytes.  The rank-r product runs on the 16x16x32 bf16 MFMA as
+// the transposed product (B A)^T = A^T B^T, so a lane's four outputs per
+// MFMA are four k of one row n; the k order inside each 64-block is
+// permuted so that over the block's four MFMAs a lane owns 16 consecutive
+// k.  A lane then reads 8 bytes of codes and one block constant and writes
+// 32 bytes per block, and a wave's rows are 32-byte code reads and 128-byte
+// stores.  A workgroup (4 waves) owns 64 rows x 256 columns; A's columns
+// for them are staged transposed in LDS, B's rows sit in registers.
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -23,98 +26,130 @@ namespace qn {
 
 namespace {
 
-constexpr int kRowsPerWG = 32;
-constexpr int kRowBatch = 8;  // rows whose loads are issued together
+constexpr int kMRows = 64;    // rows of W per workgroup (16 per wave)
+constexpr int kMCols = 256;   // columns of W per workgroup (4 blocks)
 
+__device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// kR: rank capacity (0, 32, 64 or 128); kD = kR / 32 MFMAs per 16 x 16 tile.
 template <int kR, bool kDQ>
 __global__ __launch_bounds__(256) void merge_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
     const float* __restrict__ gscale, const float* __restrict__ absmax, int64_t N, int64_t K,
     const uint16_t* __restrict__ A, const uint16_t* __restrict__ B, int r, float s,
     uint16_t* __restrict__ out, CodeParams P) {
-  // A's column in registers: fp32 for r <= 64, bf16 pairs above (register budget)
-  constexpr bool kPacked = kR > 64;
-  constexpr int kAR = kR == 0 ? 1 : (kPacked ? kR / 2 : kR);
-  __shared__ float scode[16];
-  __shared__ __attribute__((aligned(16))) float sB[kRowsPerWG][kR == 0 ? 4 : kR];  // B rows, fp32
-  const int tid = threadIdx.x;
+  constexpr int kD = kR / 32;
+  constexpr int kRS = kR + 8;  // bf16 per row of the transposed A tile (16-byte pad)
+  __shared__ float scode[16 * 64];  // q[c] for lane l at [64 c + l]: no bank conflicts
+  __shared__ __attribute__((aligned(16))) uint16_t sat[kR > 0 ? kMCols * kRS : 8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kMRows;
+  const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kMCols;
+  const int64_t n = n0 + 16 * wave + nl;  // N % 64 == 0: always a valid row
   {
     const CodeRegs R = code_regs(P);
-    const float qv = code_value(R, tid & 15);
-    if (tid < 16) scode[tid] = qv;
+    for (int i = tid; i < 16 * 64; i += 256) scode[i] = code_value(R, i >> 6);
   }
-  const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kRowsPerWG;
+  // B row n, columns 32 d + 8 g .. + 7 (zero past r), as MFMA operands
+  uint4 bfrag[kD > 0 ? kD : 1];
   if constexpr (kR > 0) {
-    // the workgroup's rows of B (rows past N and columns past r: zero)
-    for (int i = tid; i < kRowsPerWG * kR; i += 256) {
-      const int rr = i / kR, j = i % kR;
-      const int64_t n = n0 + rr;
-      const bool ok = n < N && j < r;
-      const float v = bf16_to_f32(B[(n < N ? n : N - 1) * r + (j < r ? j : r - 1)]);
-      sB[rr][j] = ok ? v : 0.f;
+    // A tile transposed: sat[kk][j] = A[j][k0 + kk], zero for j >= r or
+    // columns past K.  Thread tid handles column kk = tid of every row j;
+    // all loads are unconditional from clamped addresses (a branch around a
+    // load would wait for it at the join), the zeros selected afterwards.
+    {
+      const int kk = tid;
+      const int64_t kc = k0 + kk < K ? k0 + kk : K - 1;
+      const bool kin = k0 + kk < K;
+      uint32_t av[kR];
+#pragma unroll
+      for (int j = 0; j < kR; ++j) av[j] = A[static_cast<int64_t>(j < r ? j : r - 1) * K + kc];
+#pragma unroll
+      for (int j = 0; j < kR; ++j)
+        sat[kk * kRS + j] = (kin && j < r) ? static_cast<uint16_t>(av[j]) : uint16_t{0};
+    }
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      uint32_t bv[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const int j = 32 * d + 8 * g + h;
+        bv[h] = B[n * r + (j < r ? j : r - 1)];
+      }
+      uint32_t w4[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const int j = 32 * d + 8 * g + 2 * h;
+        w4[h] = (j < r ? bv[2 * h] : 0u) | ((j + 1 < r ? bv[2 * h + 1] : 0u) << 16);
+      }
+      bfrag[d] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
     }
   }
   __syncthreads();
-  const int64_t k = static_cast<int64_t>(blockIdx.x) * 256 + tid;
-  const bool kvalid = k < K;
-  const int64_t kc = kvalid ? k : K - 1;  // columns past K read column K - 1, store nothing
-  // A[:, k] for j < r, zero beyond r (loads clamped to row r - 1, so every
-  // load is unconditional and in bounds; kR == 0 is the frozen weight)
-  uint32_t a[kAR];
+
+  // Loads of all four blocks first (blocks past K re-read the last block
+  // and store nothing), then the arithmetic.
+  constexpr int kBlk = kMCols / 64;
+  uint2 cw[kBlk];
+  uint32_t q8[kBlk];
+  float c2[kBlk];
 #pragma unroll
-  for (int i = 0; i < kAR; ++i) {
-    if constexpr (kR == 0) {
-      a[i] = 0;
-    } else if constexpr (kPacked) {
-      const int j0 = 2 * i, j1 = 2 * i + 1;
-      const uint32_t v0 = A[static_cast<int64_t>(j0 < r ? j0 : r - 1) * K + kc];
-      const uint32_t v1 = A[static_cast<int64_t>(j1 < r ? j1 : r - 1) * K + kc];
-      a[i] = (j0 < r ? v0 : 0u) | ((j1 < r ? v1 : 0u) << 16);
+  for (int blk = 0; blk < kBlk; ++blk) {
+    const int64_t kb = k0 + 64 * blk < K ? k0 + 64 * blk : K - 64;
+    const int64_t bi = n * (K >> 6) + (kb >> 6);
+    // codes of k = kb + 16 g .. + 15 (8 bytes; byte i: k 2i high nibble, 2i + 1 low)
+    cw[blk] = *reinterpret_cast<const uint2*>(packed + (n * K + kb + 16 * g) / 2);
+    if constexpr (kDQ) {
+      q8[blk] = qscale[bi];
+      c2[blk] = gscale[bi >> 8];
     } else {
-      const uint32_t v = A[static_cast<int64_t>(i < r ? i : r - 1) * K + kc];
-      a[i] = i < r ? (v << 16) : 0u;  // fp32 bit pattern of the bf16 value
+      q8[blk] = 0;
+      c2[blk] = absmax[bi];
     }
   }
-  const int shift = (kc & 1) ? 0 : 4;  // even column: high nibble
-  const int64_t nlast = (n0 + kRowsPerWG < N ? n0 + kRowsPerWG : N) - 1;
-  for (int rb = 0; rb < kRowsPerWG; rb += kRowBatch) {
-    // all loads of the batch first (rows past N re-read the last row)
-    uint32_t byte[kRowBatch], q8[kRowBatch];
-    float c2[kRowBatch];
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+  const char* tab = reinterpret_cast<const char*>(scode);
 #pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t n = n0 + rb + i < nlast ? n0 + rb + i : nlast;
-      const int64_t bi = n * (K >> 6) + (kc >> 6);
-      byte[i] = packed[n * (K >> 1) + (kc >> 1)];
-      if constexpr (kDQ) {
-        q8[i] = qscale[bi];
-        c2[i] = gscale[bi >> 8];
-      } else {
-        q8[i] = 0;
-        c2[i] = absmax[bi];
+  for (int blk = 0; blk < kBlk; ++blk) {
+    const int64_t kb = k0 + 64 * blk;  // first column of the block
+    const float cs = kDQ ? __fmul_rn(l2_value(q8[blk], P.fp8), c2[blk]) : c2[blk];
+    f32x4_t t[4];
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      t[b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if constexpr (kR > 0) {
+        // MFMA b: output row i is column kb + 16 (i / 4) + 4 b + i % 4, so
+        // lane (nl, g) gets k = kb + 16 g + 4 b + [0, 4)
+        const int krow = 64 * blk + 16 * (nl >> 2) + 4 * b + (nl & 3);
+#pragma unroll
+        for (int d = 0; d < kD; ++d) {
+          const uint4 af = *reinterpret_cast<const uint4*>(sat + krow * kRS + 32 * d + 8 * g);
+          t[b] = mfma16(af, bfrag[d], t[b]);
+        }
       }
     }
+    const uint32_t words[2] = {cw[blk].x, cw[blk].y};
+    uint32_t o[8];
 #pragma unroll
-    for (int i = 0; i < kRowBatch; ++i) {
-      const int64_t n = n0 + rb + i;
-      const float cs = kDQ ? __fmul_rn(l2_value(q8[i], P.fp8), c2[i]) : c2[i];
-      const float w = __fmul_rn(scode[(byte[i] >> shift) & 15], cs);
-      float merged = w;
+    for (int e = 0; e < 16; e += 2) {
+      const uint32_t byte = (words[e >> 3] >> (8 * ((e & 7) >> 1))) & 0xFFu;
+      const float q0 = *reinterpret_cast<const float*>(tab + (((byte >> 4) << 8) | lane4));
+      const float q1 = *reinterpret_cast<const float*>(tab + (((byte & 15u) << 8) | lane4));
+      float m0 = __fmul_rn(q0, cs), m1 = __fmul_rn(q1, cs);
       if constexpr (kR > 0) {
-        const float* brow = sB[rb + i];
-        float t = 0.f;
-#pragma unroll
-        for (int j = 0; j < kR; ++j) {
-          float aj;
-          if constexpr (kPacked)
-            aj = __uint_as_float((j & 1) ? (a[j >> 1] & 0xFFFF0000u) : (a[j >> 1] << 16));
-          else
-            aj = __uint_as_float(a[j]);
-          t = __fmaf_rn(brow[j], aj, t);
-        }
-        merged = __fadd_rn(w, __fmul_rn(s, t));
+        m0 = __fadd_rn(m0, __fmul_rn(s, t[e >> 2][e & 3]));
+        m1 = __fadd_rn(m1, __fmul_rn(s, t[(e + 1) >> 2][(e + 1) & 3]));
       }
-      if (kvalid && n <= nlast) out[n * K + k] = static_cast<uint16_t>(pack_bf16x2(merged, 0.f) & 0xFFFF);
+      o[e >> 1] = pack_bf16x2(m0, m1);
+    }
+    if (kb < K) {  // uniform: whole blocks only (K % 64 == 0)
+      uint4* dst = reinterpret_cast<uint4*>(out + n * K + kb + 16 * g);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
     }
   }
 }
@@ -122,8 +157,8 @@ __global__ __launch_bounds__(256) void merge_kernel(
 template <int kR>
 void merge_launch(const WeightView& w, const uint16_t* A, const uint16_t* B, int r, float s,
                   uint16_t* out, const CodeParams& P, hipStream_t st) {
-  const dim3 grid(static_cast<uint32_t>((w.K + 255) / 256),
-                  static_cast<uint32_t>((w.N + kRowsPerWG - 1) / kRowsPerWG));
+  const dim3 grid(static_cast<uint32_t>((w.K + kMCols - 1) / kMCols),
+                  static_cast<uint32_t>(w.N / kMRows));
   if (w.qscale)
     hipLaunchKernelGGL((merge_kernel<kR, true>), grid, dim3(256), 0, st, w.packed, w.qscale,
                        w.gscale, w.absmax, w.N, w.K, A, B, r, s, out, P);
@@ -139,7 +174,6 @@ hipError_t launch_merge(const WeightView& w, const uint16_t* A, const uint16_t* 
   if (w.N == 0 || w.K == 0) return hipSuccess;
   const CodeParams P = code_params(w);
   if (r == 0) merge_launch<0>(w, A, B, r, s, out, P, st);  // frozen weight: A, B unused
-  else if (r <= 16) merge_launch<16>(w, A, B, r, s, out, P, st);
   else if (r <= 32) merge_launch<32>(w, A, B, r, s, out, P, st);
   else if (r <= 64) merge_launch<64>(w, A, B, r, s, out, P, st);
   else merge_launch<128>(w, A, B, r, s, out, P, st);

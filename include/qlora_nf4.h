@@ -240,9 +240,10 @@ QN_API int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M,
  * dequantised NF4 weight the adapter was trained against; re-quantise the
  * result with nf4_quantize for a merged 4-bit model.
  *   A bf16[r, K], B bf16[N, r] (device; ignored when r == 0).
- *   out device bf16[N, K], overwritten.  Per element: the rank-r product is
- *   an fp32 fma chain over j = 0 .. r-1, scaled by alpha/r in fp32, added
- *   to the fp32 dequantised weight, then rounded to bf16 (nearest even).
+ *   out device bf16[N, K], 16-byte aligned, overwritten.  Per element: the
+ *   rank-r product of the bf16 operands accumulated in fp32 (MFMA), scaled
+ *   by alpha/r in fp32, added to the fp32 dequantised weight, then rounded
+ *   to bf16 (nearest even); r == 0 writes bf16(dequant(W)) exactly.
  *   r must be 0..128.  N and K must be positive multiples of 64.
  */
 QN_API int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t r,

@@ -2,12 +2,12 @@
 
 The merged weight bf16(dequant(W) + (alpha/r) B A) is compared element by
 element with the oracle's fp64 value rounded straight to bf16.  The kernel
-forms the rank-r product in fp32 (an fma chain over j), so an element whose
-exact value lies within fp32 rounding of a bf16 rounding boundary may land
-one bf16 step away, and where the update nearly cancels the weight the
-fp32 error of the chain can span several steps of the small result.  The
-bar: every element within one bf16 step plus twice the fp32 error bound
-r 2^-24 (alpha/r) |B||A| of the chain, at most one step wherever that bound
+accumulates the rank-r product in fp32 (MFMA), so an element whose exact
+value lies within fp32 rounding of a bf16 rounding boundary may land one
+bf16 step away, and where the update nearly cancels the weight the fp32
+error of the sum can span several steps of the small result.  The bar:
+every element within one bf16 step plus twice the fp32 error bound
+r 2^-24 (alpha/r) |B||A| of an r-term fp32 sum, at most one step wherever that bound
 is under a quarter step, and at least 99.9% of the elements identical.  With B = 0 or r = 0 the merge is
 nf4_dequant's bf16 output, bit for bit.  Re-quantising the merged weight on
 the device matches the oracle's quantisation of the same bf16 values.
@@ -36,9 +36,9 @@ def _spacing(v):
 
 
 def _check_merge(got_bits, want_bits, name, acc_err, min_exact=0.999):
-    """acc_err = r 2^-24 (alpha/r) |B| |A| elementwise bounds how far the
-    fp32 fma chain over r terms can be from the exact product; that can be
-    many bf16 steps of a result that nearly cancels the weight."""
+    """acc_err = r 2^-24 (alpha/r) |B| |A| elementwise bounds how far an
+    r-term fp32 sum can be from the exact product; that can be many bf16
+    steps of a result that nearly cancels the weight."""
     steps = np.abs(_ordered(got_bits) - _ordered(want_bits))
     exact = float(np.mean(steps == 0))
     got = nf4.bf16_bits_to_f32(got_bits).astype(np.float64)
@@ -90,6 +90,15 @@ def test_merge_training_weights_r64(shape):
     rows = np.sort(np.random.default_rng(1).choice(shape[0], 512, replace=False))
     _, _, _, got, want, mag = _merge_case(wl, rows=rows)
     _check_merge(got, want, f"{shape} r=64 sampled rows", mag)
+
+
+@pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33)])
+def test_merge_ragged_columns_and_ranks(N, K, r):
+    """K not a multiple of the 256-column workgroup tile, ranks that pad the
+    32-deep MFMA steps (5, 33, 100)."""
+    wl = synth.train_linear(N, K, M=16, seed=N + K + r, r=r, alpha=2.0 * r)
+    _, _, _, got, want, mag = _merge_case(wl)
+    _check_merge(got, want, f"{N}x{K} r={r}", mag, min_exact=0.99)
 
 
 def test_merge_with_b_zero_is_the_bf16_dequant():
