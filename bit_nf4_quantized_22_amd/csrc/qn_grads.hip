@@ -8,10 +8,12 @@
 // matrix (x [M, K] or dy [M, N]) and P the narrow one (t or u, [M, r], fp32
 // or bf16): a contraction along M, the slow dimension of both row-major
 // inputs.  MFMA 16x16x32 needs each lane to hold 8 consecutive tokens of
-// one column, so every 32-token step of X is loaded with coalesced 16-byte
+// one column, so every 64-token step of X is loaded with coalesced 16-byte
 // loads and written *transposed* into LDS as bf16 pairs (column-major
-// [column][token], row pitch 40 halves so the operand reads are
-// conflict-free); P is staged the same way.  Workgroups own 256 columns and
+// [column][token], row pitch 72 halves so the operand reads are
+// conflict-free); P is staged the same way.  The next step's loads are in
+// flight during a step's MFMAs: 32 KB per workgroup, since with about one
+// workgroup per CU the bytes in flight set the streaming rate.  Workgroups own 256 columns and
 // a token chunk, write fp32 partial sums [chunk][r][C], and a second pass
 // sums the chunks in a fixed order and applies s (bit-reproducible).  The
 // wide matrix is read once; the partials are a small fraction of it.
@@ -24,8 +26,9 @@ namespace qn {
 namespace {
 
 constexpr int kCols = 256;    // columns of X per workgroup (4 waves x 64)
-constexpr int kStep = 32;     // tokens per MFMA step
-constexpr int kPitch = 40;    // LDS row pitch of the transposed tiles, in bf16
+constexpr int kStep = 64;     // tokens per step (two 32-deep MFMA steps)
+constexpr int kQ = kStep / 16;  // 16-token row groups per step
+constexpr int kPitch = kStep + 8;  // LDS row pitch of the transposed tiles, in bf16
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -42,8 +45,8 @@ __device__ __forceinline__ float ld_narrow<uint16_t>(const uint16_t* p, int64_t 
 }
 
 // RT: rank tile (r <= RT, a multiple of 16).  Grid: (ceil(C / 256), chunks).
-// Thread t loads, per step, rows 2 (t % 8) + {0, 1} + 16 q (q = 0, 1) of
-// columns 8 (t / 8) .. + 7: four 16-byte loads, 8 rows x 128 bytes per wave
+// Thread t loads, per step, rows 2 (t % 8) + {0, 1} + 16 q (q < kQ) of
+// columns 8 (t / 8) .. + 7: 2 kQ 16-byte loads, 8 rows x 128 bytes per wave
 // instruction.  Each pair of rows is packed per column into one 32-bit word
 // and stored at [column][row pair] of the transposed tile.
 template <int RT, typename T>
@@ -66,9 +69,9 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
   const int lrp = tid & 7;          // row pair within 16 rows
   const int64_t lcol = c0 + 8 * lcg;
   const int64_t lcolc = lcol + 8 <= C ? lcol : C - 8;  // C % 64 == 0: a valid 8-column group
-  auto load_x = [&](int s, uint4 (&v)[4]) {
+  auto load_x = [&](int s, uint4 (&v)[2 * kQ]) {
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+    for (int q = 0; q < kQ; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         int64_t m = m_lo + static_cast<int64_t>(s) * kStep + 16 * q + 2 * lrp + h;
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 xv[4];
+  uint4 xv[2 * kQ];
   float pv[kPer];
   load_x(0, xv);
   load_p(0, pv);
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
     __syncthreads();  // the previous step's operand reads are done
     // transposed stores: word (row pair lrp + 8 q) of column 8 lcg + e
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < kQ; ++q) {
       const uint32_t a0[4] = {xv[2 * q].x, xv[2 * q].y, xv[2 * q].z, xv[2 * q].w};
       const uint32_t a1[4] = {xv[2 * q + 1].x, xv[2 * q + 1].y, xv[2 * q + 1].z, xv[2 * q + 1].w};
 #pragma unroll
@@ -128,15 +131,19 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
       load_x(sn, xv);
       load_p(sn, pv);
     }
-    uint4 pa[RT / 16];
 #pragma unroll
-    for (int a = 0; a < RT / 16; ++a)
-      pa[a] = *reinterpret_cast<const uint4*>(&sP[(16 * a + l16) * kPitch + 8 * g]);
+    for (int kk = 0; kk < kStep / 32; ++kk) {
+      uint4 pa[RT / 16];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-      const uint4 xb = *reinterpret_cast<const uint4*>(&sX[(wave * 64 + 16 * b + l16) * kPitch + 8 * g]);
+      for (int a = 0; a < RT / 16; ++a)
+        pa[a] = *reinterpret_cast<const uint4*>(&sP[(16 * a + l16) * kPitch + 32 * kk + 8 * g]);
 #pragma unroll
-      for (int a = 0; a < RT / 16; ++a) acc[a][b] = mfma16(pa[a], xb, acc[a][b]);
+      for (int b = 0; b < 4; ++b) {
+        const uint4 xb = *reinterpret_cast<const uint4*>(
+            &sX[(wave * 64 + 16 * b + l16) * kPitch + 32 * kk + 8 * g]);
+#pragma unroll
+        for (int a = 0; a < RT / 16; ++a) acc[a][b] = mfma16(pa[a], xb, acc[a][b]);
+      }
     }
   }
 
