@@ -171,8 +171,21 @@ __global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restri
   const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (idx >= static_cast<int64_t>(r) * C) return;
   const int64_t j = idx / C, col = idx % C;
+  // 16 loads in flight per batch (clamped to the last chunk, not added),
+  // then the additions in chunk order
+  constexpr int kBatch = 16;
   float v = 0.f;
-  for (int c = 0; c < nchunk; ++c) v += part[(c * r + j) * C + col];
+  for (int c0 = 0; c0 < nchunk; c0 += kBatch) {
+    float pv[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int c = c0 + i < nchunk ? c0 + i : nchunk - 1;
+      pv[i] = part[(static_cast<int64_t>(c) * r + j) * C + col];
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (c0 + i < nchunk) v += pv[i];
+  }
   v *= s;
   if (transposed) out[col * r + j] = v;
   else out[j * C + col] = v;
