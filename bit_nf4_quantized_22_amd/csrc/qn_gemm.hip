@@ -24,14 +24,15 @@
 //     other of two weight buffers.
 // One barrier per K step.  The 256-row tile halves the dequantisation per
 // flop against 128 rows, and moving the activation copy to DMA leaves the
-// producer waves only the dequantisation: they, not the MFMAs, set the
-// pace.  All global loads are unconditional (edge rows re-read a valid
-// row), which keeps the compiler from serialising them behind branches.
-// The dequantisation looks each 4-bit code up in a 64-copy fp32 table in
-// LDS (lane l reads copy l, so a wave never has a bank conflict), multiplies
-// by the block constant and packs to bf16.  The forward stages the weight
-// tile row-major ([n][k]); the backward needs 8 consecutive n per MFMA
-// lane, so it writes the dequantised tile transposed ([k][n]).
+// producer waves only the dequantisation.  All global loads are
+// unconditional (edge rows re-read a valid row), which keeps the compiler
+// from serialising them behind branches.  A producer lane's 32 codes per
+// step lie in one 64-block: it forms the block's 16 products
+// bf16(fl32(q[c] c')) and decodes its codes with byte permutes from
+// registers, so the LDS carries only the activation DMA, the weight tile
+// and the MFMA fragment reads.  The forward stages the weight tile
+// row-major ([n][k]); the backward needs 8 consecutive n per MFMA lane, so
+// it writes the dequantised tile transposed ([k][n]), as pairs of rows.
 
 #include "qn_device.h"
 #include "qn_launch.h"
