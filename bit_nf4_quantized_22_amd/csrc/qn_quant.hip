@@ -200,7 +200,8 @@ __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restric
   }
 }
 
-// Each lane expands 32 codes (16 packed bytes, half a block, one constant).
+// Each thread expands 32 codes: four runs of 8 (4 packed bytes, one block
+// constant each), 2048 codes apart.
 template <bool kOutBf16>
 __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const uint8_t* __restrict__ packed, const uint8_t* __restrict__ qscale,
@@ -209,33 +210,43 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
   __shared__ float2 spair[256];
   fill_pair_f32(spair, P, 1);
   __syncthreads();
-  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 32;
-  if (e0 >= numel) return;
-  const float cs = block_scale(qscale, gscale, absmax, e0 >> 6, P.fp8);
-  const uint4 pk = *reinterpret_cast<const uint4*>(packed + e0 / 2);
-  const uint32_t words[4] = {pk.x, pk.y, pk.z, pk.w};
-  float v[32];
+  // Run i of thread t: codes wbase + 2048 i .. + 7, so every load and
+  // store instruction of a wave covers one contiguous range (256 bytes of
+  // codes, 1 KB of bf16 or 2 KB of fp32).  Lane-strided 16-byte stores (a
+  // lane's 32 codes contiguous) streamed at 3.5 TB/s; this order at 5.7.
+  // Runs past numel (a multiple of 32) re-read the last run and store
+  // nothing.
+  const int64_t wbase = static_cast<int64_t>(blockIdx.x) * 8192 + threadIdx.x * 8;
+  int64_t e[4];
+  uint32_t words[4];
+  float cs[4];
 #pragma unroll
-  for (int wi = 0; wi < 4; ++wi) {
+  for (int i = 0; i < 4; ++i) {
+    const int64_t ei = wbase + i * 2048;
+    e[i] = ei < numel ? ei : numel - 8;
+    words[i] = *reinterpret_cast<const uint32_t*>(packed + e[i] / 2);
+    cs[i] = block_scale(qscale, gscale, absmax, e[i] >> 6, P.fp8);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[8];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float2 pr = spair[(words[wi] >> (8 * b)) & 0xFF];
-      v[8 * wi + 2 * b] = __fmul_rn(pr.x, cs);
-      v[8 * wi + 2 * b + 1] = __fmul_rn(pr.y, cs);
+      const float2 pr = spair[(words[i] >> (8 * b)) & 0xFF];
+      v[2 * b] = __fmul_rn(pr.x, cs[i]);
+      v[2 * b + 1] = __fmul_rn(pr.y, cs[i]);
     }
-  }
-  if constexpr (kOutBf16) {
-    uint4* dst = reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      dst[i] = make_uint4(pack_bf16x2(v[8 * i], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                          pack_bf16x2(v[8 * i + 4], v[8 * i + 5]),
-                          pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
-  } else {
-    float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + e0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      dst[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
+    if (wbase + i * 2048 < numel) {
+      if constexpr (kOutBf16) {
+        *reinterpret_cast<uint4*>(static_cast<uint16_t*>(out) + e[i]) =
+            make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                       pack_bf16x2(v[6], v[7]));
+      } else {
+        float4* dst = reinterpret_cast<float4*>(static_cast<float*>(out) + e[i]);
+        dst[0] = make_float4(v[0], v[1], v[2], v[3]);
+        dst[1] = make_float4(v[4], v[5], v[6], v[7]);
+      }
+    }
   }
 }
 
