@@ -88,11 +88,12 @@ size_t bwd_ws(int64_t M, int64_t N, int32_t r) {
          bt_bytes(N, r);
 }
 
-// Gradient workspace: fp32 u, fp32 t, B^T, split-M partial sums.
+// Gradient workspace: bf16 u and t (recomputed when not given), B^T, the
+// partial sums of those projections, then the split-M partial sums.
 size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (r == 0) return 0;
-  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
-  return 2 * round_up(mr * 4, 256) + bt_bytes(N, r) +
+  return 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r) +
+         lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) +
          round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
 }
 
@@ -368,24 +369,32 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const float scale = alpha / static_cast<float>(r);
-  const size_t mr = static_cast<size_t>(M) * static_cast<size_t>(r);
+  // u and t, when not given, are recomputed as bf16 by the launches the
+  // forward and the backward use for u_out and t_out (same splits, same
+  // fixed-order sums), so they equal the saved ones bit for bit for M > 16
+  // (t at every M)
   char* base = static_cast<char*>(ws);
-  float* u32 = reinterpret_cast<float*>(base);
-  float* t32 = reinterpret_cast<float*>(base + round_up(mr * 4, 256));
-  uint16_t* bt = reinterpret_cast<uint16_t*>(base + 2 * round_up(mr * 4, 256));
-  void* part = base + 2 * round_up(mr * 4, 256) + bt_bytes(N, r);
+  const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
+  uint16_t* u16 = reinterpret_cast<uint16_t*>(base);
+  uint16_t* t16 = reinterpret_cast<uint16_t*>(base + lora_bf16_bytes(M, r));
+  uint16_t* bt = reinterpret_cast<uint16_t*>(base + 2 * lora_bf16_bytes(M, r));
+  float* lpart = reinterpret_cast<float*>(base + 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r));
+  void* part = base + 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r) + lora_part_bytes(mp, r);
   if (M > 0 && !u) {
-    if (qn::launch_skinny(x, M, K, A, r, 1.0f, u32, nullptr, nullptr, 1, s) != hipSuccess)
+    const int ks = qn::skinny_wide_splits(mp, K);
+    if (qn::launch_skinny(x, M, K, A, r, 1.0f, lpart, nullptr, nullptr, ks, s) != hipSuccess ||
+        qn::launch_lora_reduce(lpart, ks, M * r, 1.0f, u16, nullptr, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   if (M > 0 && !t) {
-    if (qn::launch_transpose(B, N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
-    if (qn::launch_skinny(dy, M, N, bt, r, 1.0f, t32, nullptr, nullptr, 1, s) != hipSuccess)
+    const int ks = qn::skinny_wide_splits(mp, N);
+    if (qn::launch_transpose(B, N, r, bt, s) != hipSuccess ||
+        qn::launch_skinny(dy, M, N, bt, r, 1.0f, lpart, nullptr, nullptr, ks, s) != hipSuccess ||
+        qn::launch_lora_reduce(lpart, ks, M * r, 1.0f, t16, nullptr, s) != hipSuccess)
       return QN_ERR_HIP;
   }
-  return hip_status(qn::launch_grads_impl(x, dy, u ? static_cast<const void*>(u) : u32, u != nullptr,
-                                          t ? static_cast<const void*>(t) : t32, t != nullptr, M,
-                                          N, K, r, scale, dA, dB, part, s));
+  return hip_status(qn::launch_grads_impl(x, dy, u ? u : u16, t ? t : t16, M, N, K, r, scale, dA,
+                                          dB, part, s));
 }
 
 }  // extern "C"

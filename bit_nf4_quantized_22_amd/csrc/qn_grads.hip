@@ -5,18 +5,19 @@
 // produces besides dx.
 //
 // Both are out[r, C] = P^T X summed over the M tokens, with X the wide bf16
-// matrix (x [M, K] or dy [M, N]) and P the narrow one (t or u, [M, r], fp32
-// or bf16): a contraction along M, the slow dimension of both row-major
+// matrix (x [M, K] or dy [M, N]) and P the narrow one (t or u, [M, r],
+// bf16): a contraction along M, the slow dimension of both row-major
 // inputs.  MFMA 16x16x32 needs each lane to hold 8 consecutive tokens of
 // one column, so every 64-token step of X is loaded with coalesced 16-byte
 // loads and written *transposed* into LDS as bf16 pairs (column-major
 // [column][token], row pitch 72 halves so the operand reads are
-// conflict-free); P is staged the same way.  The next step's loads are in
-// flight during a step's MFMAs: 32 KB per workgroup, since with about one
-// workgroup per CU the bytes in flight set the streaming rate.  Workgroups own 256 columns and
-// a token chunk, write fp32 partial sums [chunk][r][C], and a second pass
-// sums the chunks in a fixed order and applies s (bit-reproducible).  The
-// wide matrix is read once; the partials are a small fraction of it.
+// conflict-free); P is staged the same way.  Loads run two steps ahead
+// (64 KB in flight per workgroup): with one or two workgroups per CU the
+// bytes in flight set the streaming rate.  Workgroups own 256 columns and a
+// token chunk, write fp32 partial sums [chunk][r][C], and a second pass
+// sums the chunks in a fixed order and applies s (bit-reproducible).  Both
+// products share each of the two launches.  The wide matrices are read
+// once; the partials are a small fraction of them.
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -35,32 +36,49 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
-template <typename T>
-__device__ __forceinline__ float ld_narrow(const T* p, int64_t i);
-template <>
-__device__ __forceinline__ float ld_narrow<float>(const float* p, int64_t i) { return p[i]; }
-template <>
-__device__ __forceinline__ float ld_narrow<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_to_f32(p[i]);
-}
+// One of the two products: X [M, C] bf16 (x or dy), P [M, r] bf16 (t or
+// u), partial sums part[chunk][r][C] over token chunks of `chunk` rows.
+struct GradJob {
+  const uint16_t* X;
+  const uint16_t* P;
+  float* part;
+  int64_t C, chunk;
+  int ncol;  // 256-column tiles
+  int nwg;   // workgroups: ncol x chunks
+};
 
-// RT: rank tile (r <= RT, a multiple of 16).  Grid: (ceil(C / 256), chunks).
-// Thread t loads, per step, rows 2 (t % 8) + {0, 1} + 16 q (q < kQ) of
-// columns 8 (t / 8) .. + 7: 2 kQ 16-byte loads, 8 rows x 128 bytes per wave
-// instruction.  Each pair of rows is packed per column into one 32-bit word
-// and stored at [column][row pair] of the transposed tile.
-template <int RT, typename T>
-__global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restrict__ X, int64_t M,
-                                                         int64_t C, const T* __restrict__ P, int r,
-                                                         int64_t chunk, float* __restrict__ part) {
+// RT: rank tile (r <= RT, a multiple of 16).  1-D grid: the workgroups of
+// job a, then those of job b (dA and dB in one launch); inside a job the
+// column tile runs fastest.  Thread t loads, per step, rows 2 (t % 8) +
+// {0, 1} + 16 q (q < kQ) of columns 8 (t / 8) .. + 7: 2 kQ 16-byte loads,
+// 8 rows x 128 bytes per wave instruction.  Each pair of rows is packed
+// per column into one 32-bit word and stored at [column][row pair] of the
+// transposed tile.  kDepth register sets of loads are in flight: step s + 2
+// is loaded while step s is computed (one set for RT = 128, whose
+// accumulators leave no room for two).  Steps past the chunk read clamped
+// rows and a zero P, so the loop runs in pairs without branches.
+template <int RT>
+__global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const GradJob jb,
+                                                         int64_t M, int r) {
   constexpr int kPer = (kStep * RT + 255) / 256;  // P elements per thread per step
+  constexpr int kDepth = RT <= 64 ? 2 : 1;
   __shared__ __attribute__((aligned(16))) uint16_t sX[kCols * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t sP[RT * kPitch];
 
+  const bool second = static_cast<int>(blockIdx.x) >= ja.nwg;  // uniform
+  const uint16_t* X = second ? jb.X : ja.X;
+  const uint16_t* P = second ? jb.P : ja.P;
+  float* part = second ? jb.part : ja.part;
+  const int64_t C = second ? jb.C : ja.C;
+  const int64_t chunk = second ? jb.chunk : ja.chunk;
+  const int ncol = second ? jb.ncol : ja.ncol;
+  const int bid = static_cast<int>(blockIdx.x) - (second ? ja.nwg : 0);
+  const int ct = bid % ncol, ch = bid / ncol;
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * kCols;
-  const int64_t m_lo = static_cast<int64_t>(blockIdx.y) * chunk;
+  const int64_t c0 = static_cast<int64_t>(ct) * kCols;
+  const int64_t m_lo = static_cast<int64_t>(ch) * chunk;
   const int64_t m_hi = m_lo + chunk < M ? m_lo + chunk : M;
   const int nsteps = static_cast<int>((m_hi - m_lo + kStep - 1) / kStep);
 
@@ -69,7 +87,7 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
   const int lrp = tid & 7;          // row pair within 16 rows
   const int64_t lcol = c0 + 8 * lcg;
   const int64_t lcolc = lcol + 8 <= C ? lcol : C - 8;  // C % 64 == 0: a valid 8-column group
-  auto load_x = [&](int s, uint4 (&v)[2 * kQ]) {
+  auto load_step = [&](int s, uint4 (&v)[2 * kQ], uint32_t (&pv)[kPer]) {
 #pragma unroll
     for (int q = 0; q < kQ; ++q)
 #pragma unroll
@@ -78,16 +96,14 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
         m = m < m_hi ? m : m_hi - 1;  // rows past the chunk: valid data, P zeroed
         v[2 * q + h] = *reinterpret_cast<const uint4*>(X + m * C + lcolc);
       }
-  };
-  auto load_p = [&](int s, float (&pv)[kPer]) {
 #pragma unroll
     for (int i = 0; i < kPer; ++i) {
       const int idx = tid + 256 * i;
       const int mm = idx / RT, j = idx % RT;
       const int64_t m = m_lo + static_cast<int64_t>(s) * kStep + mm;
       const bool ok = idx < kStep * RT && j < r && m < m_hi;
-      const float v = ld_narrow(P, (ok ? m : m_lo) * r + (ok ? j : 0));
-      pv[i] = ok ? v : 0.f;
+      const uint32_t val = P[(ok ? m : m_lo) * r + (ok ? j : 0)];
+      pv[i] = ok ? val : 0u;
     }
   };
 
@@ -97,12 +113,11 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  uint4 xv[2 * kQ];
-  float pv[kPer];
-  load_x(0, xv);
-  load_p(0, pv);
   const int l16 = lane & 15, g = lane >> 4;
-  for (int s = 0; s < nsteps; ++s) {
+  // Step s: its loads (issued kDepth steps earlier) into the transposed LDS
+  // tiles, the loads of step s + kDepth into the same registers, then the
+  // MFMAs of step s.
+  auto step = [&](int s, uint4 (&xv)[2 * kQ], uint32_t (&pv)[kPer]) {
     __syncthreads();  // the previous step's operand reads are done
     // transposed stores: word (row pair lrp + 8 q) of column 8 lcg + e
 #pragma unroll
@@ -121,16 +136,11 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
       const int idx = tid + 256 * i;
       if (idx < kStep * RT) {
         const int mm = idx / RT, j = idx % RT;
-        sP[j * kPitch + mm] = static_cast<uint16_t>(pack_bf16x2(pv[i], 0.f) & 0xFFFF);
+        sP[j * kPitch + mm] = static_cast<uint16_t>(pv[i]);
       }
     }
     __syncthreads();
-    // next step's loads (clamped to the last step) before this step's MFMAs
-    {
-      const int sn = s + 1 < nsteps ? s + 1 : s;
-      load_x(sn, xv);
-      load_p(sn, pv);
-    }
+    load_step(s + kDepth, xv, pv);
 #pragma unroll
     for (int kk = 0; kk < kStep / 32; ++kk) {
       uint4 pa[RT / 16];
@@ -145,6 +155,20 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
         for (int a = 0; a < RT / 16; ++a) acc[a][b] = mfma16(pa[a], xb, acc[a][b]);
       }
     }
+  };
+  uint4 xv0[2 * kQ];
+  uint32_t pv0[kPer];
+  load_step(0, xv0, pv0);
+  if constexpr (kDepth == 2) {
+    uint4 xv1[2 * kQ];
+    uint32_t pv1[kPer];
+    load_step(1, xv1, pv1);
+    for (int s = 0; s < nsteps; s += 2) {
+      step(s, xv0, pv0);
+      step(s + 1, xv1, pv1);  // past the chunk when nsteps is odd: adds zeros
+    }
+  } else {
+    for (int s = 0; s < nsteps; ++s) step(s, xv0, pv0);
   }
 
   // lane (column l16, group g) holds rows j = 16 a + 4 g + v of columns
@@ -158,18 +182,28 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const uint16_t* __restr
       for (int v = 0; v < 4; ++v) {
         const int j = 16 * a + 4 * g + v;
         if (j < r && col < C)
-          part[(static_cast<int64_t>(blockIdx.y) * r + j) * C + col] = acc[a][b][v];
+          part[(static_cast<int64_t>(ch) * r + j) * C + col] = acc[a][b][v];
       }
     }
 }
 
-// out = s * sum over chunks (fixed order); transposed writes out[col][j].
-__global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restrict__ part,
-                                                           int nchunk, int r, int64_t C,
-                                                           float s, bool transposed,
-                                                           float* __restrict__ out) {
-  const int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+// dA[j][k] = s * sum over chunks of partA, then dB[n][j] (transposed) from
+// partB, in one launch; each element's chunks are added in a fixed order.
+__global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restrict__ partA,
+                                                           int nchA, int64_t K,
+                                                           float* __restrict__ dA,
+                                                           const float* __restrict__ partB,
+                                                           int nchB, int64_t N,
+                                                           float* __restrict__ dB, int r,
+                                                           float s) {
+  int64_t idx = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t nA = static_cast<int64_t>(r) * K;
+  const bool second = idx >= nA;
+  if (second) idx -= nA;
+  const int64_t C = second ? N : K;
   if (idx >= static_cast<int64_t>(r) * C) return;
+  const float* part = second ? partB : partA;
+  const int nchunk = second ? nchB : nchA;
   const int64_t j = idx / C, col = idx % C;
   // 16 loads in flight per batch (clamped to the last chunk, not added),
   // then the additions in chunk order
@@ -187,11 +221,11 @@ __global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restri
       if (c0 + i < nchunk) v += pv[i];
   }
   v *= s;
-  if (transposed) out[col * r + j] = v;
-  else out[j * C + col] = v;
+  if (second) dB[col * r + j] = v;
+  else dA[j * C + col] = v;
 }
 
-// Token chunks for C columns: about 256 workgroups, chunks a multiple of 32.
+// Token chunks for C columns: about 256 workgroups, chunks a multiple of 64.
 int64_t grads_chunk(int64_t M, int64_t C) {
   const int64_t nct = (C + kCols - 1) / kCols;
   int64_t nch = 256 / nct;
@@ -207,17 +241,16 @@ int64_t grads_nchunk(int64_t M, int64_t C) {
   return (M + chunk - 1) / chunk;
 }
 
-template <typename T>
-hipError_t launch_partial(const uint16_t* X, int64_t M, int64_t C, const T* Pn, int r,
-                          float* part, hipStream_t st) {
-  const int64_t chunk = grads_chunk(M, C);
-  const dim3 grid(static_cast<uint32_t>((C + kCols - 1) / kCols),
-                  static_cast<uint32_t>((M + chunk - 1) / chunk));
-  if (r <= 16) hipLaunchKernelGGL((grads_mfma_kernel<16, T>), grid, dim3(256), 0, st, X, M, C, Pn, r, chunk, part);
-  else if (r <= 32) hipLaunchKernelGGL((grads_mfma_kernel<32, T>), grid, dim3(256), 0, st, X, M, C, Pn, r, chunk, part);
-  else if (r <= 64) hipLaunchKernelGGL((grads_mfma_kernel<64, T>), grid, dim3(256), 0, st, X, M, C, Pn, r, chunk, part);
-  else hipLaunchKernelGGL((grads_mfma_kernel<128, T>), grid, dim3(256), 0, st, X, M, C, Pn, r, chunk, part);
-  return hipGetLastError();
+GradJob grad_job(const uint16_t* X, const uint16_t* P, int64_t M, int64_t C, float* part) {
+  GradJob j;
+  j.X = X;
+  j.P = P;
+  j.part = part;
+  j.C = C;
+  j.chunk = grads_chunk(M, C);
+  j.ncol = static_cast<int>((C + kCols - 1) / kCols);
+  j.nwg = j.ncol * static_cast<int>(grads_nchunk(M, C));
+  return j;
 }
 
 }  // namespace
@@ -227,28 +260,27 @@ size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
   return static_cast<size_t>(elems) * 4;
 }
 
-hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const void* u, bool u_bf16,
-                             const void* t, bool t_bf16, int64_t M, int64_t N, int64_t K,
-                             int r, float s, float* dA, float* dB, void* ws, hipStream_t st) {
+hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16_t* u,
+                             const uint16_t* t, int64_t M, int64_t N, int64_t K, int r, float s,
+                             float* dA, float* dB, void* ws, hipStream_t st) {
   if (r == 0) return hipSuccess;
   const int nchA = static_cast<int>(grads_nchunk(M, K));
   const int nchB = static_cast<int>(grads_nchunk(M, N));
   float* partA = static_cast<float*>(ws);
   float* partB = partA + static_cast<int64_t>(nchA) * r * K;
-  hipError_t e;
   if (M > 0) {
-    e = t_bf16 ? launch_partial(x, M, K, static_cast<const uint16_t*>(t), r, partA, st)
-               : launch_partial(x, M, K, static_cast<const float*>(t), r, partA, st);
-    if (e != hipSuccess) return e;
-    e = u_bf16 ? launch_partial(dy, M, N, static_cast<const uint16_t*>(u), r, partB, st)
-               : launch_partial(dy, M, N, static_cast<const float*>(u), r, partB, st);
+    const GradJob ja = grad_job(x, t, M, K, partA), jb = grad_job(dy, u, M, N, partB);
+    const dim3 grid(static_cast<uint32_t>(ja.nwg + jb.nwg));
+    if (r <= 16) hipLaunchKernelGGL((grads_mfma_kernel<16>), grid, dim3(256), 0, st, ja, jb, M, r);
+    else if (r <= 32) hipLaunchKernelGGL((grads_mfma_kernel<32>), grid, dim3(256), 0, st, ja, jb, M, r);
+    else if (r <= 64) hipLaunchKernelGGL((grads_mfma_kernel<64>), grid, dim3(256), 0, st, ja, jb, M, r);
+    else hipLaunchKernelGGL((grads_mfma_kernel<128>), grid, dim3(256), 0, st, ja, jb, M, r);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(grads_reduce_kernel, dim3(static_cast<uint32_t>((r * K + 255) / 256)), dim3(256), 0,
-                     st, partA, nchA, r, K, s, false, dA);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(grads_reduce_kernel, dim3(static_cast<uint32_t>((r * N + 255) / 256)), dim3(256), 0,
-                     st, partB, nchB, r, N, s, true, dB);
+  const int64_t n = static_cast<int64_t>(r) * (K + N);
+  hipLaunchKernelGGL(grads_reduce_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0,
+                     st, partA, nchA, K, dA, partB, nchB, N, dB, r, s);
   return hipGetLastError();
 }
 

@@ -100,11 +100,11 @@ hipError_t launch_dropout(const uint16_t* x, int64_t M, int64_t K, float p, uint
 hipError_t launch_dx_lora_dropout(uint16_t* dx, const uint16_t* ts, const uint16_t* A, int64_t M,
                                   int64_t K, int r, float p, uint64_t seed, hipStream_t st);
 
-// LoRA gradients (see lora_grads in the C ABI).  u and t are [M, r], each
-// fp32 or bf16; ws holds grads_workspace_bytes() of split-M partials.
+// LoRA gradients (see lora_grads in the C ABI).  u and t are bf16 [M, r];
+// ws holds grads_workspace_bytes() of split-M partials.
 size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r);
-hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const void* u, bool u_bf16,
-                             const void* t, bool t_bf16, int64_t M, int64_t N, int64_t K,
-                             int r, float s, float* dA, float* dB, void* ws, hipStream_t st);
+hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16_t* u,
+                             const uint16_t* t, int64_t M, int64_t N, int64_t K, int r, float s,
+                             float* dA, float* dB, void* ws, hipStream_t st);
 
 }  // namespace qn

@@ -163,3 +163,26 @@ def test_ragged_output_columns(N, K, M):
     torch.cuda.synchronize()
     assert np.array_equal(to_bits16(y_odd), to_bits16(y))
     assert buf[0].item() == 0
+
+
+@pytest.mark.parametrize("M", [8, 200])
+def test_grads_recompute_matches_saved(M):
+    """lora_grads without u and t recomputes them with the launches the
+    forward and backward use for u_out and t_out: dA (through t) is the same
+    bit for bit at any M, dB (through u) for token batches (M > 16)."""
+    wl = synth.tiny_layer(0)
+    rng = np.random.default_rng(500 + M)
+    x = bf16_dev(synth.bf16_bits(rng.standard_normal((M, 256)).astype(np.float32)))
+    dy = bf16_dev(synth.bf16_bits(rng.standard_normal((M, 256)).astype(np.float32)))
+    qw, _ = quantized_layer(wl)
+    A, B = bf16_dev(wl.A), bf16_dev(wl.B)
+    u = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
+    t = torch.empty((M, wl.r), dtype=torch.bfloat16, device=x.device)
+    qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha, u_out=u)
+    qn.qlora_linear_bwd_dx(qw, dy, A, B, wl.r, wl.alpha, t_out=t)
+    dA_s, dB_s = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha, u=u, t=t)
+    dA_r, dB_r = qn.lora_grads(x, dy, A, B, wl.r, wl.alpha)
+    torch.cuda.synchronize()
+    assert torch.equal(dA_s, dA_r)
+    if M > 16:
+        assert torch.equal(dB_s, dB_r)
