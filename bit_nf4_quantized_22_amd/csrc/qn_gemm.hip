@@ -19,8 +19,8 @@
 //     steps ahead (three activation buffers, 128-byte rows with an XOR
 //     swizzle instead of padding, so each 1 KB DMA fills whole rows and the
 //     fragment reads stay free of bank conflicts);
-//   * waves 4-7 load the 4-bit weight and its constants two steps ahead (a
-//     ring of three register sets) and dequantise one step ahead into the
+//   * waves 4-7 load the 4-bit weight and its constants three steps ahead
+//     (a ring of four register sets) and dequantise one step ahead into the
 //     other of two weight buffers.
 // One barrier per K step.  The 256-row tile halves the dequantisation per
 // flop against 128 rows, and moving the activation copy to DMA leaves the
@@ -423,25 +423,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   };
 
   // Waves 0-3 run the MFMAs and fetch the activation tiles by DMA; waves
-  // 4-11 load and dequantise the weight.  Per K step k: the MFMA waves
+  // 4-7 load and dequantise the weight.  Per K step k: the MFMA waves
   // consume activation buffer k % 3 and weight buffer k % 2, and start the
-  // DMA of step k + 2; the producers dequantise step k + 1 (loaded two steps
-  // earlier, a ring of three register sets) into the other weight buffer.
+  // DMA of step k + 2; the producers dequantise step k + 1 (loaded three
+  // steps earlier, a ring of four register sets) into the other weight
+  // buffer.
   // One barrier per K step.  Steps past the end re-load the last step; what
   // they store is never read.
   if (t >= 64 * kMmaWaves) {
     const int pt = t - 64 * kMmaWaves;
-    Prefetch p0, p1, p2;
+    Prefetch p0, p1, p2, p3;
     load_step<kBwd, kDQ>(g, c0, 0, p0, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 1 ? 1 : nk - 1, p1, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 2 ? 2 : nk - 1, p2, pt);
+    load_step<kBwd, kDQ>(g, c0, nk > 3 ? 3 : nk - 1, p3, pt);
     store_lora();
     __syncthreads();  // the LoRA tiles visible
     store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.fp8), P, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
-      const int kl = k + 3 < nk ? k + 3 : nk - 1;
-      // Pin the first use of the registers loaded two steps ago here, after
+      const int kl = k + 4 < nk ? k + 4 : nk - 1;
+      // Pin the first use of the registers loaded three steps ago here, after
       // the barrier, so the compiler cannot hoist their address arithmetic
       // next to the loads it has just issued and wait for those.
       asm volatile("" : "+v"(dec.w), "+v"(dec.q8), "+v"(dec.c));
@@ -451,13 +453,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
       __syncthreads();
     };
     int k = 0;
-    for (; k + 2 < nk; k += 3) {
+    for (; k + 3 < nk; k += 4) {
       step(k, p1, p0);
       step(k + 1, p2, p1);
-      step(k + 2, p0, p2);
+      step(k + 2, p3, p2);
+      step(k + 3, p0, p3);
     }
     if (k < nk) step(k, p1, p0);
     if (k + 1 < nk) step(k + 1, p2, p1);
+    if (k + 2 < nk) step(k + 2, p3, p2);
   } else {
     const ADma ad = adma_offsets(m0, g.M, L);
     const uint16_t* act_tile = g.act + m0 * L;
