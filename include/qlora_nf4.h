@@ -254,8 +254,12 @@ QN_API int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, i
  * [kwkr] §2.3: only the LoRA matrices receive gradients; the 4-bit weight
  * and its constants get none.
  *   x bf16[M, K], dy bf16[M, N], A bf16[r, K], B bf16[N, r] (device).
- *   u bf16[M, r] (x A^T from the forward) or NULL to recompute it in fp32;
- *   t bf16[M, r] (dy B from the backward) or NULL to recompute it.
+ *   u bf16[M, r] (x A^T, the forward's u_out) or NULL to recompute it;
+ *   t bf16[M, r] (dy B, the backward's t_out) or NULL to recompute it.
+ *   A recomputed u or t is the bf16 value the forward or backward returns
+ *   in u_out / t_out (same launches and summation order), so both ways
+ *   give the same dA (any M) and dB (M > 16) bit for bit.
+ *   ws     device workspace of ws_bytes >= qn_workspace_bytes(QN_OP_LORA_GRADS,..).
  *   dA fp32[r, K] and dB fp32[N, r] out (overwritten, not accumulated).
  *   r must be 1..128.  The reduction over M is split into fixed chunks and
  *   summed in a fixed order, so results are bit-reproducible.
