@@ -6,8 +6,8 @@
 // constants to 8 bits.  [kwkr "QLoRA原理深入" §2.3, §3.1] 4-bit storage,
 // dequantised for compute; block size 64; 8-bit constants.
 //
-// All three kernels are HBM-streaming: one pass over the input, one write
-// of the output, 16-byte vector loads and stores, no re-reads.
+// All kernels here are HBM-streaming: one pass over the input, one write
+// of the output, no re-reads.
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -71,29 +71,14 @@ __device__ __forceinline__ uint32_t bucket_code(const QuantBucket* sbk, float v,
   return e.base + (v > e.thr ? 1u : 0u);
 }
 
-// Each lane owns 16 consecutive weights; the 4 lanes of a 64-weight block
-// reduce their absmax with two cross-lane steps.  Code of a weight:
-//   fast path  q = w * rcp(c) (|q - fl32(w/c)| <= 2^-22 for |w| <= c,
-//              c >= 2^-100); the bucket lookup on q gives the code of q.
-//              It equals the code of fl32(w/c) unless a threshold lies
-//              within 2^-22 of q.  Thresholds sit >= 2^-19 inside their
-//              bucket (host-checked), so only the bucket's own threshold
-//              can; a lane whose q comes within 2^-20 of it ("danger"),
-//              or whose block constant is below 2^-100, redoes its 16
-//              weights on the exact path.
-//   exact path q = fl32(w / c) by IEEE division, then the same lookup.
-template <bool kBf16>
-__global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
-    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
-    float* __restrict__ absmax, QuantParams P) {
-  __shared__ QuantBucket sbk[kMaxBuckets];
+// Bucket table: bucket b holds the threshold whose bucket is b (if any)
+// and counts the thresholds in lower buckets (same bucket function as
+// bucket_code; the host checked that buckets hold at most one threshold
+// with a margin).
+__device__ __forceinline__ void fill_buckets(QuantBucket* sbk, const QuantParams& P, int nthreads) {
   const float sc = P.scale;
   const float top = static_cast<float>(P.nbuckets - 1);
-  // Bucket table: bucket b holds the threshold whose bucket is b (if any)
-  // and counts the thresholds in lower buckets (same bucket function as
-  // bucket_code; the host checked that buckets hold at most one threshold
-  // with a margin).
-  for (uint32_t b = threadIdx.x; b < P.nbuckets; b += kQThreads) {
+  for (uint32_t b = threadIdx.x; b < P.nbuckets; b += nthreads) {
     uint32_t base = 0;
     float thr = INFINITY;
 #pragma unroll
@@ -105,9 +90,28 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
     }
     sbk[b] = QuantBucket{thr, base};
   }
-  __syncthreads();
+}
 
-  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kQThreads + threadIdx.x) * kQPerThread;
+// Each lane owns 16 consecutive weights from e0; the 4 lanes of a
+// 64-weight block reduce their absmax with two cross-lane steps.  Code of
+// a weight:
+//   fast path  q = w * rcp(c) (|q - fl32(w/c)| <= 2^-22 for |w| <= c,
+//              c >= 2^-100); the bucket lookup on q gives the code of q.
+//              It equals the code of fl32(w/c) unless a threshold lies
+//              within 2^-22 of q.  Thresholds sit >= 2^-19 inside their
+//              bucket (host-checked), so only the bucket's own threshold
+//              can; a lane whose q comes within 2^-20 of it ("danger"),
+//              or whose block constant is below 2^-100, redoes its 16
+//              weights on the exact path.
+//   exact path q = fl32(w / c) by IEEE division, then the same lookup
+//              (q = w for an all-zero block: the code of v = 0).
+// Writes the 8 packed bytes (numel is even) and returns the block constant.
+template <bool kBf16>
+__device__ __forceinline__ float quantize16(const QuantBucket* sbk, const QuantParams& P,
+                                            const void* __restrict__ w, int64_t e0, int64_t numel,
+                                            uint8_t* __restrict__ packed) {
+  const float sc = P.scale;
+  const float top = static_cast<float>(P.nbuckets - 1);
   float x[16];
   load16<kBf16>(w, e0, numel, x);
 
@@ -129,10 +133,14 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
     danger |= fabsf(q - thr) <= kDanger;
   }
   if (danger) {
+    // an all-zero block (c = 0) takes the code of v = 0, as in the fast
+    // path: with a threshold at 0 (FP4's two zeros) it lands here, and 0 / 0
+    // would be NaN
+    const float cd = c > 0.0f ? c : 1.0f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       float thr;
-      code[i] = bucket_code(sbk, x[i] / c, sc, top, thr);
+      code[i] = bucket_code(sbk, x[i] / cd, sc, top, thr);
     }
   }
 
@@ -151,13 +159,55 @@ __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
       for (int64_t b = 0; b < nbytes; ++b)
         dst[b] = static_cast<uint8_t>(((b < 4 ? lo : hi) >> (8 * (b & 3))) & 0xFF);
     }
-    if ((threadIdx.x & 3) == 0) absmax[e0 / 64] = c;
   }
+  return c;
 }
 
-// One workgroup of 256 lanes per group of 256 block constants.  The code of
-// v = fl32(c / c2) is the nearest level of the uint8 grid fl32(q / 255), or
-// (kFP8) the nearest E4M3 number ([kwkr] §3.1 names fp8 for the constants).
+template <bool kBf16>
+__global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
+    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, QuantParams P) {
+  __shared__ QuantBucket sbk[kMaxBuckets];
+  fill_buckets(sbk, P, kQThreads);
+  __syncthreads();
+  const int64_t e0 = (static_cast<int64_t>(blockIdx.x) * kQThreads + threadIdx.x) * kQPerThread;
+  const float c = quantize16<kBf16>(sbk, P, w, e0, numel, packed);
+  if (e0 < numel && (threadIdx.x & 3) == 0) absmax[e0 / 64] = c;
+}
+
+// Decision thresholds of the 8-bit grid, one per thread j < 256: the
+// largest fp32 <= the fp64 mid-point of adjacent levels fl32(j / 255)
+// (exact in fp64); +inf last.
+__device__ __forceinline__ void fill_l8_thresholds(float* sthr, int j) {
+  float thr = INFINITY;
+  if (j < 255) {
+    const double m = (static_cast<double>(l8_value(j)) + static_cast<double>(l8_value(j + 1))) * 0.5;
+    thr = static_cast<float>(m);
+    if (static_cast<double>(thr) > m) thr = nextafterf(thr, -INFINITY);
+  }
+  sthr[j] = thr;
+}
+
+// Level-2 code of a block constant c in a group with maximum c2: v =
+// fl32(c / c2), the nearest level of the uint8 grid fl32(q / 255), or (kFP8)
+// the nearest E4M3 number ([kwkr] §3.1 names fp8 for the constants).
+template <bool kFP8>
+__device__ __forceinline__ uint8_t dq_code(float c, float c2, const float* sthr) {
+  int q = 0;
+  if (c2 > 0.0f) {
+    const float v = c / c2;  // IEEE division
+    if constexpr (kFP8) {
+      q = static_cast<int>(e4m3_code(v));
+    } else {
+      q = static_cast<int>(fminf(fmaxf(fmaf(v, 255.0f, 0.5f), 0.0f), 255.0f));
+      while (q < 255 && v > sthr[q]) ++q;
+      while (q > 0 && !(v > sthr[q - 1])) --q;
+    }
+  }
+  return static_cast<uint8_t>(q);
+}
+
+// One workgroup of 256 lanes per group of 256 block constants.
 template <bool kFP8>
 __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restrict__ absmax,
                                                           int64_t nblocks,
@@ -165,18 +215,7 @@ __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restric
                                                           float* __restrict__ gscale) {
   __shared__ float sthr[256];
   __shared__ float smax[4];
-  // Decision thresholds of the 8-bit grid: the largest fp32 <= the fp64
-  // mid-point of adjacent levels fl32(j / 255) (exact in fp64); +inf last.
-  {
-    const int j = threadIdx.x;
-    float thr = INFINITY;
-    if (j < 255) {
-      const double m = (static_cast<double>(l8_value(j)) + static_cast<double>(l8_value(j + 1))) * 0.5;
-      thr = static_cast<float>(m);
-      if (static_cast<double>(thr) > m) thr = nextafterf(thr, -INFINITY);
-    }
-    sthr[j] = thr;
-  }
+  fill_l8_thresholds(sthr, threadIdx.x);
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   const float c = i < nblocks ? absmax[i] : 0.0f;
   const float wm = wave_max(c);
@@ -184,20 +223,7 @@ __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restric
   __syncthreads();
   const float c2 = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
   if (threadIdx.x == 0) gscale[blockIdx.x] = c2;
-  if (i < nblocks) {
-    int q = 0;
-    if (c2 > 0.0f) {
-      const float v = c / c2;  // IEEE division
-      if constexpr (kFP8) {
-        q = static_cast<int>(e4m3_code(v));
-      } else {
-        q = static_cast<int>(fminf(fmaxf(fmaf(v, 255.0f, 0.5f), 0.0f), 255.0f));
-        while (q < 255 && v > sthr[q]) ++q;
-        while (q > 0 && !(v > sthr[q - 1])) --q;
-      }
-    }
-    qscale[i] = static_cast<uint8_t>(q);
-  }
+  if (i < nblocks) qscale[i] = dq_code<kFP8>(c, c2, sthr);
 }
 
 // Each thread expands 32 codes: four runs of 8 (4 packed bytes, one block

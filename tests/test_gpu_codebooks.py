@@ -174,3 +174,21 @@ def test_merge_with_codebook(kind, scale):
     assert e <= 4e-3, e
     # B = 0: the merge is the bf16 dequantised weight bit for bit
     assert np.array_equal(to_bits16(frozen), nf4.f32_to_bf16_bits(ref["What"]))
+
+
+@pytest.mark.parametrize("kind", ["fp4", "nf4"])
+def test_all_zero_blocks_take_the_zero_code(kind):
+    """Blocks of +0 and -0 only (absmax 0) take the code of v = 0 (index 7)
+    in both tables; FP4's zero bin has a decision threshold at exactly 0."""
+    w = np.zeros((4, 64), np.float32)
+    w[1, ::2] = -0.0
+    w[2] = np.float32(0.01)  # a normal block between them
+    w[3, 1::3] = -0.0
+    quant = qn.fp4_quantize if kind == "fp4" else qn.nf4_quantize
+    packed, absmax = quant(f32_dev(w.reshape(-1)))
+    torch.cuda.synchronize()
+    want_p, want_a = codebooks.quantize_4bit(w, kind)
+    got = packed.cpu().numpy()
+    assert np.array_equal(got, want_p)
+    assert np.all(got.reshape(4, 32)[[0, 1, 3]] == 0x77)
+    assert np.array_equal(absmax.cpu().numpy().view(np.uint32), want_a.view(np.uint32))
