@@ -159,12 +159,19 @@ def cpu_baseline(workloads):
         if elapsed >= 12.0 or elapsed + t_gemm / reps > 30.0 or reps >= 64:
             break
     total = time.perf_counter() - t_all
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")),
+                         model)
+    except OSError:
+        pass
     return {"value": round(flops / t_gemm / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
             "sample": "oracle on the bench's own inputs: quantise+DQ+dequant of W 11008x4096 and "
                       "4096x11008, fp64 fwd+bwd_dx over all 2048 tokens (r=16) repeated "
                       f"{reps}x, LoRA grads once; {total:.1f} s wall, fwd+bwd {t_gemm:.1f} s; "
-                      f"cpu_count={os.cpu_count()}"}
+                      f"cpu_count={os.cpu_count()}, BLAS threads {threads}, {model}"}
 
 
 def unfused_context(qn, torch, layers, reps=10):
