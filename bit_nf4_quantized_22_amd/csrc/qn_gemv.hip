@@ -18,9 +18,9 @@
 // of row n (one 8-byte load), the two MFMAs of a block take the first and
 // second 8 of them, and the x operand uses the same k-slot map.
 //
-// The byte table has 32 copies, lane l reading copy l % 32, so the random
-// lookups of a wave spread over all LDS banks (a single shared copy halves
-// the lookup rate on gfx950).
+// The byte table has 32 copies (64 in 16-wave workgroups), lane l reading
+// copy l mod copies, so the random lookups of a wave spread over all LDS
+// banks (a single shared copy halves the lookup rate on gfx950).
 
 #include "qn_device.h"
 #include "qn_launch.h"
