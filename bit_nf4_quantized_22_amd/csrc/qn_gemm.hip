@@ -560,16 +560,48 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   }
   if (t >= 64 * kMmaWaves) return;
 
-  // Epilogue: accumulators straight to bf16 in HBM.  The MFMAs take the
-  // weight fragment as their first operand, so each 32 x 32 tile holds the
-  // transposed product: lane (li, lg) holds token row li, output columns
-  // 8 q + 4 lg + [0, 4) in registers 4 q .. 4 q + 3, stored as one 8-byte
-  // write (a quarter of the store instructions of one 2-byte store per
-  // register, measured 3-6 us faster per launch).
+  // Epilogue.  The MFMAs take the weight fragment as their first operand,
+  // so each 32 x 32 tile holds the transposed product: lane (li, lg) holds
+  // token row li, output columns 8 q + 4 lg + [0, 4) in registers
+  // 4 q .. 4 q + 3.  With a 16-byte aligned y whose rows are whole 16-byte
+  // chunks, each wave stages its tile in LDS and stores whole 128-byte row
+  // segments (8 rows per instruction): 1.4-5.3% faster per launch than
+  // storing the registers' 8-byte runs directly (32 rows x 16 bytes per
+  // instruction), which remains for other y.  One 2-byte store per register
+  // was 3-6 us slower again.
   {
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int li = lane & 31, lg = lane >> 5;
+    const bool vec16 = (ncols & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
+    if (vec16) {
+      // stage the wave's 128 x 64 tile in LDS (the activation buffers and
+      // weight buffer 0 are free now), then write whole 128-byte row
+      // segments: 8 rows per 16-byte store instruction
+      constexpr int kSP = kBN / 2 + 8;  // staged row pitch in bf16
+      uint16_t* stg = wave == 0 ? sA0 : wave == 1 ? sA1 : wave == 2 ? sA2 : sB[0];
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int row = i * 32 + li, col = j * 32 + 8 * q + 4 * lg;
+            *reinterpret_cast<uint2*>(stg + row * kSP + col) =
+                make_uint2(pack_bf16x2(acc[i][j][4 * q], acc[i][j][4 * q + 1]),
+                           pack_bf16x2(acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]));
+          }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+      for (int s = 0; s < (kBM / 2) * (kBN / 2) / 8 / 64; ++s) {
+        const int row = s * 8 + (lane >> 3), ch = lane & 7;
+        const uint4 v = *reinterpret_cast<const uint4*>(stg + row * kSP + ch * 8);
+        const int64_t m = m0 + wm * (kBM / 2) + row;
+        const int64_t n = c0 + wn * (kBN / 2) + ch * 8;
+        if (m < g.M && n < ncols) *reinterpret_cast<uint4*>(g.out + m * ncols + n) = v;
+      }
+      return;
+    }
     const bool vec = (ncols & 3) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 7) == 0;
 #pragma unroll
     for (int i = 0; i < kTM; ++i)

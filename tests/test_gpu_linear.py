@@ -150,19 +150,21 @@ def test_empty_batch_is_a_no_op():
 @pytest.mark.parametrize("N,K", [(192, 128), (320, 192)])
 @pytest.mark.parametrize("M", [40, 300])
 def test_ragged_output_columns(N, K, M):
-    """Output widths that end in half a 128-column tile, and y at an odd
-    element offset (rows not 8-byte aligned, so the GEMM stores element by
-    element): both write the same values."""
+    """Output widths that end in half a 128-column tile, and y at an element
+    offset of 1 (rows not 8-byte aligned: element stores) or 4 (8-byte but not
+    16-byte aligned: 8-byte stores from registers instead of the staged
+    16-byte rows): every store path writes the same values."""
     wl = synth.train_linear(N, K, M=M, seed=N + M, r=8, alpha=16.0)
     run_layer_checks(wl, M=M)
     qw, _ = quantized_layer(wl)
     x, A, B = bf16_dev(wl.x), bf16_dev(wl.A), bf16_dev(wl.B)
     y = qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha)
-    buf = torch.zeros(M * N + 1, dtype=torch.bfloat16, device=x.device)
-    y_odd = qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha, y=buf[1:].view(M, N))
-    torch.cuda.synchronize()
-    assert np.array_equal(to_bits16(y_odd), to_bits16(y))
-    assert buf[0].item() == 0
+    for off in (1, 4):
+        buf = torch.zeros(M * N + off, dtype=torch.bfloat16, device=x.device)
+        y_off = qn.qlora_linear_fwd(qw, x, A, B, wl.r, wl.alpha, y=buf[off:].view(M, N))
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits16(y_off), to_bits16(y)), f"offset {off}"
+        assert not buf[:off].any().item()
 
 
 @pytest.mark.parametrize("M", [8, 200])
