@@ -31,7 +31,6 @@ namespace {
 
 constexpr int kUParts = 8;   // LoRA partial sums held per thread in the GEMV
 constexpr int kXAhead = 3;   // x prefetch distance, in blocks (register ring)
-constexpr int kXMaxM = 4;    // token rows staged in LDS instead (M <= 4)
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
@@ -222,7 +221,7 @@ struct GemvArgs {
   float s;
 };
 
-// kXM: token rows of x staged in LDS per wave (1 or 4; 0: no staging, x
+// kXM: token rows of x staged in LDS per wave (1; 0: no staging, x
 // read per block from memory into a register ring).  kCopiesT: pair-table
 // copies, 64 for 16-wave workgroups (entry address (e << 8) | 4 lane is one
 // v_perm), else 32 (LDS for several workgroups per CU).
@@ -520,18 +519,13 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   }
 }
 
-// One GEMV configuration; four-row x staging only where its LDS fits
-// (otherwise the register ring).
+// One GEMV configuration: the single token row staged in LDS (xmode 1), or
+// the register ring.
 template <int W, int S>
 void gemv_config(int xmode, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
                  const CodeParams& P) {
-  constexpr size_t kLds = 256 * (W == 16 ? 64 : 32) * 4 + W * kXMaxM * S * 128 +
-                          W * 16 * 17 * 4 + 1024 + (S * 8 + 8) * 16;
-  constexpr bool kFits4 = kLds <= 160 * 1024;
   if (xmode == 1) {
     hipLaunchKernelGGL((gemv_kernel<W, S, true, 1>), grid, dim3(W * 64), 0, st, a, P);
-  } else if (xmode == 4 && kFits4) {
-    if constexpr (kFits4) hipLaunchKernelGGL((gemv_kernel<W, S, true, 4>), grid, dim3(W * 64), 0, st, a, P);
   } else if (dq) {
     hipLaunchKernelGGL((gemv_kernel<W, S, true, 0>), grid, dim3(W * 64), 0, st, a, P);
   } else {
@@ -660,9 +654,10 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 12 ? 12 : 16;
   if (wv == 16 && sb == 16) sb = 12;  // 16 x 16 would spill at 1024 threads
   const bool dq = w.qscale != nullptr;
-  // x staging: one row for M == 1, four for M <= 4, none above (ring);
-  // the unscaled-constant path (no double quantisation) uses the ring.
-  const int xmode = !dq ? 0 : M == 1 ? 1 : M <= kXMaxM ? 4 : 0;
+  // x staging: the one row for M == 1, the register ring above (also for
+  // M <= 4: staging four rows was 15% slower at 11008 x 4096, M = 4); the
+  // unscaled-constant path (no double quantisation) uses the ring.
+  const int xmode = !dq ? 0 : M == 1 ? 1 : 0;
 #define QN_GEMV(W, S) \
   if (wv == W && sb == S) gemv_config<W, S>(xmode, dq, grid, st, a, P);
   QN_GEMV(4, 4) QN_GEMV(4, 8) QN_GEMV(4, 12) QN_GEMV(4, 16)
