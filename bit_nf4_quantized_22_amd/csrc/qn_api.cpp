@@ -27,6 +27,15 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? QN_OK : QN_ERR_HIP; }
 
+// The adapter of a call: r == 0, or A and B both NULL, is the frozen layer
+// (rank 0); exactly one of A, B NULL with r > 0 is an error.
+int adapter_rank(int32_t r, const void* A, const void* B, int32_t& r_eff) {
+  r_eff = r;
+  if (r > 0 && !A && !B) r_eff = 0;
+  else if (r > 0 && (!A || !B)) return QN_ERR_NULL;
+  return QN_OK;
+}
+
 // Validates a quantised weight for the linear ops and fills a view.
 int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   if (!w || !w->packed) return QN_ERR_NULL;
@@ -140,7 +149,8 @@ int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M,
   if (M < 0 || r < 0) return QN_ERR_SHAPE;
   if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
   if (M == 0 || w->N == 0) return QN_OK;
-  if (!x || !xa || !y || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if ((st = adapter_rank(r, A, B, r)) != QN_OK) return st;
+  if (!x || !xa || !y) return QN_ERR_NULL;
   if (!aligned(x, 16) || !aligned(xa, 16) || !aligned(y, 2) || (r > 0 && (!aligned(A, 16) || !aligned(B, 2))) ||
       (u_out && !aligned(u_out, 2)))
     return QN_ERR_ALIGN;
@@ -184,7 +194,8 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
   if (M < 0 || r < 0) return QN_ERR_SHAPE;
   if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
   if (M == 0 || w->K == 0) return QN_OK;
-  if (!dy || !dx || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if ((st = adapter_rank(r, A, B, r)) != QN_OK) return st;
+  if (!dy || !dx) return QN_ERR_NULL;
   if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
       (t_out && !aligned(t_out, 2)))
     return QN_ERR_ALIGN;
@@ -324,7 +335,8 @@ int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t 
   if (st != QN_OK) return st;
   if (r < 0) return QN_ERR_SHAPE;
   if (r > kMaxRank) return QN_ERR_UNSUPPORTED;
-  if (!out || (r > 0 && (!A || !B))) return QN_ERR_NULL;
+  if ((st = adapter_rank(r, A, B, r)) != QN_OK) return st;
+  if (!out) return QN_ERR_NULL;
   if (!aligned(out, 16) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2)))) return QN_ERR_ALIGN;
   if (!qn::tables()) return QN_ERR_UNSUPPORTED;
   (void)hipGetLastError();

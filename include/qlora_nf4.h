@@ -187,7 +187,10 @@ QN_API int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t 
  * nf4_dequant -- materialise the weight.
  * [rkmt] §2.2.1: look the 4-bit index up in the code table and scale it;
  * [kwkr] §2.3: the 16-bit copy is a compute-time value.
- *   out      device [N, K] of out_dtype (QN_F32 or QN_BF16).
+ *   out      device [N, K] of out_dtype (QN_F32 or QN_BF16), 16-byte
+ *            aligned.  N * K must be a multiple of 32 (QN_ERR_SHAPE
+ *            otherwise: a thread expands whole 32-code runs); N and K need
+ *            not be multiples of 64 (a block may cross a row).
  * Value: c' = fl32(fl32(q/255) * gscale) (or absmax when not
  * double-quantised), w = fl32(code_value * c'); bf16 output is the RNE of
  * that fp32.  Bit-identical to the definition, including -0.0.
@@ -212,7 +215,9 @@ QN_API size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, in
  *   x      device bf16[M, K];  A bf16[r, K];  B bf16[N, r].
  *   y      device bf16[M, N] out.
  *   u_out  device bf16[M, r] out (x * A^T, kept for the backward), or NULL.
- *   r      0 (frozen layer: A, B ignored) or 1..128.
+ *   r      0 (frozen layer: A, B ignored) or 1..128.  A == B == NULL with
+ *          r > 0 is the frozen layer too (no workspace needed, u_out left
+ *          untouched); exactly one of them NULL with r > 0 is QN_ERR_NULL.
  *   ws     device workspace of ws_bytes >= qn_workspace_bytes(QN_OP_FWD,..).
  */
 QN_API int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M,
@@ -226,6 +231,7 @@ QN_API int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M,
  * input and into the LoRA bypass only.
  *   dy     device bf16[M, N];  dx device bf16[M, K] out.
  *   t_out  device bf16[M, r] out (dy * B), or NULL.
+ *   r == 0, or A == B == NULL, is the frozen layer (as in qlora_linear_fwd).
  */
 QN_API int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M,
                         const qn_bf16* A, const qn_bf16* B, int32_t r, float alpha,
@@ -244,7 +250,8 @@ QN_API int qlora_linear_bwd_dx(const qn_weight* w, const qn_bf16* dy, int64_t M,
  *   rank-r product of the bf16 operands accumulated in fp32 (MFMA), scaled
  *   by alpha/r in fp32, added to the fp32 dequantised weight, then rounded
  *   to bf16 (nearest even); r == 0 writes bf16(dequant(W)) exactly.
- *   r must be 0..128.  N and K must be positive multiples of 64.
+ *   r must be 0..128; A == B == NULL with r > 0 is taken as r == 0.  N and
+ *   K must be positive multiples of 64.
  */
 QN_API int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, int32_t r,
                        float alpha, qn_bf16* out, void* stream);

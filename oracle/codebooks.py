@@ -22,9 +22,10 @@ integer code) is stored as an FP8 E4M3 number (4 exponent bits with bias 7,
 the even code; the level value is that number itself, exact in fp32, and
 c' = fl32(value * c2).  Every E4M3 number in [0, 1] has a code below 0x39.
 
-[czcl] §2.1 prints a blockwise uniform 4-bit scheme: scale = absmax / 7,
-codes round(w / scale) clamped to [-7, 7].  It contradicts NF4 and is not a
-storage format of the path; it is kept as the strawman of the error study.
+[czcl] §2.1 shows a blockwise uniform 4-bit scheme as the contrast to NF4:
+a symmetric grid of 15 evenly spaced levels whose outermost ones sit at
+plus and minus the block's absmax.  It is not a storage format of the path;
+it is kept as the strawman of the error study.
 """
 
 from fractions import Fraction
@@ -148,18 +149,39 @@ def dequant_scales_fp8(q8, c2, group=nf4.GROUP):
     return (lv[q8] * c2[np.arange(q8.size) // group]).astype(np.float32)
 
 
+def int4_uniform_levels(absmax):
+    """The 15 levels j * absmax / 7, j = -7..7, of one block (fp64)."""
+    step = float(absmax) / 7.0
+    return np.arange(-7, 8, dtype=np.float64) * step
+
+
 def int4_uniform_roundtrip(w, blocksize=nf4.BLOCKSIZE):
-    """[czcl] §2.1's uniform scheme, quantised and dequantised in fp64:
-    scale = absmax / 7, q = clamp(round(w / scale), -7, 7), w' = q * scale."""
+    """Uniform symmetric 4-bit strawman ([czcl] §2.1), fp64.
+
+    Each block of ``blocksize`` values is replaced by its nearest level of
+    int4_uniform_levels(absmax of the block).  A value exactly half-way
+    between two levels takes the one with the even index j (the half-to-even
+    rounding of the page's framework).  An all-zero block stays zero.
+    """
     w = np.asarray(w, dtype=np.float64).ravel()
-    nb = -(-w.size // blocksize)
-    padded = np.zeros(nb * blocksize)
-    padded[:w.size] = w
-    b = padded.reshape(nb, blocksize)
-    scale = np.max(np.abs(b), axis=1, keepdims=True) / 7.0
-    safe = np.where(scale > 0, scale, 1.0)
-    q = np.clip(np.rint(b / safe), -7, 7)
-    return (q * scale).ravel()[:w.size]
+    out = np.empty_like(w)
+    for b0 in range(0, w.size, blocksize):
+        blk = w[b0:b0 + blocksize]
+        c = float(np.max(np.abs(blk)))
+        if c == 0.0:
+            out[b0:b0 + blocksize] = 0.0
+            continue
+        lv = int4_uniform_levels(c)
+        dist = np.abs(blk[:, None] - lv[None, :])        # [values, 15 levels]
+        best = dist.min(axis=1, keepdims=True)
+        ties = dist == best
+        # of the nearest levels (one, or two at a half-way point) keep the one
+        # with the even index j = level position - 7
+        even = (np.arange(15) - 7) % 2 == 0
+        pick = np.where((ties & even[None, :]).any(axis=1),
+                        np.argmax(ties & even[None, :], axis=1), np.argmax(ties, axis=1))
+        out[b0:b0 + blocksize] = lv[pick]
+    return out
 
 
 def relative_mse(w, w_hat):

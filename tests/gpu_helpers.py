@@ -63,10 +63,22 @@ def f64(bits):
 TOL = 1e-2
 
 
+def max_elem_over_row_norm(got, ref):
+    """Largest |got - ref| of an element divided by the norm of its row of
+    ref: catches an error confined to a few elements or rows, which the
+    Frobenius norm over the whole output averages away."""
+    got = np.atleast_2d(np.asarray(got, np.float64))
+    ref = np.atleast_2d(np.asarray(ref, np.float64))
+    rn = np.linalg.norm(ref, axis=1, keepdims=True)
+    return float(np.max(np.abs(got - ref) / np.maximum(rn, 1e-300)))
+
+
 def check(name, got, ref, tol=TOL):
     e = rel_frob(got, ref)
-    print(f"{name}: rel_frob={e:.3e}")
+    er = max_elem_over_row_norm(got, ref)
+    print(f"{name}: rel_frob={e:.3e} max_elem/row_norm={er:.3e}")
     assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol}"
+    assert er <= tol, f"{name}: an element is off by {er:.3e} of its row's norm"
 
 
 def quantized_layer(wl, double_quant=True):

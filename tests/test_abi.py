@@ -138,6 +138,31 @@ def test_linear_argument_errors(lib):
              None) == qn.QN_ERR_WORKSPACE
 
 
+def test_null_adapter_is_the_frozen_layer(lib):
+    """A == B == NULL with r > 0 is the frozen layer: no workspace is asked
+    for and no NULL error is raised (an argument error after that rule, a
+    misaligned output, shows the call got past it without launching);
+    exactly one of A, B NULL is still QN_ERR_NULL."""
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256)
+    fwd, bwd, merge = lib.qlora_linear_fwd, lib.qlora_linear_bwd_dx, lib.qlora_merge
+    assert fwd(ctypes.byref(w), FAKE, 32, None, None, 8, 16.0, ODD, None, None, 0,
+               None) == qn.QN_ERR_ALIGN
+    assert bwd(ctypes.byref(w), FAKE, 32, None, None, 8, 16.0, ODD, None, None, 0,
+               None) == qn.QN_ERR_ALIGN
+    assert merge(ctypes.byref(w), None, None, 8, 16.0, ODD, None) == qn.QN_ERR_ALIGN
+    for a, b in ((FAKE, None), (None, FAKE)):
+        assert fwd(ctypes.byref(w), FAKE, 32, a, b, 8, 16.0, FAKE, None, FAKE, 1 << 20,
+                   None) == qn.QN_ERR_NULL
+        assert bwd(ctypes.byref(w), FAKE, 32, a, b, 8, 16.0, FAKE, None, FAKE, 1 << 20,
+                   None) == qn.QN_ERR_NULL
+        assert merge(ctypes.byref(w), a, b, 8, 16.0, FAKE, None) == qn.QN_ERR_NULL
+
+
+def test_dequant_needs_whole_32_code_runs(lib):
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 3, 10, 64, 256)  # 30 codes
+    assert lib.nf4_dequant(ctypes.byref(w), qn.QN_BF16, FAKE, None) == qn.QN_ERR_SHAPE
+
+
 def test_merge_argument_errors(lib):
     w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256)
     bad = qn.qn_weight(0x100000, None, None, 0x100000, 100, 128, 64, 256)

@@ -47,3 +47,14 @@ def test_llama65b_layer_projection(idx):
     qw, ref = quantized_layer(wl)
     assert_quantized_equal(qw, ref)
     run_layer_checks(wl, rows=_rows(4096, 64, 100 + idx), grads=False, qw=qw, ref=ref)
+
+
+@pytest.mark.parametrize("idx", [0, 4, 6], ids=["q", "gate", "down"])
+def test_llama7b_projection_rank128(idx):
+    """r = 128 with alpha = 32 ([fg8] §8): the fused GEMMs' LoRA contraction
+    in two 64-deep passes, the 128-column LoRA projections and gradients."""
+    wl = synth.decoder_layer_linear(synth.LLAMA7B_TARGETS, idx, M=2048, r=128, alpha=32.0,
+                                    std=0.02, seed=4)
+    print(wl.name, flush=True)
+    qw, ref = quantized_layer(wl)
+    run_layer_checks(wl, rows=_rows(2048, 128, 50 + idx), qw=qw, ref=ref)

@@ -7,12 +7,14 @@ fp64; the HIP path rounds it to bf16 for the MFMA, so the expected error is
 the bf16 rounding of weights, activations and outputs (~1e-3).
 """
 
+import functools
+
 import numpy as np
 import pytest
 import torch
 
 import bit_nf4_quantized_22_amd as qn
-from tests.gpu_helpers import (TOL, bf16_dev, check, f32_dev, f64, linear, quantized_layer,
+from tests.gpu_helpers import (TOL, bf16_dev, check, f32_dev, f64, linear, nf4, quantized_layer,
                                rel_frob, run_layer_checks, synth, to_bits16, to_np)
 
 pytestmark = pytest.mark.gpu
@@ -188,3 +190,42 @@ def test_grads_recompute_matches_saved(M):
     assert torch.equal(dA_s, dA_r)
     if M > 16:
         assert torch.equal(dB_s, dB_r)
+
+
+@functools.lru_cache(maxsize=3)
+def _decode_weight(N, K):
+    """Device-quantised W (with and without double quantisation) and the
+    oracle's fp32 dequantised weights, shared by the cases of one shape."""
+    wl = synth.decode_layer(16, N, K, seed=2, r=64, alpha=16.0)
+    w32 = synth.bf16_to_f32(wl.W)
+    packed, absmax = nf4.quantize_nf4(w32)
+    q8, c2 = nf4.double_quantize(absmax)
+    What = {True: nf4.dequantize(packed, nf4.dequant_scales(q8, c2), w32.size).reshape(N, K),
+            False: nf4.dequantize(packed, absmax, w32.size).reshape(N, K)}
+    wdev = bf16_dev(wl.W).reshape(N, K)
+    qw = {True: qn.quantize_weight(wdev, True), False: qn.quantize_weight(wdev, False)}
+    return wl, qw, What
+
+
+@pytest.mark.parametrize("dq", [True, False], ids=["dq", "absmax"])
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("shape", [(8192, 22016), (22016, 8192), (8256, 4160)],
+                         ids=["65b-down", "65b-gate", "uneven"])
+def test_decode_gemv_long_rows(shape, M, dq):
+    """Decode shapes whose rows take several passes of the GEMV's waves (the
+    65B down and gate/up projections) and an uneven one (8256 x 4160: 65
+    blocks per row, so a pass ends on a single block and some wave slices
+    are empty), r = 64 so that M r exceeds the workgroup's thread count at
+    M = 16; y and u_out against the oracle, with and without double
+    quantisation of the block constants."""
+    N, K = shape
+    wl, qw, What = _decode_weight(N, K)
+    x = wl.x[:M]
+    u = torch.empty((M, wl.r), dtype=torch.bfloat16, device="cuda:0")
+    y = qn.qlora_linear_fwd(qw[dq], bf16_dev(x), bf16_dev(wl.A), bf16_dev(wl.B), wl.r, wl.alpha,
+                            u_out=u)
+    torch.cuda.synchronize()
+    want = linear.linear_forward(f64(x), What[dq].astype(np.float64), f64(wl.A), f64(wl.B),
+                                 wl.alpha, wl.r)
+    _check(f"y {shape} M={M} dq={dq}", to_np(y), want)
+    _check(f"u {shape} M={M}", to_np(u), linear.lora_down(f64(x), f64(wl.A)))

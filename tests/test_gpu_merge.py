@@ -68,13 +68,13 @@ def _merge_case(wl, double_quant=True, rows=None, B_override=None):
 def test_merge_tiny_fp32_layer():
     wl = synth.tiny_layer(0)
     _, _, _, got, want, mag = _merge_case(wl)
-    _check_merge(got, want, "tiny r=8", mag, min_exact=0.99)
+    _check_merge(got, want, "tiny r=8", mag)
 
 
 def test_merge_tiny_layer_without_double_quant():
     wl = synth.tiny_layer(0)
     _, _, _, got, want, mag = _merge_case(wl, double_quant=False)
-    _check_merge(got, want, "tiny r=8 absmax", mag, min_exact=0.99)
+    _check_merge(got, want, "tiny r=8 absmax", mag)
 
 
 def test_merge_decode_weight_r16():
@@ -83,13 +83,15 @@ def test_merge_decode_weight_r16():
     _check_merge(got, want, "4096x4096 r=16", mag)
 
 
+@pytest.mark.parametrize("r,alpha", [(64, 16.0), (128, 32.0)])
 @pytest.mark.parametrize("shape", [(11008, 4096), (4096, 11008)])
-def test_merge_training_weights_r64(shape):
+def test_merge_training_weights(shape, r, alpha):
+    # r = 64, alpha = 16 and r = 128, alpha = 32: the settings [fg8] §8 reports
     wl = synth.decoder_layer_linear(
-        [("w", shape[0], shape[1])], 0, M=16, r=64, alpha=16.0, std=0.02, seed=11)
+        [("w", shape[0], shape[1])], 0, M=16, r=r, alpha=alpha, std=0.02, seed=11)
     rows = np.sort(np.random.default_rng(1).choice(shape[0], 512, replace=False))
     _, _, _, got, want, mag = _merge_case(wl, rows=rows)
-    _check_merge(got, want, f"{shape} r=64 sampled rows", mag)
+    _check_merge(got, want, f"{shape} r={r} sampled rows", mag)
 
 
 @pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33)])
@@ -98,7 +100,7 @@ def test_merge_ragged_columns_and_ranks(N, K, r):
     32-deep MFMA steps (5, 33, 100)."""
     wl = synth.train_linear(N, K, M=16, seed=N + K + r, r=r, alpha=2.0 * r)
     _, _, _, got, want, mag = _merge_case(wl)
-    _check_merge(got, want, f"{N}x{K} r={r}", mag, min_exact=0.99)
+    _check_merge(got, want, f"{N}x{K} r={r}", mag)
 
 
 def test_merge_with_b_zero_is_the_bf16_dequant():

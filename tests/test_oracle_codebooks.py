@@ -154,3 +154,49 @@ def test_error_study_matches_the_pages_advice():
         assert res[name]["nf4"] < res[name]["fp4"] < res[name]["int4"], res[name]
     assert res["uniform"]["int4"] < res["uniform"]["nf4"], res["uniform"]
     assert 0.007 < res["normal"]["nf4"] < 0.010
+
+
+def test_uniform_int4_hand_worked_blocks():
+    """The uniform strawman of [czcl] §2.1 on blocks whose levels are exact
+    (absmax 7 * 2^e makes the level spacing the power of two 2^e), with the
+    result of every value worked out by hand from the definition: nearest
+    of the 15 levels j * absmax / 7, ties to the even j."""
+    # absmax 7: levels are the integers -7..7
+    blk = np.array([7.0, 3.5, -3.5, 2.5, -2.5, 0.5, -0.5, 6.6, -6.6, 1.2,
+                    0.0, -7.0, 4.49, 4.51, -1.5, 1.5])
+    want = np.array([7.0, 4.0, -4.0, 2.0, -2.0, 0.0, 0.0, 7.0, -7.0, 1.0,
+                     0.0, -7.0, 4.0, 5.0, -2.0, 2.0])
+    assert np.array_equal(codebooks.int4_uniform_roundtrip(blk, blocksize=16), want)
+    # absmax 14 (spacing 2): 3 and 5 are half-way (1.5 and 2.5 steps) and take
+    # the even levels 2 -> 4.0; 1 (half a step) goes to 0; -13 is 6.5 steps and
+    # goes to -6 -> -12.0; 14 is the top level
+    blk = np.array([14.0, 3.0, 5.0, 1.0, -13.0, -1.0, 9.0, 0.25])
+    want = np.array([14.0, 4.0, 4.0, 0.0, -12.0, 0.0, 8.0, 0.0])
+    assert np.array_equal(codebooks.int4_uniform_roundtrip(blk, blocksize=8), want)
+    # a negative absmax element maps to the bottom level exactly
+    blk = np.array([-0.875, 0.0625, 0.4375, 0.5])  # absmax 0.875 = 7/8, spacing 1/8
+    want = np.array([-0.875, 0.0, 0.5, 0.5])       # 0.0625 = half a step -> 0; 3.5 -> 4 steps
+    assert np.array_equal(codebooks.int4_uniform_roundtrip(blk, blocksize=4), want)
+    # an all-zero block stays zero; blocks are independent of each other
+    blk = np.concatenate([np.zeros(4), [7.0, 1.4, -2.6, 0.0]])
+    want = np.concatenate([np.zeros(4), [7.0, 1.0, -3.0, 0.0]])
+    assert np.array_equal(codebooks.int4_uniform_roundtrip(blk, blocksize=4), want)
+
+
+def test_uniform_int4_has_fifteen_symmetric_levels():
+    """Every reconstructed value is an integer multiple of absmax / 7 between
+    -7 and 7 steps, both ends are reached by the block's extreme values, and
+    a block and its negation give negated results (the grid is symmetric)."""
+    rng = np.random.default_rng(12)
+    w = rng.standard_normal(64 * 50)
+    w_hat = codebooks.int4_uniform_roundtrip(w).reshape(-1, 64)
+    blocks = w.reshape(-1, 64)
+    step = np.abs(blocks).max(1, keepdims=True) / 7.0
+    j = w_hat / step
+    assert np.allclose(j, np.rint(j), atol=1e-9) and np.all(np.abs(np.rint(j)) <= 7)
+    assert len(np.unique(np.rint(j))) <= 15
+    k = np.argmax(np.abs(blocks), axis=1)
+    assert np.allclose(np.abs(w_hat[np.arange(len(k)), k]), 7 * step[:, 0], rtol=1e-15)
+    assert np.array_equal(codebooks.int4_uniform_roundtrip(-w), -codebooks.int4_uniform_roundtrip(w))
+    # the error of every value is at most half a step
+    assert np.all(np.abs(w_hat - blocks) <= step / 2 * (1 + 1e-12))

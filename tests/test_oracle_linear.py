@@ -139,3 +139,35 @@ def test_rank_zero_is_frozen():
     x, W, _, _, dy = _case(seed=8)
     y = linear.linear_forward(x, W, None, None, 16.0, 0)
     assert np.array_equal(y, x @ W.T)
+
+
+def test_cross_check_with_torch_fp64_on_a_dequantised_weight():
+    """The oracle's forward, backward to the input and LoRA gradients equal
+    torch's CPU fp64 autograd of the same layer, y = x W^T + s (x A^T) B^T,
+    on an NF4-dequantised W (an independent library implementation of the
+    products and of the chain rule: dx, dA and dB come from torch's
+    backward, not from the oracle's formulas)."""
+    import torch
+
+    rng = np.random.default_rng(31)
+    M, N, K, r, alpha = 9, 192, 128, 4, 8.0
+    w = (rng.standard_normal(N * K) * 0.02).astype(np.float32)
+    packed, absmax = nf4.quantize_nf4(w)
+    q8, c2 = nf4.double_quantize(absmax)
+    What = nf4.dequantize(packed, nf4.dequant_scales(q8, c2), w.size).reshape(N, K)
+    x = rng.standard_normal((M, K))
+    A = rng.standard_normal((r, K)) * 0.1
+    B = rng.standard_normal((N, r)) * 0.1
+    dy = rng.standard_normal((M, N))
+    tx = torch.tensor(x, dtype=torch.float64, requires_grad=True)
+    tA = torch.tensor(A, dtype=torch.float64, requires_grad=True)
+    tB = torch.tensor(B, dtype=torch.float64, requires_grad=True)
+    tW = torch.tensor(What.astype(np.float64))
+    ty = torch.nn.functional.linear(tx, tW) + (alpha / r) * torch.nn.functional.linear(
+        torch.nn.functional.linear(tx, tA), tB)
+    ty.backward(torch.tensor(dy))
+    y = linear.linear_forward(x, What, A, B, alpha, r)
+    dx = linear.linear_backward_input(dy, What, A, B, alpha, r)
+    dA, dB = linear.lora_grads(x, dy, A, B, alpha, r)
+    for got, want in ((y, ty.detach()), (dx, tx.grad), (dA, tA.grad), (dB, tB.grad)):
+        assert np.allclose(got, want.numpy(), rtol=1e-12, atol=1e-12)

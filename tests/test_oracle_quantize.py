@@ -5,7 +5,7 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import nf4
+from oracle import codebooks, nf4
 
 
 def rn_f32(fr):
@@ -69,6 +69,38 @@ def test_matches_brute_force_on_random_blocks(seed):
     codes, amax = brute_force_codes(w)
     assert np.array_equal(packed, pack_ref(codes))
     assert [Fraction(float(a)) for a in absmax] == amax
+
+
+def test_tiny_and_subnormal_scales_match_brute_force():
+    """Blocks whose absmax is tiny (1e-30), at the bottom of the normal range
+    (near 2^-126) or subnormal (1e-40, 1e-44, the smallest subnormal 2^-149),
+    and blocks where w / c itself is subnormal or underflows to zero: the
+    fp32 quotient and the nearest code follow the exact-rational brute force
+    (IEEE division with gradual underflow, ties to the lower code)."""
+    rng = np.random.default_rng(21)
+    blocks = []
+    for scale in (1e-30, 1.5e-38, 1e-40, 1e-44):
+        b = (rng.standard_normal(64) * scale).astype(np.float32)
+        blocks.append(b)
+    tiny = np.zeros(64, np.float32)
+    tiny[0] = np.float32(2.0 ** -149)     # absmax = the smallest subnormal
+    tiny[1] = -np.float32(2.0 ** -149)    # v = -1 exactly
+    blocks.append(tiny)
+    mixed = np.zeros(64, np.float32)
+    mixed[0] = np.float32(1.0)
+    mixed[1:8] = np.array([1e-40, -1e-40, 2.0 ** -149, 1e-45, -3e-39, 1e-38, 5e-39], np.float32)
+    mixed[8:64] = (rng.standard_normal(56) * 1e-3).astype(np.float32)
+    blocks.append(mixed)
+    big = (rng.standard_normal(64) * 1e30).astype(np.float32)  # large but finite
+    blocks.append(big)
+    w = np.concatenate(blocks)
+    packed, absmax = nf4.quantize_nf4(w)
+    codes, amax = brute_force_codes(w)
+    assert np.array_equal(packed, pack_ref(codes))
+    assert [Fraction(float(a)) for a in absmax] == amax
+    assert absmax[4] == np.float32(2.0 ** -149)
+    got = nf4.unpack_codes(packed)
+    assert got[4 * 64] == 15 and got[4 * 64 + 1] == 0   # +-c of the subnormal block
 
 
 def test_heavy_tailed_and_ragged_tail():
@@ -191,15 +223,14 @@ def test_blocks_are_independent():
 
 def test_nf4_beats_uniform_int4_on_normal_weights():
     # [kwkr] §2.1-2.2: a uniform 16-level grid wastes levels on normal data;
-    # the quantile grid loses less.  The uniform baseline is the symmetric
-    # absmax/7 int4 scheme shown in [czcl] §2.1.
+    # the quantile grid loses less.  The uniform baseline is the oracle's
+    # symmetric 15-level strawman of [czcl] §2.1 (pinned by hand-worked
+    # blocks in test_oracle_codebooks.py).
     rng = np.random.default_rng(0)
     w = (rng.standard_normal(64 * 4096) * 0.02).astype(np.float32)
     packed, absmax = nf4.quantize_nf4(w)
     w_nf4 = nf4.dequantize(packed, absmax, w.size)
-    blocks = w.reshape(-1, 64).astype(np.float64)
-    scale = np.abs(blocks).max(1, keepdims=True) / 7.0
-    w_int4 = (np.clip(np.round(blocks / scale), -7, 7) * scale).ravel()
+    w_int4 = codebooks.int4_uniform_roundtrip(w)
     mse_nf4 = np.mean((w_nf4 - w) ** 2)
     mse_int4 = np.mean((w_int4 - w) ** 2)
     assert mse_nf4 < mse_int4
