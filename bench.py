@@ -362,13 +362,12 @@ def main():
         L["dA"] = torch.empty((RANK, K), dtype=torch.float32, device=dev)
         L["dB"] = torch.empty((N, RANK), dtype=torch.float32, device=dev)
         ws_b = max(qn.qn_workspace_bytes(op, M_TRAIN, N, K, RANK) for op in (0, 1, 2))
-        L["ws"] = torch.empty(ws_b, dtype=torch.uint8, device=dev)
+        L["ws"] = qn.workspace(ws_b, dev)
         # decode: distinct quantised copies (Infinity Cache defeat), own workspace
         ncopy = int(np.ceil(ROTATE_BYTES / (N * K * BYTES_PER_WEIGHT)))
         L["copies"] = [qn.quantize_weight(L["W"]) for _ in range(ncopy)]
         L["ydec"] = {m: torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in DECODE_M}
-        L["wsdec"] = torch.empty(qn.qn_workspace_bytes(0, max(DECODE_M), N, K, RANK),
-                                 dtype=torch.uint8, device=dev)
+        L["wsdec"] = qn.workspace(qn.qn_workspace_bytes(0, max(DECODE_M), N, K, RANK), dev)
         layers.append(L)
     torch.cuda.synchronize()
 

@@ -257,11 +257,15 @@ def qn_workspace_bytes(op, M, N, K, r):
     return int(load_library().qn_workspace_bytes(op, M, N, K, r))
 
 
+def workspace(nbytes, device):
+    """A uint8 device workspace of nbytes for the linear ops."""
+    return _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+
+
 def _workspace(op, M, N, K, r, ws, device):
-    torch = _torch()
     need = qn_workspace_bytes(op, M, N, K, r)
     if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        ws = workspace(need, device)
     return ws, (0 if ws is None else ws.numel())
 
 

@@ -64,8 +64,6 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   return QN_OK;
 }
 
-// Forward workspace: fp32 u (up to 16 partial sums of it on the decode
-// path) followed by bf16(s u).
 // fp32 partial sums of u (or t) over L-slices: up to kDecodeMaxSlices of
 // them on the decode path, kWideMaxSlices for token batches.
 size_t lora_part_bytes(int64_t M, int32_t r) {
@@ -163,12 +161,11 @@ int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M,
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
   // u = x A^T as fp32 partial sums over L-slices, added up (in slice order)
   // by the GEMV or GEMM that applies the LoRA-up term
-  float* u32 = nullptr;
+  float* u32 = static_cast<float*>(ws);
   const bool decode = M <= kGemvMaxM;
   const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K))
                         : qn::skinny_wide_splits(M, w->K);
   if (r > 0) {
-    u32 = static_cast<float*>(ws);
     if (qn::launch_skinny(xa, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s) != hipSuccess)
       return QN_ERR_HIP;
   }
@@ -212,9 +209,10 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
   const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
   const int ks = qn::skinny_wide_splits(mp, w->N);
   if (r > 0) {
-    float* t32 = static_cast<float*>(ws);
-    ts = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r));
-    uint16_t* bt = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(mp, r) +
+    char* base = static_cast<char*>(ws);
+    float* t32 = reinterpret_cast<float*>(base);
+    ts = reinterpret_cast<uint16_t*>(base + lora_part_bytes(mp, r));
+    uint16_t* bt = reinterpret_cast<uint16_t*>(base + lora_part_bytes(mp, r) +
                                                lora_bf16_bytes(M, r));
     if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
     if (qn::launch_skinny(dy, M, w->N, bt, r, scale, t32, nullptr, nullptr, ks, s) != hipSuccess)

@@ -192,20 +192,22 @@ __global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restri
 }
 
 // ---------------------------------------------------------------------------
-// Dequant-GEMV.  One workgroup of kWaves waves per band of 16 output
-// features (rows of W).  Wave w owns a contiguous slice of at most kS
-// blocks of the band's K range (longer rows take several passes) and issues
-// all of its weight loads (8 bytes per lane per block) and block constants
-// before anything else.  x is read per block, kXAhead blocks ahead (it is
-// small and L2-resident).  The LoRA inputs (u as `usplit` fp32 partial
-// sums [usplit][M][r], and the band's 16 rows of B) are loaded at the start
-// with plain indexing and only consumed in the epilogue.  Partial sums meet
-// in LDS in a fixed order (bit-reproducible).
+// Dequant-GEMV, M <= 16 tokens.  One workgroup of kWaves waves per band of
+// 16 output features (rows of W).  Wave w owns a contiguous slice of at most
+// kS blocks of the band's K range (longer rows take several passes).  The
+// LoRA inputs (u as `usplit` fp32 partial sums [usplit][M][r], and the
+// band's 16 rows of B) are loaded at the start and only consumed in the
+// epilogue.  Partial sums meet in LDS in a fixed order (bit-reproducible).
 //
-// Everything before the weight loads is kept to a few instructions: at
-// these sizes the whole matrix is in flight within a microsecond or two,
-// so every serial step (a division in address arithmetic, an LDS round trip
-// per block) shows up directly in the kernel time.
+// What paces a decode call (measured with per-wave timestamps): every
+// wave's weight loads are issued into a memory system that is already
+// saturated, so issuing them stalls for microseconds, and any work placed
+// behind the loads in program order (a table fill, a barrier) waits that
+// long.  The table is therefore built and published before the first load;
+// all loads of a slice are then issued in a pinned order (x, constants,
+// weights, with scheduling barriers so the compiler cannot move a use of a
+// late load ahead of an early one), and the walk waits for one block at a
+// time, so decoding overlaps the rest of the stream.
 struct GemvArgs {
   const uint8_t* packed;
   const uint8_t* qscale;
@@ -213,7 +215,7 @@ struct GemvArgs {
   const float* absmax;
   int64_t N, K;
   const uint16_t* x;
-  const float* u;
+  const float* u;   // usplit fp32 partial sums [usplit][M][r] of x A^T
   const uint16_t* B;
   uint16_t* y;
   uint16_t* u_out;
@@ -221,251 +223,91 @@ struct GemvArgs {
   float s;
 };
 
-// kXM: token rows of x staged in LDS per wave (1; 0: no staging, x
-// read per block from memory into a register ring).  kCopiesT: pair-table
-// copies, 64 for 16-wave workgroups (entry address (e << 8) | 4 lane is one
-// v_perm), else 32 (LDS for several workgroups per CU).
-template <int kWaves, int kS, bool kDQ, int kXM>
-__global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, const CodeParams P) {
+// The decode's LDS tables: kCopiesT interleaved copies of the 256-entry
+// byte table (entry e = (bf16(q[e >> 4]), bf16(q[e & 15])), the even
+// element first) and the 256 level-2 values.  uint4 f of the table holds
+// entry f / (kCopiesT / 4), copies 4 (f % (kCopiesT / 4)) .. + 3; for f =
+// tid + i kThreads the odd element (low nibble, e & 15) is fixed per thread
+// and the even element (e >> 4) is wave-uniform.
+template <int kCopiesT, int kThreads>
+__device__ __forceinline__ void gemv_tables(uint32_t* stab, float* sl8, const CodeParams& P,
+                                            int tid) {
+  const CodeRegs R = code_regs(P);
+  constexpr int kPer = kCopiesT / 4;  // uint4 per entry
+  const int e_hi0 = __builtin_amdgcn_readfirstlane(tid / (16 * kPer));
+  constexpr int kFill = 256 * kCopiesT / 4 / kThreads;
+  const float q_odd = code_value(R, static_cast<uint32_t>((tid / kPer) & 15));
+#pragma unroll
+  for (int i = 0; i < kFill; ++i) {
+    const uint32_t wv = pack_bf16x2(
+        code_value_uniform(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
+    reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
+  }
+  for (int i = tid; i < 256; i += kThreads) sl8[i] = l2_value(static_cast<uint32_t>(i), P.fp8);
+}
+
+// Pair of bf16 code values of byte `byte` of `word` from lane `lane`'s copy
+// of the table (lane4 = 4 lane).  With 64 copies the entry address
+// (e << 8) | 4 lane is a single byte permute.
+template <int kCopiesT>
+__device__ __forceinline__ uint32_t pair_lookup(const uint32_t* stab, uint32_t word, int byte,
+                                                uint32_t lane4) {
+  uint32_t addr;
+  if constexpr (kCopiesT == 64) {
+    addr = __builtin_amdgcn_perm(word, lane4, 0x0C0C0400u + (static_cast<uint32_t>(byte) << 8));
+  } else {
+    addr = (((word >> (8 * byte)) & 0xFFu) << 7) | (lane4 & 0x7Cu);
+  }
+  return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(stab) + addr);
+}
+
+// Workgroup barrier for LDS data only: waits for this wave's LDS stores,
+// not for its loads in flight (a __syncthreads() also waits for those),
+// and keeps the compiler from scheduling anything across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// LoRA inputs of the epilogue.  u arrives as usplit partial sums
+// [usplit][M][r]: thread t works on element e = t % (M r) for slices sg,
+// sg + G, .. (sg = t / (M r), G = threads / (M r) groups), kUParts of them
+// at most (the host keeps usplit <= G kUParts).  Unused slots read slice 0
+// and are masked when summed.  With M r > threads, elements >= threads are
+// summed from memory later.
+template <int kThreads, int kBPer, int kUParts>
+__device__ __forceinline__ void gemv_lora_loads(const GemvArgs& a, int64_t n0, int tid,
+                                                uint32_t (&bt)[kBPer], float (&upart)[kUParts]) {
+  const int r = a.r, mr = a.M * a.r;
+  const int nbt = 16 * r;
+#pragma unroll
+  for (int q = 0; q < kBPer; ++q) {
+    const int e = tid + q * kThreads;
+    bt[q] = a.B[n0 * r + (e < nbt ? e : (nbt > 0 ? nbt - 1 : 0))];
+  }
+  const int ugroups = mr > 0 && mr <= kThreads ? kThreads / mr : 1;
+  const int ue = mr > 0 ? tid % mr : 0, ug = mr > 0 ? tid / mr : 0;
+  const float* ut = a.u + (ug < ugroups ? ue : 0);
+#pragma unroll
+  for (int q = 0; q < kUParts; ++q) {
+    const int sl = ug + q * ugroups;
+    upart[q] = ut[static_cast<int64_t>(sl < a.usplit && ug < ugroups ? sl : 0) * mr];
+  }
+}
+
+// Epilogue: the waves' partial sums meet in LDS in a fixed order, u is
+// summed from its partials (fixed order), and s u B^T is added to the band.
+// The LoRA inputs are loaded here, after the weight stream, so no register
+// holds them during the walk.  The table memory holds u and the band's B
+// rows once every wave is done with the table (the first barrier below).
+template <int kWaves, int kUParts>
+__device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const f32x4_t& acc,
+                                              float (*spart)[16][17], uint32_t* stab, int tid) {
   constexpr int kThreads = kWaves * 64;
-  constexpr int kCopiesT = kWaves == 16 ? 64 : 32;
-  constexpr int kTabWords = 256 * kCopiesT;
-  constexpr int kBPer = (16 * 128 + kThreads - 1) / kThreads;  // B-tile elements per thread
-  constexpr bool kXL = kXM > 0;
-  // staged x per wave: [token m < kXM][block i < kS][64 bf16]
-  constexpr int kXBytes = kXL ? kXM * kS * 128 : 16;
-  constexpr int kXPer = kXL ? (kXM * kS * 8 + 63) / 64 : 1;  // 16-byte chunks per lane
-  // Pair table during the walk; afterwards the same memory holds u and the
-  // band's B rows for the epilogue.
-  __shared__ __attribute__((aligned(16))) uint32_t stab[kTabWords];
-  __shared__ float sl8[256];
-  __shared__ float spart[kWaves][16][17];
-  __shared__ __attribute__((aligned(16))) char sx[kXL ? kWaves * kXBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint4 sxz[kXL ? kS * 8 + 8 : 1];  // zeros
-  // epilogue: su [M r <= 2048] + sB [16 r <= 2048 bf16] + group sums [<= 1024]
-  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2 + 1024, "epilogue buffers must fit");
-
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nl = lane & 15, g = lane >> 4;
-  const int64_t K = a.K, nblk = K >> 6;
-  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
-  const int64_t n = n0 + nl;
+  constexpr int kBPer = (16 * 128 + kThreads - 1) / kThreads;
+  const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, g = lane >> 4;
   const int M = a.M, r = a.r, mr = M * r, usplit = a.usplit;
-
-  // -- LoRA inputs (consumed only in the epilogue) --
-  // Issued without any branch (a branch join would wait for them); with
-  // r == 0 the host points B and u at valid memory and element 0 is read.
-  // u arrives as usplit partial sums [usplit][M][r].  Thread t works on
-  // element e = t % (M r) for slices sg, sg + G, sg + 2 G, .. (sg = t / (M r),
-  // G = threads / (M r) groups), kUParts of them at most: the host keeps
-  // usplit <= G kUParts.  Unused slots read slice 0 and are masked in the
-  // epilogue, which sums each thread's slots, then the groups, in a fixed
-  // order.  With M r > threads, elements >= threads are summed from memory
-  // in the epilogue.
-  uint32_t bt[kBPer];  // 32-bit so the compiler does not pack them (that waits on the loads)
-  float upart[kUParts];
-  {
-    const int nbt = 16 * r;
-#pragma unroll
-    for (int q = 0; q < kBPer; ++q) {
-      const int e = tid + q * kThreads;
-      bt[q] = a.B[n0 * r + (e < nbt ? e : (nbt > 0 ? nbt - 1 : 0))];
-    }
-    const int ugroups = mr > 0 && mr <= kThreads ? kThreads / mr : 1;
-    const int ue = mr > 0 ? tid % mr : 0, ug = mr > 0 ? tid / mr : 0;
-    const float* ut = a.u + (ug < ugroups ? ue : 0);
-#pragma unroll
-    for (int q = 0; q < kUParts; ++q) {
-      const int sl = ug + q * ugroups;
-      upart[q] = ut[static_cast<int64_t>(sl < usplit && ug < ugroups ? sl : 0) * mr];
-    }
-  }
-
-  // Weight loads: lane l reads 8 bytes of row n0 + l / 4 at byte 8 (l % 4)
-  // of the block, so each group of 4 consecutive lanes reads 32 contiguous
-  // bytes (one row's block); ds_bpermute then moves them to the MFMA lane
-  // (row l % 16, byte group l / 16), i.e. from lane 4 (l % 16) + l / 16.
-  // (Loading in MFMA lane order directly, consecutive lanes in different
-  // rows, streams about a third slower.)
-  const uint8_t* wrow = a.packed + (n0 + (lane >> 2)) * (K >> 1) + 8 * (lane & 3);
-  const int wperm = ((lane & 15) * 4 + (lane >> 4)) * 4;
-  // Token rows >= M: the ring path reads row M - 1 and zeroes the value;
-  // the staged path reads a zero region.
-  const bool xvalid = nl < M;
-  const int xm = xvalid ? nl : M - 1;
-  const uint16_t* xrow = a.x + static_cast<int64_t>(xm) * K + 16 * g;
-  const int64_t rowblk0 = n * nblk;
-  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
-  char* sxw = sx + (kXL ? wave * kXBytes : 0);
-  const char* xbase = kXL ? (xvalid ? sxw + xm * (kS * 128) + g * 32
-                                    : reinterpret_cast<const char*>(sxz) + g * 32)
-                          : nullptr;
-  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
-  f32x4_t acc = zero;
-
-  const int64_t per_pass = static_cast<int64_t>(kWaves) * kS;
-  for (int64_t p0 = 0; p0 < nblk; p0 += per_pass) {
-    const int64_t pn = min(per_pass, nblk - p0);
-    const int64_t b_lo = p0 + pn * wave / kWaves;  // <= nblk - 1 even for an empty slice
-    const int nb = static_cast<int>(p0 + pn * (wave + 1) / kWaves - b_lo);
-    const int nbc = nb > 0 ? nb - 1 : 0;
-
-    // 1. tables (first pass only): the barrier they need comes before the
-    // loads of the slice, so no wave then waits for another wave's loads
-    if (p0 == 0) {
-      // uint4 f of the table holds entry f / (kCopiesT / 4), copies
-      // 4 (f % (kCopiesT / 4)) .. + 3; for f = tid + i kThreads the odd
-      // element (low nibble, e & 15) is fixed per thread and the even
-      // element (e >> 4) is wave-uniform.
-      const CodeRegs R = code_regs(P);
-      constexpr int kPer = kCopiesT / 4;  // uint4 per entry
-      const int e_hi0 = __builtin_amdgcn_readfirstlane(tid / (16 * kPer));
-      constexpr int kFill = kTabWords / 4 / kThreads;
-      const float q_odd = code_value(R, static_cast<uint32_t>((tid / kPer) & 15));
-#pragma unroll
-      for (int i = 0; i < kFill; ++i) {
-        const uint32_t wv = pack_bf16x2(
-            code_value_uniform(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
-        reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
-      }
-      for (int i = tid; i < 256; i += kThreads) sl8[i] = l2_value(static_cast<uint32_t>(i), P.fp8);
-      if constexpr (kXL)
-        for (int i = tid; i < kS * 8 + 8; i += kThreads) sxz[i] = make_uint4(0, 0, 0, 0);
-      __syncthreads();
-    }
-
-    // 2. x of the slice into registers (staged path): 16-byte chunk c of
-    // the wave's [m][i][128 B] staging area; rows >= M and blocks past the
-    // slice re-read valid data and are never used.
-    uint4 xs[kXPer];
-    int xc[kXPer];
-    if constexpr (kXL) {
-#pragma unroll
-      for (int q = 0; q < kXPer; ++q) {
-        int c = lane + 64 * q;
-        c = c < kXM * kS * 8 ? c : kXM * kS * 8 - 1;
-        xc[q] = c;
-        const int cm = c / (kS * 8), ci = (c >> 3) % kS;
-        const int64_t m = cm < M ? cm : M - 1;
-        const int64_t bi = b_lo + (ci < nbc ? ci : nbc);
-        xs[q] = *reinterpret_cast<const uint4*>(a.x + m * K + bi * 64 + (c & 7) * 8);
-      }
-    }
-
-    // 3. block constants and all weight loads of this wave's slice
-    const int64_t qb = rowblk0 + b_lo;  // index of the slice's first block constant
-    constexpr int kQD = kS / 4 + 1;
-    uint32_t qd[kQD];
-    float cq[kDQ ? 1 : kS];
-    float g_lo = 0.f, g_hi = 0.f;
-    if constexpr (kDQ) {
-      // 8-bit constants of the slice: aligned dwords covering
-      // [qb, qb + kS); the total count N K / 64 is a multiple of 4, so the
-      // clamp keeps every dword inside the array.
-      const uint32_t* q32 = reinterpret_cast<const uint32_t*>(a.qscale);
-      const int64_t dmax = ((a.N * nblk) >> 2) - 1;
-#pragma unroll
-      for (int j = 0; j < kQD; ++j) {
-        const int64_t d = (qb >> 2) + j;
-        qd[j] = q32[d < dmax ? d : dmax];
-      }
-      g_lo = a.gscale[qb >> 8];
-      g_hi = a.gscale[(qb + nbc) >> 8];
-    } else {
-#pragma unroll
-      for (int i = 0; i < kS; ++i) cq[i] = a.absmax[qb + (i < nbc ? i : nbc)];
-    }
-    uint2 w[kS];
-#pragma unroll
-    for (int i = 0; i < kS; ++i)
-      w[i] = *reinterpret_cast<const uint2*>(wrow + (b_lo + (i < nbc ? i : nbc)) * 32);
-
-    // 4. x: staged slice to LDS (read back only by this wave), or the
-    // first blocks of the register ring
-    uint4 xr[kXL ? 1 : kXAhead + 1][2];
-    auto load_x = [&](int i) {
-      if constexpr (!kXL) {
-        const int ic = i < nbc ? i : nbc;
-        const uint4* xp = reinterpret_cast<const uint4*>(xrow + (b_lo + ic) * 64);
-        xr[i % (kXAhead + 1)][0] = xp[0];
-        xr[i % (kXAhead + 1)][1] = xp[1];
-      }
-    };
-    if constexpr (kXL) {
-#pragma unroll
-      for (int q = 0; q < kXPer; ++q) *reinterpret_cast<uint4*>(sxw + xc[q] * 16) = xs[q];
-    } else {
-#pragma unroll
-      for (int i = 0; i < kXAhead; ++i) load_x(i);
-    }
-    auto x_of = [&](int i, int h) -> uint4 {
-      if constexpr (kXL) {
-        return *reinterpret_cast<const uint4*>(xbase + i * 128 + h * 16);
-      } else {
-        const uint4 v = xr[i % (kXAhead + 1)][h];
-        return xvalid ? v : make_uint4(0, 0, 0, 0);
-      }
-    };
-
-    // 5. block constants c' of every block of the slice (one LDS round trip)
-    float cs[kS];
-    if constexpr (kDQ) {
-      const uint32_t sh = static_cast<uint32_t>(qb & 3);
-      const int gfirst = static_cast<int>(qb & 255);
-#pragma unroll
-      for (int j = 0; j < kS / 4; ++j) {
-        const uint32_t al = __builtin_amdgcn_alignbyte(qd[j + 1], qd[j], sh);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i = 4 * j + b;
-          const float c = __fmul_rn(sl8[(al >> (8 * b)) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
-          cs[i] = i < nb ? c : 0.f;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kS; ++i) cs[i] = i < nb ? cq[i] : 0.f;
-    }
-
-    // 6. walk the slice; the pair lookups of block i + 1 are issued before
-    // the MFMAs of block i.  No control flow: blocks past the slice (the
-    // last wave of an uneven split) re-read valid data and have c' = 0 (a
-    // branch here lets the compiler sink the weight loads into it).
-    auto look = [&](uint32_t word, int byte) -> uint32_t {
-      uint32_t addr;
-      if constexpr (kCopiesT == 64) {
-        // bytes [4 lane, e, 0, 0]: (e << 8) | 4 lane
-        addr = __builtin_amdgcn_perm(word, lane4, 0x0C0C0400u + (static_cast<uint32_t>(byte) << 8));
-      } else {
-        addr = (((word >> (8 * byte)) & 0xFFu) << 7) | (lane4 & 0x7Cu);
-      }
-      return *reinterpret_cast<const uint32_t*>(reinterpret_cast<const char*>(stab) + addr);
-    };
-    uint4 d[kS][2];
-#pragma unroll
-    for (int i = 0; i < kS; ++i) {
-      const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].x)));
-      const uint32_t w1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].y)));
-      d[i][0] = make_uint4(look(w0, 0), look(w0, 1), look(w0, 2), look(w0, 3));
-      d[i][1] = make_uint4(look(w1, 0), look(w1, 1), look(w1, 2), look(w1, 3));
-      if (i > 0) {
-        f32x4_t t = mfma16(x_of(i - 1, 0), d[i - 1][0], zero);
-        t = mfma16(x_of(i - 1, 1), d[i - 1][1], t);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[i - 1], t[v], acc[v]);
-      }
-      load_x(i + kXAhead);
-    }
-    {
-      f32x4_t t = mfma16(x_of(kS - 1, 0), d[kS - 1][0], zero);
-      t = mfma16(x_of(kS - 1, 1), d[kS - 1][1], t);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[kS - 1], t[v], acc[v]);
-    }
-  }
-
-  // -- epilogue --
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
 #pragma unroll
   for (int v = 0; v < 4; ++v) spart[wave][4 * g + v][nl] = acc[v];
   __syncthreads();  // every wave is done with the pair table
@@ -473,6 +315,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   uint16_t* sB = reinterpret_cast<uint16_t*>(stab + 16 * 128);  // [16][r] bf16
   float* sug = reinterpret_cast<float*>(stab + 16 * 128 + 16 * 128 / 2);  // [groups][M r]
   if (r > 0) {
+    uint32_t bt[kBPer];
+    float upart[kUParts];
+    gemv_lora_loads<kThreads, kBPer, kUParts>(a, n0, tid, bt, upart);
     const int ugroups = mr <= kThreads ? kThreads / mr : 1;
     const int ue = tid % mr, ug = tid / mr;
     if (ug < ugroups) {
@@ -500,8 +345,8 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
       for (int gq = 0; gq < ugroups; ++gq) v += sug[gq * mr + tid];
       su[tid] = v;
     }
+    __syncthreads();
   }
-  __syncthreads();
   if (a.u_out && blockIdx.x == 0)
     for (int i = tid; i < mr; i += kThreads)
       a.u_out[i] = static_cast<uint16_t>(pack_bf16x2(su[i], 0.f) & 0xFFFF);
@@ -519,17 +364,335 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_kernel(const GemvArgs a, con
   }
 }
 
-// One GEMV configuration: the single token row staged in LDS (xmode 1), or
-// the register ring.
+// Register-ring GEMV for 2 <= M <= 16 tokens: x is read per block from
+// memory into a register ring kXAhead blocks ahead (x of 16 tokens is too
+// large to stage in LDS per wave).  Rows >= M read row M - 1 and are
+// zeroed.
+template <int kWaves, int kS, bool kDQ>
+__global__ __launch_bounds__(kWaves * 64) void gemv_ring_kernel(const GemvArgs a, const CodeParams P) {
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kCopiesT = kWaves == 16 ? 64 : 32;
+  constexpr int kTabWords = 256 * kCopiesT;
+  constexpr int kQD = (kS + 3) / 4 + 1;  // dwords covering constant bytes sh .. sh + kS - 1, sh < 4
+  // Pair table during the walk; afterwards the same memory holds u and the
+  // band's B rows for the epilogue.
+  __shared__ __attribute__((aligned(16))) uint32_t stab[kTabWords];
+  __shared__ float sl8[256];
+  __shared__ float spart[kWaves][16][17];
+  // epilogue: su [M r <= 2048] + sB [16 r <= 2048 bf16] + group sums [<= 1024]
+  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2 + 1024, "epilogue buffers must fit");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t K = a.K, nblk = K >> 6;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+  const int M = a.M;
+
+  // tables first, published before any load is in flight
+  gemv_tables<kCopiesT, kThreads>(stab, sl8, P, tid);
+  lds_barrier();
+
+  // Weight loads: lane l reads 8 bytes of row n0 + l / 4 at byte 8 (l % 4)
+  // of the block, so each group of 4 consecutive lanes reads 32 contiguous
+  // bytes (one row's block); ds_bpermute then moves them to the MFMA lane
+  // (row l % 16, byte group l / 16), i.e. from lane 4 (l % 16) + l / 16.
+  // (Loading in MFMA lane order directly, consecutive lanes in different
+  // rows, streams about a third slower.)
+  const uint8_t* wrow = a.packed + (n0 + (lane >> 2)) * (K >> 1) + 8 * (lane & 3);
+  const int wperm = ((lane & 15) * 4 + (lane >> 4)) * 4;
+  const bool xvalid = nl < M;
+  const int xm = xvalid ? nl : M - 1;
+  const uint16_t* xrow = a.x + static_cast<int64_t>(xm) * K + 16 * g;
+  const int64_t rowblk0 = (n0 + nl) * nblk;
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = zero;
+
+  const int64_t per_pass = static_cast<int64_t>(kWaves) * kS;
+  for (int64_t p0 = 0; p0 < nblk; p0 += per_pass) {
+    const int64_t pn = min(per_pass, nblk - p0);
+    const int64_t b_lo = p0 + pn * wave / kWaves;  // <= nblk - 1 even for an empty slice
+    const int nb = static_cast<int>(p0 + pn * (wave + 1) / kWaves - b_lo);
+    const int nbc = nb > 0 ? nb - 1 : 0;
+
+    // block constants and all weight loads of this wave's slice
+    const int64_t qb = rowblk0 + b_lo;  // index of the slice's first block constant
+    uint32_t qd[kQD];
+    float cq[kDQ ? 1 : kS];
+    float g_lo = 0.f, g_hi = 0.f;
+    if constexpr (kDQ) {
+      // 8-bit constants of the slice: aligned dwords covering
+      // [qb, qb + kS); the total count N K / 64 is a multiple of 4, so the
+      // clamp keeps every dword inside the array.
+      const uint32_t* q32 = reinterpret_cast<const uint32_t*>(a.qscale);
+      const int64_t dmax = ((a.N * nblk) >> 2) - 1;
+#pragma unroll
+      for (int j = 0; j < kQD; ++j) {
+        const int64_t d = (qb >> 2) + j;
+        qd[j] = q32[d < dmax ? d : dmax];
+      }
+      g_lo = a.gscale[qb >> 8];
+      g_hi = a.gscale[(qb + nbc) >> 8];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS; ++i) cq[i] = a.absmax[qb + (i < nbc ? i : nbc)];
+    }
+    uint2 w[kS];
+#pragma unroll
+    for (int i = 0; i < kS; ++i)
+      w[i] = *reinterpret_cast<const uint2*>(wrow + (b_lo + (i < nbc ? i : nbc)) * 32);
+
+    // the first blocks of the x ring
+    uint4 xr[kXAhead + 1][2];
+    auto load_x = [&](int i) {
+      const int ic = i < nbc ? i : nbc;
+      const uint4* xp = reinterpret_cast<const uint4*>(xrow + (b_lo + ic) * 64);
+      xr[i % (kXAhead + 1)][0] = xp[0];
+      xr[i % (kXAhead + 1)][1] = xp[1];
+    };
+#pragma unroll
+    for (int i = 0; i < kXAhead; ++i) load_x(i);
+    auto x_of = [&](int i, int h) -> uint4 {
+      const uint4 v = xr[i % (kXAhead + 1)][h];
+      return xvalid ? v : make_uint4(0, 0, 0, 0);
+    };
+
+    // block constants c' of every block of the slice (one LDS round trip)
+    float cs[kS];
+    if constexpr (kDQ) {
+      const uint32_t sh = static_cast<uint32_t>(qb & 3);
+      const int gfirst = static_cast<int>(qb & 255);
+#pragma unroll
+      for (int j = 0; j < (kS + 3) / 4; ++j) {
+        const uint32_t al = __builtin_amdgcn_alignbyte(qd[j + 1], qd[j], sh);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int i = 4 * j + b;
+          if (i < kS) {
+            const float c = __fmul_rn(sl8[(al >> (8 * b)) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
+            cs[i] = i < nb ? c : 0.f;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS; ++i) cs[i] = i < nb ? cq[i] : 0.f;
+    }
+
+    // walk the slice; the pair lookups of block i + 1 are issued before
+    // the MFMAs of block i.  No control flow: blocks past the slice (the
+    // last wave of an uneven split) re-read valid data and have c' = 0 (a
+    // branch here lets the compiler sink the weight loads into it).
+    auto look = [&](uint32_t word, int byte) -> uint32_t {
+      return pair_lookup<kCopiesT>(stab, word, byte, lane4);
+    };
+    uint4 d[kS][2];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].x)));
+      const uint32_t w1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].y)));
+      d[i][0] = make_uint4(look(w0, 0), look(w0, 1), look(w0, 2), look(w0, 3));
+      d[i][1] = make_uint4(look(w1, 0), look(w1, 1), look(w1, 2), look(w1, 3));
+      if (i > 0) {
+        f32x4_t t = mfma16(x_of(i - 1, 0), d[i - 1][0], zero);
+        t = mfma16(x_of(i - 1, 1), d[i - 1][1], t);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[i - 1], t[v], acc[v]);
+      }
+      load_x(i + kXAhead);
+    }
+    {
+      f32x4_t t = mfma16(x_of(kS - 1, 0), d[kS - 1][0], zero);
+      t = mfma16(x_of(kS - 1, 1), d[kS - 1][1], t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(cs[kS - 1], t[v], acc[v]);
+    }
+  }
+
+  gemv_epilogue<kWaves, kUParts>(a, acc, spart, stab, tid);
+}
+
+// Staged GEMV for one token (M == 1).  The 16 x kS x 64 x-values of a wave's
+// slice are copied to that wave's LDS region once per pass; in the walk only
+// the four lanes that hold token row 0 of the MFMA's x operand read them
+// (the other rows of the product are never stored), so x costs no vector
+// memory bandwidth per block.  Loads of a pass, in issue order: the x slice,
+// the 8-bit block constants (aligned dwords covering the slice) and group
+// constants, then the weights block by block; the walk waits for one more
+// block per step.
+template <int kWaves, int kS, bool kDQ>
+__global__ __launch_bounds__(kWaves * 64) void gemv1_kernel(const GemvArgs a, const CodeParams P) {
+  constexpr int kThreads = kWaves * 64;
+  constexpr int kCopiesT = kWaves == 16 ? 64 : 32;
+  constexpr int kTabWords = 256 * kCopiesT;
+  constexpr int kXBytes = kS * 128;                            // a wave's x slice
+  constexpr int kXPer = (kS * 8 + 63) / 64;                    // its 16-byte chunks per lane
+  constexpr int kQD = (kS + 3) / 4 + 1;  // dwords covering constant bytes sh .. sh + kS - 1, sh < 4
+  // the waves' partial sums share memory with the x staging area, which is
+  // free once the walk has ended
+  constexpr int kXAll = kWaves * kXBytes > kWaves * 16 * 17 * 4 ? kWaves * kXBytes : kWaves * 16 * 17 * 4;
+  __shared__ __attribute__((aligned(16))) uint32_t stab[kTabWords];
+  __shared__ float sl8[256];
+  __shared__ __attribute__((aligned(16))) char sx[kXAll];
+  float (*spart)[16][17] = reinterpret_cast<float (*)[16][17]>(sx);
+  static_assert(kTabWords >= 16 * 128 + 16 * 128 / 2 + 1024, "epilogue buffers must fit");
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nl = lane & 15, g = lane >> 4;
+  const int64_t K = a.K, nblk = K >> 6;
+  const int64_t n0 = static_cast<int64_t>(blockIdx.x) * 16;
+
+  // 1. tables, published before any load is in flight
+  gemv_tables<kCopiesT, kThreads>(stab, sl8, P, tid);
+  lds_barrier();
+
+  // the band's 16 rows as a buffer: lane offset in a VGPR, block offset
+  // (wave-uniform) in an SGPR, so a slice's loads need no 64-bit addresses
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.packed + n0 * (K >> 1)), static_cast<short>(0),
+      static_cast<int>(16 * (K >> 1)), 0x00020000);
+  const int wlane = static_cast<int>((lane >> 2) * (K >> 1) + 8 * (lane & 3));
+  const int wperm = ((lane & 15) * 4 + (lane >> 4)) * 4;
+  const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
+  char* sxw = sx + wave * kXBytes;
+  const char* xb = sxw + g * 32;
+  const bool xon = nl == 0;  // lanes holding token row 0 of the x operand
+  const f32x4_t zero = {0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = zero;
+
+  const int64_t per_pass = static_cast<int64_t>(kWaves) * kS;
+  for (int64_t p0 = 0; p0 < nblk; p0 += per_pass) {
+    const int64_t pn = min(per_pass, nblk - p0);
+    const int64_t b_lo = p0 + pn * wave / kWaves;  // <= nblk - 1 even for an empty slice
+    const int nb = static_cast<int>(p0 + pn * (wave + 1) / kWaves - b_lo);
+    const int nbc = nb > 0 ? nb - 1 : 0;
+    __builtin_amdgcn_sched_barrier(0);
+
+    // x slice: 16-byte chunk c of block c / 8 (blocks past the slice re-read
+    // a valid one and are never used)
+    uint4 xs[kXPer];
+    int xc[kXPer];
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) {
+      int c = lane + 64 * q;
+      c = c < kS * 8 ? c : kS * 8 - 1;
+      xc[q] = c;
+      const int ci = c >> 3;
+      xs[q] = *reinterpret_cast<const uint4*>(a.x + (b_lo + (ci < nbc ? ci : nbc)) * 64 + (c & 7) * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // block constants of row n0 + nl over the slice
+    const int64_t qb = (n0 + nl) * nblk + b_lo;
+    uint32_t qd[kQD];
+    float cq[kDQ ? 1 : kS];
+    float g_lo = 0.f, g_hi = 0.f;
+    if constexpr (kDQ) {
+      // aligned dwords covering [qb, qb + kS); the count N K / 64 is a
+      // multiple of 4, so the clamp keeps every dword inside the array
+      const uint32_t* q32 = reinterpret_cast<const uint32_t*>(a.qscale);
+      const int64_t dmax = ((a.N * nblk) >> 2) - 1;
+#pragma unroll
+      for (int j = 0; j < kQD; ++j) {
+        const int64_t d = (qb >> 2) + j;
+        qd[j] = q32[d < dmax ? d : dmax];
+      }
+      g_lo = a.gscale[qb >> 8];
+      g_hi = a.gscale[(qb + nbc) >> 8];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kS; ++i) cq[i] = a.absmax[qb + (i < nbc ? i : nbc)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // weights: lane l reads 8 bytes of row n0 + l / 4 at byte 8 (l % 4) of
+    // the block (four lanes cover a row's 32-byte block); ds_bpermute then
+    // moves them to the MFMA lane (row l % 16, byte group l / 16)
+    uint2 w[kS];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      const int boff = __builtin_amdgcn_readfirstlane(static_cast<int>((b_lo + (i < nbc ? i : nbc)) * 32));
+      w[i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(wr, wlane, boff, 0));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // x to this wave's LDS region (read back only by this wave); the empty
+    // asm keeps the stores, and their wait for x, behind the weight loads
+#pragma unroll
+    for (int q = 0; q < kXPer; ++q) {
+      asm volatile("" : "+v"(xs[q].x), "+v"(xs[q].y), "+v"(xs[q].z), "+v"(xs[q].w)::"memory");
+      *reinterpret_cast<uint4*>(sxw + xc[q] * 16) = xs[q];
+    }
+
+    // c' of block i of the slice, from the 8-bit constants in registers
+    // (blocks past the slice get 0)
+    const uint32_t sh = static_cast<uint32_t>(qb & 3);
+    const int gfirst = static_cast<int>(qb & 255);
+    auto cscale = [&](int i) -> float {
+      float c;
+      if constexpr (kDQ) {
+        const uint32_t al = __builtin_amdgcn_alignbyte(qd[i / 4 + 1], qd[i / 4], sh);
+        c = __fmul_rn(sl8[(al >> (8 * (i % 4))) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
+      } else {
+        c = cq[i];
+      }
+      return i < nb ? c : 0.f;
+    };
+    __builtin_amdgcn_sched_barrier(0);
+
+    // walk: decode block i + 1 (its lookups in flight) while block i multiplies
+    uint4 dcur[2], dnext[2];
+    auto decode = [&](int i, uint4 (&d)[2]) {
+      const uint32_t w0 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].x)));
+      const uint32_t w1 = static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute(wperm, static_cast<int>(w[i].y)));
+      d[0] = make_uint4(pair_lookup<kCopiesT>(stab, w0, 0, lane4), pair_lookup<kCopiesT>(stab, w0, 1, lane4),
+                        pair_lookup<kCopiesT>(stab, w0, 2, lane4), pair_lookup<kCopiesT>(stab, w0, 3, lane4));
+      d[1] = make_uint4(pair_lookup<kCopiesT>(stab, w1, 0, lane4), pair_lookup<kCopiesT>(stab, w1, 1, lane4),
+                        pair_lookup<kCopiesT>(stab, w1, 2, lane4), pair_lookup<kCopiesT>(stab, w1, 3, lane4));
+    };
+    uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+    decode(0, dcur);
+    float ccur = cscale(0), cnext = 0.f;
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      if (i + 1 < kS) {
+        decode(i + 1, dnext);
+        cnext = cscale(i + 1);
+      }
+      if (xon) {
+        x0 = *reinterpret_cast<const uint4*>(xb + i * 128);
+        x1 = *reinterpret_cast<const uint4*>(xb + i * 128 + 16);
+      }
+      f32x4_t t = mfma16(x0, dcur[0], zero);
+      t = mfma16(x1, dcur[1], t);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[v] = fmaf(ccur, t[v], acc[v]);
+      __builtin_amdgcn_sched_barrier(0);
+      dcur[0] = dnext[0];
+      dcur[1] = dnext[1];
+      ccur = cnext;
+    }
+  }
+  __syncthreads();  // the partial sums below overwrite the x staging area
+  gemv_epilogue<kWaves, kUParts>(a, acc, spart, stab, tid);
+}
+
+// One GEMV configuration: the staged kernel for one token, the register
+// ring above.
 template <int W, int S>
-void gemv_config(int xmode, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
+void gemv_config(int M, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
                  const CodeParams& P) {
-  if (xmode == 1) {
-    hipLaunchKernelGGL((gemv_kernel<W, S, true, 1>), grid, dim3(W * 64), 0, st, a, P);
+  if (M == 1) {
+    if (dq)
+      hipLaunchKernelGGL((gemv1_kernel<W, S, true>), grid, dim3(W * 64), 0, st, a, P);
+    else
+      hipLaunchKernelGGL((gemv1_kernel<W, S, false>), grid, dim3(W * 64), 0, st, a, P);
   } else if (dq) {
-    hipLaunchKernelGGL((gemv_kernel<W, S, true, 0>), grid, dim3(W * 64), 0, st, a, P);
+    hipLaunchKernelGGL((gemv_ring_kernel<W, S, true>), grid, dim3(W * 64), 0, st, a, P);
   } else {
-    hipLaunchKernelGGL((gemv_kernel<W, S, false, 0>), grid, dim3(W * 64), 0, st, a, P);
+    hipLaunchKernelGGL((gemv_ring_kernel<W, S, false>), grid, dim3(W * 64), 0, st, a, P);
   }
 }
 
@@ -558,10 +721,12 @@ int skinny_cols(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8; }
 }  // namespace
 
 int gemv_threads(int64_t N, int64_t K) {
-  int wv = 4;
-  while (wv < 16 && (N / 16) * wv * 2 <= 4096) wv *= 2;
+  // about 16-24 resident waves per CU in one round: 16 waves per band up
+  // to 384 bands, 8 up to 768, else 4 (11008 x 4096 at M = 1 ran about 10%
+  // faster with 8 waves than with 4)
+  const int64_t bands = N / 16;
   (void)K;
-  return wv * 64;
+  return (bands <= 384 ? 16 : bands <= 768 ? 8 : 4) * 64;
 }
 
 int skinny_splits(int64_t M, int64_t L, int r, int gemv_thr) {
@@ -635,7 +800,7 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   a.N = w.N;
   a.K = w.K;
   a.x = x;
-  // with r == 0 the kernel still reads element 0 of u and B (never used)
+  // with r == 0 the kernel reads neither; both still point at valid memory
   a.u = r > 0 ? u : reinterpret_cast<const float*>(x);
   a.B = r > 0 ? B : x;
   a.y = y;
@@ -646,23 +811,24 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   a.s = s;
   const int64_t nbands = w.N / 16, nblk = w.K >> 6;
   const dim3 grid(static_cast<uint32_t>(nbands));
-  // About 16 resident waves per CU in one round: waves per band from
-  // 4096 / bands (4, 8 or 16), blocks per wave the smallest of 4, 8, 12, 16
-  // that covers the row (longer rows: 16 per pass, several passes).
+  // Waves per band from gemv_threads; blocks per wave the smallest of 4, 8,
+  // 11, 12, 16 that covers the row (11: 172 blocks of a 11008-long row over
+  // 16 waves); longer rows take several passes of 16 (of 12 at 16 waves,
+  // where 16 x 16 would spill).
   const int wv = gemv_threads(w.N, w.K) / 64;
   const int64_t need = (nblk + wv - 1) / wv;
-  int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 12 ? 12 : 16;
-  if (wv == 16 && sb == 16) sb = 12;  // 16 x 16 would spill at 1024 threads
+  int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 11 ? 11 : need <= 12 ? 12 : 16;
+  if (wv == 16 && sb == 16) sb = 12;
+  // one token over 8 waves: two passes of 4 blocks rather than one of 8
+  // (the 8-block kernel needs 89 VGPRs, which allows two workgroups per CU
+  // instead of three; 11008 x 4096: 10.4 us against 10.9)
+  if (M == 1 && wv == 8 && sb == 8) sb = 4;
   const bool dq = w.qscale != nullptr;
-  // x staging: the one row for M == 1, the register ring above (also for
-  // M <= 4: staging four rows was 15% slower at 11008 x 4096, M = 4); the
-  // unscaled-constant path (no double quantisation) uses the ring.
-  const int xmode = !dq ? 0 : M == 1 ? 1 : 0;
 #define QN_GEMV(W, S) \
-  if (wv == W && sb == S) gemv_config<W, S>(xmode, dq, grid, st, a, P);
-  QN_GEMV(4, 4) QN_GEMV(4, 8) QN_GEMV(4, 12) QN_GEMV(4, 16)
-  QN_GEMV(8, 4) QN_GEMV(8, 8) QN_GEMV(8, 12) QN_GEMV(8, 16)
-  QN_GEMV(16, 4) QN_GEMV(16, 8) QN_GEMV(16, 12)
+  if (wv == W && sb == S) gemv_config<W, S>(M, dq, grid, st, a, P);
+  QN_GEMV(4, 4) QN_GEMV(4, 8) QN_GEMV(4, 11) QN_GEMV(4, 12) QN_GEMV(4, 16)
+  QN_GEMV(8, 4) QN_GEMV(8, 8) QN_GEMV(8, 11) QN_GEMV(8, 12) QN_GEMV(8, 16)
+  QN_GEMV(16, 4) QN_GEMV(16, 8) QN_GEMV(16, 11) QN_GEMV(16, 12)
 #undef QN_GEMV
   return hipGetLastError();
 }

@@ -21,7 +21,9 @@
  *     QN_ERR_HIP means a launch failed (hipGetLastError after the launch);
  *     outputs are then undefined.  No C++ exception crosses the ABI.
  *   - The library allocates no device memory.  Scratch space comes from a
- *     caller-provided workspace sized by qn_workspace_bytes().
+ *     caller-provided workspace sized by qn_workspace_bytes().  One
+ *     workspace serves every operation, but calls that may run at the same
+ *     time (on different streams) need workspaces of their own.
  *   - Inputs must be finite.  NaN or Inf in a weight or activation gives
  *     undefined (but memory-safe) results.
  *   - Calls are thread-safe; the only global state is a read-only table
