@@ -28,7 +28,7 @@ EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scal
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
-           "fp4_quantize", "dq_quantize_scales_fp8")
+           "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc")
 
 
 class QnError(RuntimeError):
@@ -78,6 +78,7 @@ def load_library():
         "lora_adamw_step": (ctypes.c_int, [vp, vp, vp, vp, vp, i64, f32, f32, f32, f32, f32, i32,
                                            vp]),
         "lora_dropout": (ctypes.c_int, [vp, i64, i64, f32, u64, vp, vp]),
+        "qlora_linear_fwd_noalloc": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp]),
         "qlora_linear_fwd_dropout": (ctypes.c_int, [wp, vp, vp, i64, vp, vp, i32, f32, vp, vp, vp,
                                                     sz, vp]),
         "qlora_linear_bwd_dx_dropout": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, f32, u64, vp,
@@ -278,6 +279,28 @@ def qlora_linear_fwd_dropout(qw, x, x_drop, A, B, r, alpha, y=None, u_out=None, 
                              stream=None):
     """y = x W^T + (alpha/r) (x_drop A^T) B^T, x_drop from lora_dropout."""
     return _fwd(qw, x, x_drop, A, B, r, alpha, y, u_out, ws, stream)
+
+
+def qlora_linear_fwd_noalloc(qw, x, A, B, r, alpha, y, u_out=None, stream=None):
+    """qlora_linear_fwd on the library's own scratch array: y (and u_out)
+    must be given; the call allocates nothing."""
+    torch = _torch()
+    lib = load_library()
+    M = x.shape[0]
+    _dev(x, torch.bfloat16, M * qw.K, "x")
+    if r:
+        _dev(A, torch.bfloat16, r * qw.K, "A")
+        _dev(B, torch.bfloat16, qw.N * r, "B")
+    if y is None:
+        raise ValueError("y: the allocation-free forward writes into a given tensor")
+    _dev(y, torch.bfloat16, M * qw.N, "y")
+    _dev(u_out, torch.bfloat16, M * r, "u_out")
+    cw = qw.c_struct()
+    a, b = (_ptr(A), _ptr(B)) if r else (None, None)
+    _check("qlora_linear_fwd_noalloc", lib.qlora_linear_fwd_noalloc(
+        ctypes.byref(cw), _ptr(x), M, a, b, r, float(alpha), _ptr(y), _ptr(u_out),
+        _stream(stream)))
+    return y
 
 
 def _fwd(qw, x, x_drop, A, B, r, alpha, y, u_out, ws, stream):

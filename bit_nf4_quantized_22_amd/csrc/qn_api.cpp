@@ -140,7 +140,7 @@ int dq(bool fp8, const float* absmax, int64_t nblocks, int32_t group, uint8_t* q
 // Forward with the LoRA-down input xa (x itself, or the dropped x).
 int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M, const qn_bf16* A,
              const qn_bf16* B, int32_t r, float alpha, qn_bf16* y, qn_bf16* u_out, void* ws,
-             size_t ws_bytes, void* stream) {
+             size_t ws_bytes, void* stream, bool own_scratch = false) {
   qn::WeightView v;
   int st = check_weight(w, v, true);
   if (st != QN_OK) return st;
@@ -153,6 +153,16 @@ int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M,
       (u_out && !aligned(u_out, 2)))
     return QN_ERR_ALIGN;
   const size_t need = fwd_ws(M, r);
+  if (own_scratch) {
+    // the library's per-device array stands in for the caller's workspace
+    if (need > qn::kScratchBytes) return QN_ERR_WORKSPACE;
+    ws = nullptr;
+    ws_bytes = 0;
+    if (need > 0) {
+      if (qn::scratch_address(&ws) != hipSuccess) return QN_ERR_HIP;
+      ws_bytes = qn::kScratchBytes;
+    }
+  }
   if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
   if (!qn::tables()) return QN_ERR_UNSUPPORTED;
@@ -293,6 +303,12 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
                      const qn_bf16* B, int32_t r, float alpha, qn_bf16* y, qn_bf16* u_out,
                      void* ws, size_t ws_bytes, void* stream) {
   return fwd_impl(w, x, x, M, A, B, r, alpha, y, u_out, ws, ws_bytes, stream);
+}
+
+int qlora_linear_fwd_noalloc(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_bf16* A,
+                             const qn_bf16* B, int32_t r, float alpha, qn_bf16* y,
+                             qn_bf16* u_out, void* stream) {
+  return fwd_impl(w, x, x, M, A, B, r, alpha, y, u_out, nullptr, 0, stream, true);
 }
 
 int qlora_linear_fwd_dropout(const qn_weight* w, const qn_bf16* x, const qn_bf16* x_drop,

@@ -47,6 +47,13 @@ constexpr int kWideMaxSlices = 16;
 // Number of L-slices launch_skinny uses for M > 16 tokens.
 int skinny_wide_splits(int64_t M, int64_t L);
 
+// Size of the library's own per-device scratch array (qn_scratch.hip), the
+// workspace of the allocation-free forward.
+constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
+// Device address of the current device's scratch array (resolved once per
+// device, then cached).
+hipError_t scratch_address(void** out);
+
 // Threads per workgroup of the decode GEMV for an N x K weight.
 int gemv_threads(int64_t N, int64_t K);
 // Number of L-slices launch_skinny uses for the decode path (M <= 16),

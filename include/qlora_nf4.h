@@ -228,6 +228,27 @@ QN_API int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M,
                      void* stream);
 
 /*
+ * qlora_linear_fwd_noalloc -- qlora_linear_fwd without a workspace
+ * argument, for callers that cannot allocate device memory (code under
+ * graph capture, tight serving loops, hosts that forbid allocation).
+ * Same arguments (minus ws, ws_bytes), same kernels and the same results
+ * bit for bit.  The workspace is a fixed 64 MiB array inside the library,
+ * one per GPU, created when the library is first used on that GPU and held
+ * until the process ends; this call allocates nothing.  Sizes whose
+ * forward workspace (qn_workspace_bytes(QN_OP_FWD, M, N, K, r)) exceeds
+ * 64 MiB return QN_ERR_WORKSPACE before anything runs (r = 64: M up to
+ * 15887 tokens; r = 128: 7943).  The first call on a device resolves that
+ * device's array address (hipGetSymbolAddress, with the stream's device
+ * current); make it once before capturing a graph.  Every call on one GPU
+ * shares its array and nothing in it needs to start at zero, but calls
+ * that may overlap on one GPU (different streams, or threads without
+ * ordering) race on it and must be serialised by the caller.
+ */
+QN_API int qlora_linear_fwd_noalloc(const qn_weight* w, const qn_bf16* x, int64_t M,
+                                    const qn_bf16* A, const qn_bf16* B, int32_t r,
+                                    float alpha, qn_bf16* y, qn_bf16* u_out, void* stream);
+
+/*
  * qlora_linear_bwd_dx -- dx = dy * dequant(W) + (alpha/r) * (dy * B) * A.
  * [kwkr] §2.3: the gradient flows through the frozen 4-bit weight to the
  * input and into the LoRA bypass only.

@@ -250,3 +250,25 @@ def test_code_type_argument_errors(lib):
     # a zero-initialised type pair is NF4 with the uint8 code
     w = qn.qn_weight(0x100000, None, None, 0x100000, 64, 64, 64, 256)
     assert (w.quant_type, w.scale_type) == (qn.QN_NF4, qn.QN_SCALE_U8)
+
+
+def test_noalloc_forward_host_checks(lib):
+    """qlora_linear_fwd_noalloc: the forward's argument errors, found on the
+    host before any HIP call, and QN_ERR_WORKSPACE when the forward
+    workspace would exceed the library's 64 MiB array."""
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256)
+    fwd = lib.qlora_linear_fwd_noalloc
+    assert fwd(ctypes.byref(w), FAKE, 8192, FAKE, FAKE, 128, 32.0, FAKE, None,
+               None) == qn.QN_ERR_WORKSPACE
+    assert fwd(ctypes.byref(w), FAKE, 1 << 40, FAKE, FAKE, 64, 16.0, FAKE, None,
+               None) == qn.QN_ERR_WORKSPACE
+    assert fwd(ctypes.byref(w), FAKE, 8192, None, None, 128, 32.0, ODD, None,
+               None) == qn.QN_ERR_ALIGN
+    assert fwd(ctypes.byref(w), FAKE, -1, FAKE, FAKE, 8, 16.0, FAKE, None,
+               None) == qn.QN_ERR_SHAPE
+    assert fwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 129, 16.0, FAKE, None,
+               None) == qn.QN_ERR_UNSUPPORTED
+    assert fwd(ctypes.byref(w), FAKE, 32, FAKE, None, 8, 16.0, FAKE, None,
+               None) == qn.QN_ERR_NULL
+    assert fwd(ctypes.byref(w), None, 32, FAKE, FAKE, 8, 16.0, FAKE, None,
+               None) == qn.QN_ERR_NULL
