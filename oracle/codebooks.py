@@ -1,6 +1,7 @@
 """Codebook variants of the 4-bit storage: the FP4 weight type, an FP8 level-2
-code for the block constants, and the uniform INT4 strawman; fp32 where a code
-is decided, fp64 elsewhere.
+code for the block constants, mean-centred double quantisation with a signed
+8-bit code, and the uniform INT4 strawman; fp32 where a code is decided, fp64
+elsewhere.
 
 TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
 
@@ -21,6 +22,24 @@ integer code) is stored as an FP8 E4M3 number (4 exponent bits with bias 7,
 3 mantissa bits, subnormals below 2^-6), rounded to nearest with ties to
 the even code; the level value is that number itself, exact in fp32, and
 c' = fl32(value * c2).  Every E4M3 number in [0, 1] has a code below 0x39.
+
+Mean-centred double quantisation.  [rkmt] §2.2.2 and [kwkr] §3.1 quantise
+the block constants a second time, to 8 bits; the pages stop there.  The
+QLoRA publication they summarise also subtracts the mean of the constants
+first, so that a symmetric signed code serves them.  Reading, step by step:
+  1. offset mu = fl32(S / n), S the fp64 sum of the n constants taken by
+     adjacent pairs (the constants, zero-padded to a power of two, are added
+     0+1, 2+3, ... and the partial sums again, level by level), so the sum
+     has one fixed order;
+  2. centred constants d = fl32(c - mu);
+  3. per group of 256, c2 = max |d|;
+  4. t = fl32(d / c2) (t = 0 when c2 = 0) takes the nearest level of the
+     signed grid fl32(k / 127), k = -127..127, ties toward k = 0; the code is
+     k as a two's-complement byte;
+  5. c' = fl32(fl32(fl32(k / 127) * c2) + mu).
+Step 5 may give a slightly negative c' for a constant near 0 (the error is
+at most half a level step of its group); that block's dequantised weights
+then change sign, with magnitudes at that error's size.
 
 [czcl] §2.1 shows a blockwise uniform 4-bit scheme as the contrast to NF4:
 a symmetric grid of 15 evenly spaced levels whose outermost ones sit at
@@ -147,6 +166,75 @@ def dequant_scales_fp8(q8, c2, group=nf4.GROUP):
     c2 = np.asarray(c2, dtype=np.float32).ravel()
     lv = e4m3_values().astype(np.float32)
     return (lv[q8] * c2[np.arange(q8.size) // group]).astype(np.float32)
+
+
+def tree_sum_f64(values):
+    """fp64 sum of the values by adjacent pairs: zero-padded to a power of two,
+    then a[0::2] + a[1::2] level by level until one value is left."""
+    a = np.asarray(values, dtype=np.float64).ravel()
+    if a.size == 0:
+        return 0.0
+    n = 1
+    while n < a.size:
+        n *= 2
+    a = np.concatenate([a, np.zeros(n - a.size)])
+    while a.size > 1:
+        a = a[0::2] + a[1::2]
+    return float(a[0])
+
+
+def centred_offset(absmax):
+    """Step 1: mu = fl32(tree_sum_f64(c) / n), the offset subtracted from the
+    block constants."""
+    c = np.asarray(absmax, dtype=np.float32).ravel()
+    if c.size == 0:
+        return np.float32(0.0)
+    return np.float32(tree_sum_f64(c) / float(c.size))
+
+
+def s8_levels():
+    """Level of every code byte: fl32(k / 127) for k the byte read as a
+    two's-complement integer (byte 0x80, k = -128, is never produced)."""
+    k = np.arange(256, dtype=np.int64)
+    k = np.where(k >= 128, k - 256, k)
+    return np.array([_nearest_f32(Fraction(int(v), 127)) for v in k], dtype=np.float32)
+
+
+def s8_encode(t):
+    """Step 4: code byte of each fp32 t in [-1, 1], nearest level of the grid
+    fl32(k / 127), ties toward k = 0."""
+    t = np.asarray(t, dtype=np.float32)
+    lv = np.array([_nearest_f32(Fraction(j, 127)) for j in range(128)], dtype=np.float64)
+    mids = (lv[:-1] + lv[1:]) / 2.0  # exact in fp64
+    a = np.abs(t.astype(np.float64))
+    j = np.searchsorted(mids, a, side="left")  # mid-points strictly below |t|
+    k = np.where(t < 0, -j, j)
+    return (k & 0xFF).astype(np.uint8)
+
+
+def double_quantize_centred(absmax, group=nf4.GROUP):
+    """Steps 1-4.  Returns (code bytes uint8[n], c2 fp32[ceil(n / group)], mu fp32)."""
+    c = np.ascontiguousarray(np.asarray(absmax, dtype=np.float32)).ravel()
+    if not np.all(np.isfinite(c)) or np.any(c < 0):
+        raise ValueError("oracle: block constants must be finite and >= 0")
+    mu = centred_offset(c)
+    nb = c.size
+    ng = -(-nb // group)
+    d = np.zeros(ng * group, dtype=np.float32)
+    d[:nb] = c - mu  # IEEE fp32 subtraction
+    groups = d.reshape(ng, group)
+    c2 = np.max(np.abs(groups), axis=1)
+    denom = np.where(c2 > 0, c2, np.float32(1.0)).astype(np.float32)
+    t = groups / denom[:, None]  # IEEE fp32 division; 0 / 1 = 0 for an all-zero group
+    return s8_encode(t).ravel()[:nb], c2.astype(np.float32), mu
+
+
+def dequant_scales_centred(q8, c2, mu, group=nf4.GROUP):
+    """Step 5: c' = fl32(fl32(level of q * c2) + mu)."""
+    q8 = np.asarray(q8, dtype=np.uint8).ravel()
+    c2 = np.asarray(c2, dtype=np.float32).ravel()
+    prod = (s8_levels()[q8] * c2[np.arange(q8.size) // group]).astype(np.float32)
+    return (prod + np.float32(mu)).astype(np.float32)
 
 
 def int4_uniform_levels(absmax):

@@ -2,7 +2,9 @@
 bit-level definition, the FP4 quantiser against brute force with exact
 rationals, the E4M3 encoder against torch's float8_e4m3fn conversion (an
 independent implementation), the error bounds of both level-2 codes, and
-the error study the pages' advice rests on."""
+the error study the pages' advice rests on; the mean-centred code against a
+hand-worked group, brute-force nearest levels in exact rationals, the
+pairing order of its sum, its half-step error bound and special cases."""
 
 from fractions import Fraction
 
@@ -200,3 +202,128 @@ def test_uniform_int4_has_fifteen_symmetric_levels():
     assert np.array_equal(codebooks.int4_uniform_roundtrip(-w), -codebooks.int4_uniform_roundtrip(w))
     # the error of every value is at most half a step
     assert np.all(np.abs(w_hat - blocks) <= step / 2 * (1 + 1e-12))
+
+
+# ---- mean-centred double quantisation -------------------------------------
+
+def test_centred_dq_hand_worked_group():
+    """Constants 1, 2, 3, 6: mean 3, centred -2, -1, 0, 3, group max |d| = 3,
+    t = -2/3, -1/3, 0, 1 -> nearest k / 127: 127 t = -84.67, -42.33, 0, 127
+    -> k = -85, -42, 0, 127 (bytes 171, 214, 0, 127)."""
+    q, c2, mu = codebooks.double_quantize_centred(np.array([1, 2, 3, 6], np.float32))
+    assert mu == 3.0 and c2.tolist() == [3.0]
+    assert q.tolist() == [171, 214, 0, 127]
+    cp = codebooks.dequant_scales_centred(q, c2, mu)
+    # c' = 3 + 3 k / 127 up to fp32 rounding: 0.99213, 2.00787, 3, 6
+    want = [3 - 255 / 127, 3 - 126 / 127, 3.0, 6.0]
+    assert np.allclose(cp.astype(np.float64), want, rtol=0, atol=4e-7)
+    assert cp[2] == 3.0 and cp[3] == 6.0
+
+
+def test_tree_sum_pairs_adjacent_values():
+    """1 + 2^-53 rounds to 1 in fp64 (a tie, to even) but 2^-53 + 2^-53 is
+    exact: adjacent pairing gives (1 + 2^-53) + (2^-53 + 2^-53) = 1 + 2^-52,
+    where a left-to-right sum gives 1; five values pad to eight with zeros."""
+    e = 2.0 ** -53
+    assert codebooks.tree_sum_f64([1.0, e, e, e]) == 1.0 + 2.0 ** -52
+    assert codebooks.tree_sum_f64([e, e, e, 1.0]) == 1.0 + 2.0 ** -52
+    assert codebooks.tree_sum_f64([1.0, e, e, e, 0.5]) == 1.5 + 2.0 ** -52
+    assert codebooks.tree_sum_f64([]) == 0.0 and codebooks.tree_sum_f64([2.5]) == 2.5
+    # integers below 2^20: every order is exact, so the sum is the integer sum
+    rng = np.random.default_rng(11)
+    ints = rng.integers(0, 1 << 20, size=12345)
+    assert codebooks.tree_sum_f64(ints.astype(np.float32)) == float(int(ints.sum()))
+
+
+def test_centred_offset_is_the_mean():
+    """mu is the mean of the constants to fp32 rounding (exact mean from
+    math.fsum), so the centred constants average to about zero."""
+    import math
+    rng = np.random.default_rng(12)
+    c = np.abs(rng.standard_normal((700, 64))).max(axis=1).astype(np.float32) * 0.02
+    mu = codebooks.centred_offset(c)
+    exact = math.fsum(c.astype(np.float64)) / c.size
+    assert abs(float(mu) - exact) <= 2.0 ** -24 * exact * 1.0001
+    d = (c - mu).astype(np.float64)
+    assert abs(d.mean()) <= 2.0 ** -22 * exact
+
+
+def test_s8_encode_is_the_nearest_level_by_brute_force():
+    """Against exhaustive search over the 255 levels in exact rationals, ties
+    toward k = 0, on random t, on every level and on every exact mid-point."""
+    lv = [Fraction(float(codebooks._nearest_f32(Fraction(k, 127)))) for k in range(-127, 128)]
+    rng = np.random.default_rng(13)
+    ts = list(rng.uniform(-1, 1, 300).astype(np.float32))
+    ts += [np.float32(float(v)) for v in lv]
+    for j in range(127):
+        m = (lv[127 + j] + lv[128 + j]) / 2
+        f = np.float32(float(m))
+        if Fraction(float(f)) == m:  # mid-points that are fp32 numbers are ties
+            ts += [f, -f]
+    ts = np.array(ts, dtype=np.float32)
+    got = codebooks.s8_encode(ts).view(np.int8).astype(int)
+    for t, k in zip(ts, got):
+        ft = Fraction(float(t))
+        dist = [abs(ft - v) for v in lv]
+        best = min(dist)
+        cands = [i - 127 for i, d in enumerate(dist) if d == best]
+        assert k == min(cands, key=abs), (t, k, cands)
+    # symmetry: -t takes the negated code
+    assert np.array_equal(codebooks.s8_encode(-ts).view(np.int8), -got.astype(np.int8))
+
+
+def test_s8_levels_are_k_over_127():
+    """Byte b holds the fp32 nearest to k / 127 (k = b as a signed byte):
+    both fp32 neighbours are farther from k / 127."""
+    lv = codebooks.s8_levels()
+    for b in range(256):
+        k = b - 256 if b >= 128 else b
+        f = lv[b]
+        d = abs(Fraction(float(f)) - Fraction(k, 127))
+        for nb in (np.nextafter(f, np.float32(-2)), np.nextafter(f, np.float32(2))):
+            assert abs(Fraction(float(nb)) - Fraction(k, 127)) > d, b
+    assert lv[0] == 0 and lv[127] == 1 and lv[129] == -1
+
+
+def test_centred_dq_error_is_half_a_level():
+    """|c' - c| <= c2 / 254 (half a step of the group's signed grid) plus the
+    fp32 roundings of d, t, the product and the sum."""
+    rng = np.random.default_rng(14)
+    w = rng.standard_normal((3000, 64)).astype(np.float32)
+    c = np.abs(w).max(axis=1).astype(np.float32) * np.float32(0.02)
+    q, c2, mu = codebooks.double_quantize_centred(c)
+    cp = codebooks.dequant_scales_centred(q, c2, mu).astype(np.float64)
+    g = np.arange(c.size) // 256
+    slack = 2.0 ** -22 * (c.astype(np.float64) + c2[g] + float(mu))
+    assert np.all(np.abs(cp - c) <= c2[g] / 254 + slack)
+
+
+def test_centred_dq_special_cases():
+    """Equal constants centre to zero: c2 = 0, every code 0, c' = mu = c
+    exactly; one constant is its own mean; zero constants give mu = 0."""
+    c = np.full(300, 0.0375, np.float32)
+    q, c2, mu = codebooks.double_quantize_centred(c)
+    assert mu == np.float32(0.0375) and not q.any() and not c2.any()
+    assert np.array_equal(codebooks.dequant_scales_centred(q, c2, mu), c)
+    q, c2, mu = codebooks.double_quantize_centred(np.array([0.7], np.float32))
+    assert mu == np.float32(0.7) and q.tolist() == [0]
+    q, c2, mu = codebooks.double_quantize_centred(np.zeros(5, np.float32))
+    assert mu == 0 and not q.any() and not c2.any()
+
+
+def test_level2_error_study():
+    """Relative MSE of the block constants of normal weights (blocks of 64)
+    under the three level-2 codes.  Centring pays: the constants of normal
+    blocks cluster around their mean (about 2.5 sigma), so the signed grid's
+    step, max |c - mu| / 127, is finer than the uint8 grid's max c / 255;
+    without the centring the signed grid (max c / 127) would lose to it."""
+    rng = np.random.default_rng(15)
+    w = rng.standard_normal((8000, 64)).astype(np.float32)
+    c = np.abs(w).max(axis=1).astype(np.float32)
+    q8, c2 = nf4.double_quantize(c)
+    mse_u8 = codebooks.relative_mse(c, nf4.dequant_scales(q8, c2))
+    qf, cf = codebooks.double_quantize_fp8(c)
+    mse_fp8 = codebooks.relative_mse(c, codebooks.dequant_scales_fp8(qf, cf))
+    qc, cc, mu = codebooks.double_quantize_centred(c)
+    mse_c = codebooks.relative_mse(c, codebooks.dequant_scales_centred(qc, cc, mu))
+    assert mse_c < mse_u8 < mse_fp8, (mse_c, mse_u8, mse_fp8)
