@@ -28,7 +28,8 @@ EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scal
            "nf4_dequant", "qn_workspace_bytes", "qlora_linear_fwd", "qlora_linear_bwd_dx",
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
-           "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc")
+           "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc",
+           "dq_quantize_scales_centred")
 
 
 class QnError(RuntimeError):
@@ -42,7 +43,8 @@ class qn_weight(ctypes.Structure):
                 ("gscale", ctypes.c_void_p), ("absmax", ctypes.c_void_p),
                 ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("blocksize", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("quant_type", ctypes.c_int32), ("scale_type", ctypes.c_int32)]
+                ("quant_type", ctypes.c_int32), ("scale_type", ctypes.c_int32),
+                ("offset", ctypes.c_void_p)]
 
 
 _lib = None
@@ -68,6 +70,7 @@ def load_library():
         "fp4_quantize": (ctypes.c_int, [vp, i32, i64, i32, vp, vp, vp]),
         "dq_quantize_scales": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "dq_quantize_scales_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
+        "dq_quantize_scales_centred": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
         "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
         "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -125,9 +128,9 @@ def _dev(t, dtype, numel=None, name="tensor"):
 
 
 QN_NF4, QN_FP4 = 0, 1
-QN_SCALE_U8, QN_SCALE_FP8 = 0, 1
+QN_SCALE_U8, QN_SCALE_FP8, QN_SCALE_CENTRED = 0, 1, 2
 _QUANT_TYPES = {"nf4": QN_NF4, "fp4": QN_FP4}
-_SCALE_TYPES = {"u8": QN_SCALE_U8, "fp8": QN_SCALE_FP8}
+_SCALE_TYPES = {"u8": QN_SCALE_U8, "fp8": QN_SCALE_FP8, "centred": QN_SCALE_CENTRED}
 
 
 class QuantWeight:
@@ -135,14 +138,16 @@ class QuantWeight:
 
     packed uint8[N*K/2]; qscale uint8[N*K/64] and gscale fp32[ceil(N*K/64/256)]
     when double-quantised, else absmax fp32[N*K/64].  quant_type "nf4" or
-    "fp4" (the code table), scale_type "u8" or "fp8" (the level-2 code).
+    "fp4" (the code table), scale_type "u8", "fp8" or "centred" (the level-2
+    code; "centred" also carries offset, fp32[1], the subtracted mean).
     """
 
     def __init__(self, packed, N, K, qscale=None, gscale=None, absmax=None, quant_type="nf4",
-                 scale_type="u8"):
+                 scale_type="u8", offset=None):
         self.packed, self.qscale, self.gscale, self.absmax = packed, qscale, gscale, absmax
         self.N, self.K = int(N), int(K)
         self.quant_type, self.scale_type = quant_type, scale_type
+        self.offset = offset
 
     def c_struct(self):
         return qn_weight(self.packed.data_ptr(),
@@ -150,7 +155,8 @@ class QuantWeight:
                          None if self.gscale is None else self.gscale.data_ptr(),
                          None if self.absmax is None else self.absmax.data_ptr(),
                          self.N, self.K, BLOCKSIZE, GROUP, _QUANT_TYPES[self.quant_type],
-                         _SCALE_TYPES[self.scale_type])
+                         _SCALE_TYPES[self.scale_type],
+                         None if self.offset is None else self.offset.data_ptr())
 
 
 def nf4_codebook():
@@ -223,18 +229,44 @@ def dq_quantize_scales(absmax, qscale=None, gscale=None, stream=None, fp8=False)
     return qscale, gscale
 
 
+def dq_quantize_scales_centred(absmax, qscale=None, gscale=None, offset=None, stream=None):
+    """Mean-centred double quantisation: returns (qscale uint8[nb] (signed
+    codes), gscale fp32[ceil(nb/256)], offset fp32[1])."""
+    torch = _torch()
+    lib = load_library()
+    _dev(absmax, torch.float32, name="absmax")
+    nb = absmax.numel()
+    ng = -(-nb // GROUP)
+    dev = absmax.device
+    qscale = torch.empty(nb, dtype=torch.uint8, device=dev) if qscale is None else qscale
+    gscale = torch.empty(ng, dtype=torch.float32, device=dev) if gscale is None else gscale
+    offset = torch.empty(1, dtype=torch.float32, device=dev) if offset is None else offset
+    _dev(qscale, torch.uint8, nb, "qscale")
+    _dev(gscale, torch.float32, ng, "gscale")
+    _dev(offset, torch.float32, 1, "offset")
+    _check("dq_quantize_scales_centred", lib.dq_quantize_scales_centred(
+        _ptr(absmax), nb, GROUP, _ptr(qscale), _ptr(gscale), _ptr(offset), _stream(stream)))
+    return qscale, gscale, offset
+
+
 def quantize_weight(w, double_quant=True, stream=None, quant_type="nf4", scale_type="u8"):
     """4-bit quantisation (+ double quantisation) of a [N, K] tensor -> QuantWeight.
 
     quant_type "nf4" (nf4_quantize) or "fp4" (fp4_quantize); scale_type "u8"
-    (dq_quantize_scales) or "fp8" (dq_quantize_scales_fp8)."""
+    (dq_quantize_scales), "fp8" (dq_quantize_scales_fp8) or "centred"
+    (dq_quantize_scales_centred)."""
     if quant_type not in _QUANT_TYPES or scale_type not in _SCALE_TYPES:
-        raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8' or 'fp8'")
+        raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8', 'fp8' or "
+                         "'centred'")
     N, K = w.shape
     quant = fp4_quantize if quant_type == "fp4" else nf4_quantize
     packed, absmax = quant(w, stream=stream)
     if not double_quant:
         return QuantWeight(packed, N, K, absmax=absmax, quant_type=quant_type)
+    if scale_type == "centred":
+        qscale, gscale, offset = dq_quantize_scales_centred(absmax, stream=stream)
+        return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
+                           scale_type=scale_type, offset=offset)
     qscale, gscale = dq_quantize_scales(absmax, stream=stream, fp8=scale_type == "fp8")
     return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
                        scale_type=scale_type)

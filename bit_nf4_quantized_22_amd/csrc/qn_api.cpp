@@ -41,17 +41,21 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   if (!w || !w->packed) return QN_ERR_NULL;
   if (w->blocksize != kBlock || w->group != kGroup) return QN_ERR_UNSUPPORTED;
   if (w->quant_type != QN_NF4 && w->quant_type != QN_FP4) return QN_ERR_UNSUPPORTED;
-  if (w->scale_type != QN_SCALE_U8 && w->scale_type != QN_SCALE_FP8) return QN_ERR_UNSUPPORTED;
+  if (w->scale_type != QN_SCALE_U8 && w->scale_type != QN_SCALE_FP8 &&
+      w->scale_type != QN_SCALE_CENTRED)
+    return QN_ERR_UNSUPPORTED;
   if (!qn::tables(w->quant_type)) return QN_ERR_UNSUPPORTED;
   if (w->N < 0 || w->K < 0) return QN_ERR_SHAPE;
   if (linear && (w->N <= 0 || w->K <= 0 || w->N % 64 != 0 || w->K % 64 != 0)) return QN_ERR_SHAPE;
+  const bool centred = w->qscale && w->scale_type == QN_SCALE_CENTRED;
   if (w->qscale) {
-    if (!w->gscale) return QN_ERR_NULL;
+    if (!w->gscale || (centred && !w->offset)) return QN_ERR_NULL;
   } else if (!w->absmax) {
     return QN_ERR_NULL;
   }
   if (!aligned(w->packed, 16)) return QN_ERR_ALIGN;
-  if ((w->gscale && !aligned(w->gscale, 4)) || (w->absmax && !aligned(w->absmax, 4)))
+  if ((w->gscale && !aligned(w->gscale, 4)) || (w->absmax && !aligned(w->absmax, 4)) ||
+      (centred && !aligned(w->offset, 4)))
     return QN_ERR_ALIGN;
   v.packed = w->packed;
   v.qscale = w->qscale;
@@ -60,7 +64,11 @@ int check_weight(const qn_weight* w, qn::WeightView& v, bool linear) {
   v.N = w->N;
   v.K = w->K;
   v.quant_type = w->quant_type == QN_FP4 ? qn::kQuantFP4 : qn::kQuantNF4;
-  v.fp8 = w->qscale && w->scale_type == QN_SCALE_FP8 ? 1 : 0;
+  v.l2 = !w->qscale ? qn::kL2Grid8
+        : w->scale_type == QN_SCALE_FP8 ? qn::kL2E4M3
+        : w->scale_type == QN_SCALE_CENTRED ? qn::kL2Centred
+                                            : qn::kL2Grid8;
+  v.mu = centred ? w->offset : nullptr;
   return QN_OK;
 }
 
@@ -273,6 +281,18 @@ int dq_quantize_scales(const float* absmax, int64_t nblocks, int32_t group, uint
 int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t group,
                            uint8_t* qscale, float* gscale, void* stream) {
   return dq(true, absmax, nblocks, group, qscale, gscale, stream);
+}
+
+int dq_quantize_scales_centred(const float* absmax, int64_t nblocks, int32_t group,
+                               uint8_t* qscale, float* gscale, float* offset, void* stream) {
+  if (group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (nblocks < 0) return QN_ERR_SHAPE;
+  if (nblocks == 0) return QN_OK;
+  if (!absmax || !qscale || !gscale || !offset) return QN_ERR_NULL;
+  if (!aligned(absmax, 4) || !aligned(gscale, 4) || !aligned(offset, 4)) return QN_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(
+      qn::launch_dq_centred(absmax, nblocks, qscale, gscale, offset, as_stream(stream)));
 }
 
 int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* stream) {

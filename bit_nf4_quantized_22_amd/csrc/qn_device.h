@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "qn_launch.h"
 #include "qn_tables.h"
 
 namespace qn {
@@ -54,18 +55,44 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
   return code + ((rem > 0x80000u || (rem == 0x80000u && (code & 1u))) ? 1u : 0u);
 }
 
-// Level-2 value of code q: the uint8 grid fl32(q / 255), or the E4M3 number.
-__device__ __forceinline__ float l2_value(uint32_t q, int fp8) {
-  return fp8 ? e4m3_value(q) : l8_value(q);
+// Level of a signed code byte q (two's complement k): fl32(k / 127), by the
+// same three operations as l8_value (correctly rounded for every k in
+// -128..127, checked exhaustively with exact rationals).
+__device__ __forceinline__ float s8_value(uint32_t q) {
+  const float kf = static_cast<float>(static_cast<int>(static_cast<int8_t>(q & 0xFFu)));
+  const float r = 1.0f / 127.0f;
+  const float x = kf * r;
+  return fmaf(fmaf(-x, 127.0f, kf), r, x);
+}
+
+// Level-2 value of code q of the given kind.
+__device__ __forceinline__ float l2_value(uint32_t q, int kind) {
+  return kind == kL2E4M3 ? e4m3_value(q) : kind == kL2Centred ? s8_value(q) : l8_value(q);
+}
+
+// fl32(fl32(a b) + c), rounded twice.  hipcc contracts a multiply feeding
+// an add into one fused multiply-add (a single rounding) even through
+// __fmul_rn / __fadd_rn; the empty asm hides the product from that.
+__device__ __forceinline__ float mul_then_add(float a, float b, float c) {
+  float p = a * b;
+  asm("" : "+v"(p));
+  return p + c;
+}
+
+// Double-dequantised block constant c' = fl32(fl32(L2[q] * c2) + mu); mu is
+// the centred code's offset and 0 for the others (adding +0 leaves the
+// non-negative product unchanged, bit for bit).
+__device__ __forceinline__ float dq_value(uint32_t q, float c2, int kind, float mu) {
+  return mul_then_add(l2_value(q, kind), c2, mu);
 }
 
 // Block constant c' of block `bi` of a quantised weight: double-dequantised
-// fl32(L2[q8] * c2) when qscale != nullptr, else the stored fp32 absmax.
+// when qscale != nullptr, else the stored fp32 absmax.
 __device__ __forceinline__ float block_scale(const uint8_t* __restrict__ qscale,
                                              const float* __restrict__ gscale,
                                              const float* __restrict__ absmax, int64_t bi,
-                                             int fp8) {
-  if (qscale) return __fmul_rn(l2_value(qscale[bi], fp8), gscale[bi >> 8]);
+                                             int kind, float mu) {
+  if (qscale) return dq_value(qscale[bi], gscale[bi >> 8], kind, mu);
   return absmax[bi];
 }
 
@@ -86,12 +113,20 @@ __device__ __forceinline__ float wave_sum(float v) {
 // every workgroup); each kernel builds its LDS tables from a few scalars
 // read with wave-uniform indices.
 
-// The 16 code values of the weight's table (fp32, ascending) and the kind
-// of its level-2 code (0: uint8 grid, 1: E4M3).
+// The 16 code values of the weight's table (fp32, ascending), the kind of
+// its level-2 code (kL2*) and, for the centred code, the device address of
+// its offset mu (nullptr otherwise).
 struct CodeParams {
   float q[16];
-  int fp8;
+  int l2;
+  const float* mu;
 };
+
+// The offset to add to every double-dequantised constant (one scalar load,
+// wave-uniform).
+__device__ __forceinline__ float l2_offset(const CodeParams& P) {
+  return P.mu ? *P.mu : 0.0f;
+}
 
 // The 16 code values spread over lanes 0..15 of one VGPR (v_writelane of
 // the scalar kernel arguments).  q[c] for a per-lane c is then a

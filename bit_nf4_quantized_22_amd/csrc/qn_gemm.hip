@@ -125,8 +125,8 @@ __device__ __forceinline__ void load_step(const GemmArgs& g, int64_t c0, int kt,
 
 // Block constant of a prefetched weight chunk.
 template <bool kDQ>
-__device__ __forceinline__ float chunk_scale(const Prefetch& pf, int fp8) {
-  return kDQ ? __fmul_rn(l2_value(pf.q8, fp8), pf.c) : pf.c;
+__device__ __forceinline__ float chunk_scale(const Prefetch& pf, int kind, float mu) {
+  return kDQ ? dq_value(pf.q8, pf.c, kind, mu) : pf.c;
 }
 
 // Dequantise one K step of weight codes into the LDS weight tile.  A
@@ -432,6 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
   // they store is never read.
   if (t >= 64 * kMmaWaves) {
     const int pt = t - 64 * kMmaWaves;
+    const float mu = kDQ ? l2_offset(P) : 0.0f;
     Prefetch p0, p1, p2, p3;
     load_step<kBwd, kDQ>(g, c0, 0, p0, pt);
     load_step<kBwd, kDQ>(g, c0, nk > 1 ? 1 : nk - 1, p1, pt);
@@ -439,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     load_step<kBwd, kDQ>(g, c0, nk > 3 ? 3 : nk - 1, p3, pt);
     store_lora();
     __syncthreads();  // the LoRA tiles visible
-    store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.fp8), P, sB[0], pt);
+    store_step<kBwd>(p0, chunk_scale<kDQ>(p0, P.l2, mu), P, sB[0], pt);
     __syncthreads();
     auto step = [&](int k, Prefetch& dec, Prefetch& ld) {
       const int kl = k + 4 < nk ? k + 4 : nk - 1;
@@ -447,7 +448,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
       // the barrier, so the compiler cannot hoist their address arithmetic
       // next to the loads it has just issued and wait for those.
       asm volatile("" : "+v"(dec.w), "+v"(dec.q8), "+v"(dec.c));
-      const float cs = chunk_scale<kDQ>(dec, P.fp8);
+      const float cs = chunk_scale<kDQ>(dec, P.l2, mu);
       load_step<kBwd, kDQ>(g, c0, kl, ld, pt);
       store_step<kBwd>(dec, cs, P, sB[(k & 1) ^ 1], pt);
       __syncthreads();

@@ -243,7 +243,7 @@ __device__ __forceinline__ void gemv_tables(uint32_t* stab, float* sl8, const Co
         code_value_uniform(R, static_cast<uint32_t>(e_hi0 + i * (kThreads / (16 * kPer)))), q_odd);
     reinterpret_cast<uint4*>(stab)[tid + i * kThreads] = make_uint4(wv, wv, wv, wv);
   }
-  for (int i = tid; i < 256; i += kThreads) sl8[i] = l2_value(static_cast<uint32_t>(i), P.fp8);
+  for (int i = tid; i < 256; i += kThreads) sl8[i] = l2_value(static_cast<uint32_t>(i), P.l2);
 }
 
 // Pair of bf16 code values of byte `byte` of `word` from lane `lane`'s copy
@@ -391,6 +391,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_ring_kernel(const GemvArgs a
 
   // tables first, published before any load is in flight
   gemv_tables<kCopiesT, kThreads>(stab, sl8, P, tid);
+  const float mu = kDQ ? l2_offset(P) : 0.0f;
   lds_barrier();
 
   // Weight loads: lane l reads 8 bytes of row n0 + l / 4 at byte 8 (l % 4)
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_ring_kernel(const GemvArgs a
         for (int b = 0; b < 4; ++b) {
           const int i = 4 * j + b;
           if (i < kS) {
-            const float c = __fmul_rn(sl8[(al >> (8 * b)) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
+            const float c = mul_then_add(sl8[(al >> (8 * b)) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi, mu);
             cs[i] = i < nb ? c : 0.f;
           }
         }
@@ -546,6 +547,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv1_kernel(const GemvArgs a, co
 
   // 1. tables, published before any load is in flight
   gemv_tables<kCopiesT, kThreads>(stab, sl8, P, tid);
+  const float mu = kDQ ? l2_offset(P) : 0.0f;
   lds_barrier();
 
   // the band's 16 rows as a buffer: lane offset in a VGPR, block offset
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(kWaves * 64) void gemv1_kernel(const GemvArgs a, co
       float c;
       if constexpr (kDQ) {
         const uint32_t al = __builtin_amdgcn_alignbyte(qd[i / 4 + 1], qd[i / 4], sh);
-        c = __fmul_rn(sl8[(al >> (8 * (i % 4))) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi);
+        c = mul_then_add(sl8[(al >> (8 * (i % 4))) & 0xFFu], gfirst + i < 256 ? g_lo : g_hi, mu);
       } else {
         c = cq[i];
       }

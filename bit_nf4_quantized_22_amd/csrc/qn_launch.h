@@ -10,6 +10,11 @@ namespace qn {
 
 struct CodeParams;  // qn_device.h
 
+// Kinds of level-2 code of the block constants.
+constexpr int kL2Grid8 = 0;    // uint8 grid fl32(q / 255) of c / c2
+constexpr int kL2E4M3 = 1;     // E4M3 number of c / c2
+constexpr int kL2Centred = 2;  // signed grid fl32(k / 127) of (c - mu) / c2
+
 struct WeightView {
   const uint8_t* packed;
   const uint8_t* qscale;  // nullptr: not double-quantised
@@ -17,7 +22,8 @@ struct WeightView {
   const float* absmax;
   int64_t N, K;
   int quant_type;  // kQuantNF4 or kQuantFP4 (the code table)
-  int fp8;         // level-2 code: 0 uint8 grid, 1 E4M3
+  int l2;          // level-2 code: 0 uint8 grid, 1 E4M3, 2 mean-centred signed grid
+  const float* mu; // the centred code's offset (device, one fp32), else nullptr
 };
 
 // Code values and level-2 kind of a weight, for the kernels.
@@ -27,6 +33,11 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, int quant_ty
                            uint8_t* packed, float* absmax, hipStream_t s);
 hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qscale,
                      float* gscale, hipStream_t s);
+// Mean-centred level-2 code: mu (pairwise fp64 sum of the constants / n,
+// written to *mu), then per 256-group c2 = max |c - mu| and signed codes.
+// gscale doubles as scratch for the partial sums before its final values.
+hipError_t launch_dq_centred(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
+                             float* mu, hipStream_t s);
 hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStream_t s);
 
 // out[M, r] = in[M, L] * P^T, P row-major [r, L] (in and P 16-byte

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kMRows;
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kMCols;
   const int64_t n = n0 + 16 * wave + nl;  // N % 64 == 0: always a valid row
+  const float mu = kDQ ? l2_offset(P) : 0.0f;
   {
     const CodeRegs R = code_regs(P);
     for (int i = tid; i < 16 * 64; i += 256) scode[i] = code_value(R, i >> 6);
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void merge_kernel(
 #pragma unroll
   for (int blk = 0; blk < kBlk; ++blk) {
     const int64_t kb = k0 + 64 * blk;  // first column of the block
-    const float cs = kDQ ? __fmul_rn(l2_value(q8[blk], P.fp8), c2[blk]) : c2[blk];
+    const float cs = kDQ ? dq_value(q8[blk], c2[blk], P.l2, mu) : c2[blk];
     f32x4_t t[4];
 #pragma unroll
     for (int b = 0; b < 4; ++b) {

@@ -226,6 +226,107 @@ __global__ __launch_bounds__(256) void dq_quantize_kernel(const float* __restric
   if (i < nblocks) qscale[i] = dq_code<kFP8>(c, c2, sthr);
 }
 
+// ---- mean-centred level-2 code ----------------------------------------
+// The offset mu is the mean of the block constants, summed in fp64 by
+// adjacent pairs (the constants zero-padded to a power of two, added 0+1,
+// 2+3, ..., then the partial sums likewise), so its value does not depend
+// on the launch shape.  A workgroup sums 4096 consecutive values: each lane
+// 16 as a balanced tree in registers, then the 256 lane sums pair up in LDS.
+// 4096-aligned chunks are subtrees of the whole tree, so partial sums of
+// partial sums give the same result.
+
+__device__ __forceinline__ double tree_input(const float* p, int64_t i) {
+  return static_cast<double>(p[i]);
+}
+// fp64 partial sums are kept as pairs of 32-bit words (the scratch area is
+// only 4-byte aligned)
+__device__ __forceinline__ double tree_input(const uint32_t* p, int64_t i) {
+  const uint64_t b = static_cast<uint64_t>(p[2 * i]) | (static_cast<uint64_t>(p[2 * i + 1]) << 32);
+  return __longlong_as_double(static_cast<long long>(b));
+}
+
+constexpr int kTreeChunk = 4096;
+
+// kFinal: one workgroup, n <= 4096, writes mu = fl32(sum / count);
+// otherwise workgroup b writes the sum of chunk b to part[2b], part[2b + 1].
+template <typename T, bool kFinal>
+__global__ __launch_bounds__(256) void mean_tree_kernel(const T* __restrict__ in, int64_t n,
+                                                        uint32_t* __restrict__ part,
+                                                        int64_t count, float* __restrict__ mu) {
+  __shared__ double sp[256];
+  const int t = threadIdx.x;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * kTreeChunk + t * 16;
+  double v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = base + i < n ? tree_input(in, base + i) : 0.0;
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+#pragma unroll
+    for (int i = 0; i < w; ++i) v[i] = __dadd_rn(v[2 * i], v[2 * i + 1]);
+  }
+  sp[t] = v[0];
+  __syncthreads();
+  for (int st = 1; st < 256; st *= 2) {
+    if ((t & (2 * st - 1)) == 0) sp[t] = __dadd_rn(sp[t], sp[t + st]);
+    __syncthreads();
+  }
+  if (t == 0) {
+    if constexpr (kFinal) {
+      *mu = __double2float_rn(__ddiv_rn(sp[0], static_cast<double>(count)));
+    } else {
+      const uint64_t b = static_cast<uint64_t>(__double_as_longlong(sp[0]));
+      part[2 * static_cast<int64_t>(blockIdx.x)] = static_cast<uint32_t>(b);
+      part[2 * static_cast<int64_t>(blockIdx.x) + 1] = static_cast<uint32_t>(b >> 32);
+    }
+  }
+}
+
+// Largest fp32 not above the fp64 mid-point of the signed-grid levels j / 127
+// and (j + 1) / 127, j = 0..126 (the mid-point is exact in fp64); +inf last.
+__device__ __forceinline__ void fill_s8_thresholds(float* sthr, int j) {
+  float thr = INFINITY;
+  if (j < 127) {
+    const double m =
+        (static_cast<double>(s8_value(j)) + static_cast<double>(s8_value(j + 1))) * 0.5;
+    thr = static_cast<float>(m);
+    if (static_cast<double>(thr) > m) thr = nextafterf(thr, -INFINITY);
+  }
+  sthr[j] = thr;
+}
+
+// Code of a centred constant d in a group with c2 = max |d|: t = fl32(d / c2),
+// the level j / 127 nearest to |t| (ties toward 0), signed like t, as a
+// two's-complement byte.
+__device__ __forceinline__ uint8_t s8_code(float d, float c2, const float* sthr) {
+  if (!(c2 > 0.0f)) return 0;
+  const float t = d / c2;  // IEEE division
+  const float a = fabsf(t);
+  int j = static_cast<int>(fminf(fmaxf(fmaf(a, 127.0f, 0.5f), 0.0f), 127.0f));
+  while (j < 127 && a > sthr[j]) ++j;
+  while (j > 0 && !(a > sthr[j - 1])) --j;
+  return static_cast<uint8_t>((t < 0.0f ? -j : j) & 0xFF);
+}
+
+// One workgroup of 256 lanes per group of 256 block constants.
+__global__ __launch_bounds__(256) void dq_centred_kernel(const float* __restrict__ absmax,
+                                                         int64_t nblocks,
+                                                         const float* __restrict__ mu,
+                                                         uint8_t* __restrict__ qscale,
+                                                         float* __restrict__ gscale) {
+  __shared__ float sthr[128];
+  __shared__ float smax[4];
+  if (threadIdx.x < 128) fill_s8_thresholds(sthr, threadIdx.x);
+  const float off = *mu;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const float d = i < nblocks ? __fsub_rn(absmax[i], off) : 0.0f;
+  const float wm = wave_max(fabsf(d));
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  if (threadIdx.x == 0) gscale[blockIdx.x] = c2;
+  if (i < nblocks) qscale[i] = s8_code(d, c2, sthr);
+}
+
 // Each thread expands 32 codes: four runs of 8 (4 packed bytes, one block
 // constant each), 2048 codes apart.
 template <bool kOutBf16>
@@ -235,6 +336,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     void* __restrict__ out, CodeParams P) {
   __shared__ float2 spair[256];
   fill_pair_f32(spair, P, 1);
+  const float mu = l2_offset(P);
   __syncthreads();
   // Run i of thread t: codes wbase + 2048 i .. + 7, so every load and
   // store instruction of a wave covers one contiguous range (256 bytes of
@@ -251,7 +353,7 @@ __global__ __launch_bounds__(256) void nf4_dequant_kernel(
     const int64_t ei = wbase + i * 2048;
     e[i] = ei < numel ? ei : numel - 8;
     words[i] = *reinterpret_cast<const uint32_t*>(packed + e[i] / 2);
-    cs[i] = block_scale(qscale, gscale, absmax, e[i] >> 6, P.fp8);
+    cs[i] = block_scale(qscale, gscale, absmax, e[i] >> 6, P.l2, mu);
   }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -282,7 +384,8 @@ CodeParams code_params(const WeightView& w) {
   const Tables* t = tables(w.quant_type);
   CodeParams P;
   for (int i = 0; i < 16; ++i) P.q[i] = t->q32[i];
-  P.fp8 = w.fp8;
+  P.l2 = w.l2;
+  P.mu = w.l2 == kL2Centred ? w.mu : nullptr;
   return P;
 }
 
@@ -314,6 +417,39 @@ hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qs
   else
     hipLaunchKernelGGL(dq_quantize_kernel<false>, dim3(static_cast<uint32_t>(groups)), dim3(256),
                        0, s, absmax, nblocks, qscale, gscale);
+  return hipGetLastError();
+}
+
+hipError_t launch_dq_centred(const float* absmax, int64_t nblocks, uint8_t* qscale, float* gscale,
+                             float* mu, hipStream_t s) {
+  if (nblocks == 0) return hipSuccess;
+  // partial sums go to gscale (ceil(nblocks / 256) words) before its final
+  // values: level 1 needs 2 ceil(nblocks / 4096) words, which fit once
+  // nblocks > 4096; deeper levels follow it and are smaller still
+  uint32_t* stage = reinterpret_cast<uint32_t*>(gscale);
+  if (nblocks <= kTreeChunk) {
+    hipLaunchKernelGGL((mean_tree_kernel<float, true>), dim3(1), dim3(256), 0, s, absmax, nblocks,
+                       nullptr, nblocks, mu);
+  } else {
+    int64_t cnt = (nblocks + kTreeChunk - 1) / kTreeChunk;
+    hipLaunchKernelGGL((mean_tree_kernel<float, false>), dim3(static_cast<uint32_t>(cnt)),
+                       dim3(256), 0, s, absmax, nblocks, stage, nblocks, nullptr);
+    const uint32_t* cur = stage;
+    uint32_t* next = stage + 2 * cnt;
+    while (cnt > kTreeChunk) {
+      const int64_t m = (cnt + kTreeChunk - 1) / kTreeChunk;
+      hipLaunchKernelGGL((mean_tree_kernel<uint32_t, false>), dim3(static_cast<uint32_t>(m)),
+                         dim3(256), 0, s, cur, cnt, next, nblocks, nullptr);
+      cur = next;
+      next += 2 * m;
+      cnt = m;
+    }
+    hipLaunchKernelGGL((mean_tree_kernel<uint32_t, true>), dim3(1), dim3(256), 0, s, cur, cnt,
+                       nullptr, nblocks, mu);
+  }
+  const int64_t groups = (nblocks + 255) / 256;
+  hipLaunchKernelGGL(dq_centred_kernel, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, s,
+                     absmax, nblocks, mu, qscale, gscale);
   return hipGetLastError();
 }
 

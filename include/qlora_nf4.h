@@ -74,6 +74,7 @@ typedef uint16_t qn_bf16; /* bf16 bit pattern */
 /* level-2 code of the block constants (qn_weight.scale_type) */
 #define QN_SCALE_U8   0
 #define QN_SCALE_FP8  1
+#define QN_SCALE_CENTRED 2
 
 /*
  * A quantised weight W[N, K] (N = out_features, K = in_features).
@@ -90,10 +91,14 @@ typedef uint16_t qn_bf16; /* bf16 bit pattern */
  *   row; other sizes return QN_ERR_SHAPE.
  *   quant_type  QN_NF4 (the NF4 table of nf4_codebook) or QN_FP4 (that of
  *           fp4_codebook); the codes must come from the matching quantiser.
- *   scale_type  QN_SCALE_U8 (qscale from dq_quantize_scales) or
- *           QN_SCALE_FP8 (from dq_quantize_scales_fp8); ignored when
- *           qscale == NULL.  Other values return QN_ERR_UNSUPPORTED.  A
- *           zero-initialised struct means NF4 with the uint8 code.
+ *   scale_type  QN_SCALE_U8 (qscale from dq_quantize_scales),
+ *           QN_SCALE_FP8 (from dq_quantize_scales_fp8) or QN_SCALE_CENTRED
+ *           (from dq_quantize_scales_centred); ignored when qscale == NULL.
+ *           Other values return QN_ERR_UNSUPPORTED.  A zero-initialised
+ *           struct means NF4 with the uint8 code.
+ *   offset  device fp32[1]: the mean subtracted by the centred code;
+ *           required (QN_ERR_NULL) iff qscale != NULL and scale_type ==
+ *           QN_SCALE_CENTRED, ignored otherwise.
  */
 typedef struct qn_weight {
   const uint8_t* packed;
@@ -106,6 +111,7 @@ typedef struct qn_weight {
   int32_t group;
   int32_t quant_type;
   int32_t scale_type;
+  const float* offset;
 } qn_weight;
 
 /* Human-readable text for a status code (static storage, never NULL). */
@@ -184,6 +190,29 @@ QN_API int fp4_quantize(const void* w, int32_t dtype, int64_t numel, int32_t blo
  */
 QN_API int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t group,
                                   uint8_t* qscale, float* gscale, void* stream);
+
+/*
+ * dq_quantize_scales_centred -- mean-centred double quantisation.
+ * [rkmt] §2.2.2 and [kwkr] §3.1 quantise the block constants to 8 bits a
+ * second time; the publication the pages summarise subtracts the constants'
+ * mean first so that a symmetric signed code serves them.  Here:
+ *   mu = fl32(S / nblocks), S the fp64 sum of the constants by adjacent
+ *        pairs (zero-padded to a power of two, added 0+1, 2+3, ... level by
+ *        level): one fixed order, bit-reproducible;
+ *   d = fl32(c - mu); per group of 256, gscale = max |d|;
+ *   qscale = k as a two's-complement byte, k in -127..127 the nearest level
+ *        fl32(k / 127) to fl32(d / gscale) (ties toward k = 0; 0 when
+ *        gscale == 0);
+ *   the dequantised constant is fl32(fl32(fl32(k / 127) * gscale) + mu).
+ *   absmax  device fp32[nblocks] in;  qscale uint8[nblocks] out;
+ *   gscale  fp32[ceil(nblocks/256)] out (also scratch during the call);
+ *   offset  device fp32[1] out (mu).  4-byte alignment suffices.
+ * Use scale_type = QN_SCALE_CENTRED and qn_weight.offset = offset.  Other
+ * errors as dq_quantize_scales; nblocks == 0 writes nothing.
+ */
+QN_API int dq_quantize_scales_centred(const float* absmax, int64_t nblocks, int32_t group,
+                                      uint8_t* qscale, float* gscale, float* offset,
+                                      void* stream);
 
 /*
  * nf4_dequant -- materialise the weight.

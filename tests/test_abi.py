@@ -239,7 +239,7 @@ def test_code_type_argument_errors(lib):
     assert lib.dq_quantize_scales_fp8(FAKE, -1, 256, FAKE, FAKE, None) == qn.QN_ERR_SHAPE
     assert lib.dq_quantize_scales_fp8(FAKE, 10, 256, None, FAKE, None) == qn.QN_ERR_NULL
     # unknown code types are rejected by every call that takes a weight
-    for qt, st in ((2, 0), (-1, 0), (0, 2), (1, 7)):
+    for qt, st in ((2, 0), (-1, 0), (0, 3), (1, 7)):
         w = qn.qn_weight(0x100000, 0x100000, 0x100000, None, 128, 128, 64, 256, qt, st)
         assert lib.nf4_dequant(ctypes.byref(w), qn.QN_BF16, FAKE, None) == qn.QN_ERR_UNSUPPORTED
         assert lib.qlora_merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, FAKE, None) == \
@@ -250,6 +250,31 @@ def test_code_type_argument_errors(lib):
     # a zero-initialised type pair is NF4 with the uint8 code
     w = qn.qn_weight(0x100000, None, None, 0x100000, 64, 64, 64, 256)
     assert (w.quant_type, w.scale_type) == (qn.QN_NF4, qn.QN_SCALE_U8)
+
+
+def test_centred_code_argument_errors(lib):
+    """dq_quantize_scales_centred checks its arguments like the other level-2
+    quantisers and needs the offset output; a weight of the centred kind
+    needs its offset (QN_ERR_NULL without it), which the other kinds and an
+    undouble-quantised weight ignore."""
+    f = lib.dq_quantize_scales_centred
+    assert f(FAKE, 10, 128, FAKE, FAKE, FAKE, None) == qn.QN_ERR_UNSUPPORTED
+    assert f(FAKE, -1, 256, FAKE, FAKE, FAKE, None) == qn.QN_ERR_SHAPE
+    assert f(FAKE, 10, 256, FAKE, FAKE, None, None) == qn.QN_ERR_NULL
+    assert f(FAKE, 10, 256, None, FAKE, FAKE, None) == qn.QN_ERR_NULL
+    assert f(FAKE, 10, 256, FAKE, FAKE, ODD, None) == qn.QN_ERR_ALIGN
+    assert f(None, 0, 256, None, None, None, None) == qn.QN_OK
+    w = qn.qn_weight(0x100000, 0x100000, 0x100000, None, 128, 128, 64, 256, 0,
+                     qn.QN_SCALE_CENTRED, None)
+    assert lib.nf4_dequant(ctypes.byref(w), qn.QN_BF16, FAKE, None) == qn.QN_ERR_NULL
+    assert lib.qlora_merge(ctypes.byref(w), FAKE, FAKE, 8, 16.0, FAKE, None) == qn.QN_ERR_NULL
+    w.offset = ODD
+    assert lib.nf4_dequant(ctypes.byref(w), qn.QN_BF16, FAKE, None) == qn.QN_ERR_ALIGN
+    # without qscale the scale type is ignored: the absmax weight passes the
+    # weight checks and stops at the misaligned output
+    w = qn.qn_weight(0x100000, None, None, 0x100000, 128, 128, 64, 256, 0,
+                     qn.QN_SCALE_CENTRED, None)
+    assert lib.qlora_merge(ctypes.byref(w), None, None, 8, 16.0, ODD, None) == qn.QN_ERR_ALIGN
 
 
 def test_noalloc_forward_host_checks(lib):

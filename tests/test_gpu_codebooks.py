@@ -1,7 +1,9 @@
 """Codebook variants on the GPU against the oracle (oracle/codebooks.py): the
-FP4 weight table and the FP8 (E4M3) level-2 code.
+FP4 weight table, the FP8 (E4M3) level-2 code and mean-centred double
+quantisation (signed 8-bit code around the constants' mean).
 
-Bars: codes, block constants and level-2 codes bit-exact; dequantised
+Bars: codes, block constants, level-2 codes and the centred offset
+bit-exact; dequantised
 weights bit-exact (fp32 and bf16); the linear ops and the merge with such
 weights within the same tolerances as with NF4 (relative Frobenius 1e-2).
 """
@@ -17,13 +19,17 @@ from tests.gpu_helpers import (bf16_dev, check, f32_dev, f64, rel_frob, run_laye
 
 pytestmark = pytest.mark.gpu
 
-COMBOS = [("fp4", "u8"), ("fp4", "fp8"), ("fp4", None), ("nf4", "fp8")]
+COMBOS = [("fp4", "u8"), ("fp4", "fp8"), ("fp4", None), ("nf4", "fp8"), ("nf4", "centred"),
+          ("fp4", "centred")]
 
 
 def oracle_weight(W32, kind, scale):
     packed, absmax = codebooks.quantize_4bit(W32, kind)
-    q8 = c2 = None
-    if scale == "u8":
+    q8 = c2 = mu = None
+    if scale == "centred":
+        q8, c2, mu = codebooks.double_quantize_centred(absmax)
+        scales = codebooks.dequant_scales_centred(q8, c2, mu)
+    elif scale == "u8":
         q8, c2 = nf4.double_quantize(absmax)
         scales = nf4.dequant_scales(q8, c2)
     elif scale == "fp8":
@@ -32,7 +38,7 @@ def oracle_weight(W32, kind, scale):
     else:
         scales = absmax
     What = codebooks.dequantize_4bit(packed, scales, W32.size, kind).reshape(W32.shape)
-    return dict(packed=packed, absmax=absmax, q8=q8, c2=c2, What=What)
+    return dict(packed=packed, absmax=absmax, q8=q8, c2=c2, mu=mu, What=What)
 
 
 def device_weight(W, dtype, kind, scale):
@@ -52,6 +58,9 @@ def assert_weight_equal(qw, ref):
         badq = np.nonzero(gq != ref["q8"].ravel())[0]
         assert badq.size == 0, f"{badq.size} level-2 codes differ, first at {badq[:5]}"
         assert np.array_equal(qw.gscale.cpu().numpy().view(np.uint32), ref["c2"].view(np.uint32))
+        if ref["mu"] is not None:
+            got_mu = qw.offset.cpu().numpy().view(np.uint32)
+            assert got_mu.tolist() == [int(np.float32(ref["mu"]).view(np.uint32))]
     else:
         assert np.array_equal(qw.absmax.cpu().numpy().view(np.uint32),
                               ref["absmax"].view(np.uint32))
@@ -127,7 +136,8 @@ def test_fp8_level2_code_crafted_ratios():
     assert bad.size == 0, f"{bad.size} codes differ, e.g. c={c[bad[:4]]}"
 
 
-@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("fp4", None), ("nf4", "fp8")])
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("fp4", None), ("nf4", "fp8"),
+                                        ("nf4", "centred"), ("fp4", "centred")])
 @pytest.mark.parametrize("M", [1, 16, 40])
 def test_linear_layer_with_codebook(kind, scale, M):
     wl = synth.tiny_layer(0)
@@ -140,27 +150,29 @@ def test_linear_layer_with_codebook(kind, scale, M):
     run_layer_checks(wl, M=M, qw=qw, ref=ref)
 
 
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("nf4", "centred")])
 @pytest.mark.parametrize("M", [1, 16])
-def test_decode_with_fp4_fp8(M):
+def test_decode_with_codebook(M, kind, scale):
     wl = synth.decode_layer(M, 4096, 11008, seed=2)
-    qw = device_weight(wl.W, "bf16", "fp4", "fp8")
-    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), "fp4", "fp8")
+    qw = device_weight(wl.W, "bf16", kind, scale)
+    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), kind, scale)
     y = qn.qlora_linear_fwd(qw, bf16_dev(wl.x), bf16_dev(wl.A), bf16_dev(wl.B), wl.r, wl.alpha)
     torch.cuda.synchronize()
     want = linear.linear_forward(f64(wl.x), ref["What"].astype(np.float64), f64(wl.A), f64(wl.B),
                                  wl.alpha, wl.r)
-    check(f"decode fp4+fp8 M={M}", to_np(y), want)
+    check(f"decode {kind}+{scale} M={M}", to_np(y), want)
 
 
-def test_training_shape_with_fp4_fp8():
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("nf4", "centred")])
+def test_training_shape_with_codebook(kind, scale):
     wl = synth.train_linear(4096, 11008, M=2048, seed=3)
-    qw = device_weight(wl.W, "bf16", "fp4", "fp8")
-    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), "fp4", "fp8")
+    qw = device_weight(wl.W, "bf16", kind, scale)
+    ref = oracle_weight(weight_f32(wl.W, "bf16").reshape(wl.N, wl.K), kind, scale)
     rows = np.sort(np.random.default_rng(0).choice(2048, 128, replace=False))
     run_layer_checks(wl, rows=rows, qw=qw, ref=ref)
 
 
-@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("nf4", "fp8")])
+@pytest.mark.parametrize("kind,scale", [("fp4", "fp8"), ("nf4", "fp8"), ("nf4", "centred")])
 def test_merge_with_codebook(kind, scale):
     wl = synth.decode_layer(1, 1024, 2048, seed=5, r=16, alpha=32.0)
     qw = device_weight(wl.W, "bf16", kind, scale)
@@ -192,3 +204,67 @@ def test_all_zero_blocks_take_the_zero_code(kind):
     assert np.array_equal(got, want_p)
     assert np.all(got.reshape(4, 32)[[0, 1, 3]] == 0x77)
     assert np.array_equal(absmax.cpu().numpy().view(np.uint32), want_a.view(np.uint32))
+
+
+def _centred_on_gpu(c):
+    q, g, mu = qn.dq_quantize_scales_centred(f32_dev(c))
+    torch.cuda.synchronize()
+    return q.cpu().numpy(), g.cpu().numpy(), mu.cpu().numpy()
+
+
+def _assert_centred_equal(c):
+    q, g, mu = _centred_on_gpu(c)
+    rq, rg, rmu = codebooks.double_quantize_centred(c)
+    assert mu.view(np.uint32).tolist() == [int(np.float32(rmu).view(np.uint32))], (mu, rmu)
+    assert np.array_equal(g.view(np.uint32), rg.view(np.uint32))
+    bad = np.nonzero(q != rq)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, e.g. c={c[bad[:4]]}"
+
+
+def test_centred_code_near_ties():
+    """Constants placed at mu + m c2 for mid-points m between adjacent signed
+    levels, one fp32 step either side, the levels themselves, a group of
+    constants equal to mu (centred to zero), and all-zero or all-equal
+    tensors.  The placement is repeated with the new mean until mu no longer
+    moves, so the ratios land on the decision boundaries of the final mu."""
+    rng = np.random.default_rng(21)
+    base = np.abs(rng.standard_normal(256 * 1040)).astype(np.float32) * 0.05
+    lv = np.array([float(codebooks.s8_levels()[j]) for j in range(128)])
+    mids = (lv[:-1] + lv[1:]) / 2
+    picks = [(float(np.float32(rng.uniform(0.01, 0.04))),
+              rng.integers(0, 127, 256), rng.integers(0, 2, 256) * 2 - 1,
+              rng.integers(0, 4, 256), rng.integers(0, 128, 256)) for _ in range(38)]
+
+    def place(mu):
+        c = base.copy()
+        for gi, (c2, mi, sg, how, li) in enumerate(picks, start=1):
+            blk = np.empty(256, np.float32)
+            for i in range(256):
+                v = np.float32(mu + sg[i] * mids[mi[i]] * c2)
+                blk[i] = [v, np.nextafter(v, np.float32(-1)), np.nextafter(v, np.float32(1)),
+                          np.float32(mu + sg[i] * lv[li[i]] * c2)][how[i]]
+            blk[0] = np.float32(mu + c2)
+            c[256 * gi:256 * (gi + 1)] = np.maximum(blk, 0)
+        c[256 * 39:256 * 40] = np.float32(mu)
+        return c
+
+    mu = float(codebooks.centred_offset(base))
+    for _ in range(10):
+        c = place(mu)
+        new = float(codebooks.centred_offset(c))
+        if new == mu:
+            break
+        mu = new
+    _assert_centred_equal(c)
+    _assert_centred_equal(np.zeros(300, np.float32))
+    _assert_centred_equal(np.full(513, 0.04, np.float32))
+
+
+@pytest.mark.parametrize("nb", [1, 255, 4096, 4097, 12345 * 64, 4096 * 4096 + 12345])
+def test_centred_offset_sum_over_levels(nb):
+    """The pairwise sum runs in one workgroup (nb <= 4096), in two levels and,
+    past 4096 * 4096 constants, in three; wide-range constants (log-normal)
+    make the result depend on the order, so the bit-exact mu pins it."""
+    rng = np.random.default_rng(nb)
+    c = np.exp(rng.normal(-3.0, 2.0, nb)).astype(np.float32)
+    _assert_centred_equal(c)
