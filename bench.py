@@ -21,7 +21,19 @@ weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
             graphs are replayed each step: at 6-15 us per call, eager Python
             launches would measure the host, not the GPU.
 
-After the K steps, "quantise_65b" times the quantiser (nf4_quantize +
+The decode graphs also cover the q_proj decode shape, W 4096x4096
+N(0, 0.02) (its own rotating copies, x, A, B from the same recipe).
+
+After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
+v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
+N(0, 0.02) drawn and quantised on the device: quantise + DQ, fwd, bwd_dx
+and lora_grads of all seven at M = 2048, r = 64, alpha = 16.  "layer_65b"
+times fwd and bwd_dx of the 65B-shaped layer (8192 hidden, 22016 MLP, bf16
+N(0, 0.015)) at M = 4096, r = 64, alpha = 16.  "hbm_measured" gives the
+copy and read rates that plain torch kernels reach on 1 GiB, as context for
+the fractions of the 8 TB/s peak.
+
+"quantise_65b" times the quantiser (nf4_quantize +
 dq_quantize_scales) over 80 layers of the 65B shapes (7 projections,
 809.5M weights per layer): 8 distinct device-resident layers of bf16
 N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
@@ -71,6 +83,9 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 SHAPES = [(11008, 4096), (4096, 11008)]
 M_TRAIN, RANK, ALPHA = 2048, 16, 32.0
 DECODE_M = (1, 4, 16)
+DECODE_SQUARE = (4096, 4096)   # the q_proj decode shape, W ~ N(0, 0.02)
+LAYER7B = dict(M=2048, r=64, alpha=16.0, std=0.02, seed=6)
+LAYER65B = dict(M=4096, r=64, alpha=16.0, std=0.015, seed=8)
 GEMV_HEADLINE = (4096, 11008, 1)
 ROTATE_BYTES = 512 << 20
 Q65_LAYERS, Q65_DISTINCT = 80, 8
@@ -158,6 +173,27 @@ def cpu_baseline(workloads):
         elapsed = time.perf_counter() - t_all
         if elapsed >= 12.0 or elapsed + t_gemm / reps > 30.0 or reps >= 64:
             break
+    # HBM-bound rows on the decode-shaped weight W 4096x11008 (the metric's
+    # shape): quantise + double-quantise, dequantise, and the decode forward
+    # at M = 1 (dequantise, then the fp64 product with the LoRA term), each
+    # once; the quantiser is plain NumPy, which runs on one thread
+    (N, K), wl = workloads[1]
+    w32 = synth.bf16_to_f32(wl.W)
+    t0 = time.perf_counter()
+    packed, absmax = nf4.quantize_nf4(w32)
+    q8, c2 = nf4.double_quantize(absmax)
+    t_q = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    what = nf4.dequantize(packed, nf4.dequant_scales(q8, c2), w32.size).reshape(N, K)
+    t_dq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    what = nf4.dequantize(packed, nf4.dequant_scales(q8, c2), w32.size).reshape(N, K)
+    linear.linear_forward(f64(wl.x)[:1], what.astype(np.float64), f64(wl.A), f64(wl.B),
+                          wl.alpha, wl.r)
+    t_gv = time.perf_counter() - t0
+    nk = N * K
+    q_rate = nk / t_q
+    w65 = Q65_LAYERS * sum(n * k for (_, n, k) in synth.LLAMA65B_TARGETS)
     total = time.perf_counter() - t_all
     model = "unknown"
     try:
@@ -168,9 +204,20 @@ def cpu_baseline(workloads):
         pass
     return {"value": round(flops / t_gemm / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads),
             "kind": "oracle",
+            "quantise_GBps": round(nk * (2.5 + 9 / 64) / t_q / 1e9, 4),
+            "quantise_s_4096x11008_one_thread": round(t_q, 3),
+            "dequant_GBps": round(nk * (BYTES_PER_WEIGHT + 2) / t_dq / 1e9, 4),
+            "gemv_GBps": round(gemv_bytes(N, K, 1, RANK) / t_gv / 1e9, 4),
+            "gemv_s_per_call_M1": round(t_gv, 3),
+            "quantise_65b_80_layers_s_extrapolated": round(w65 / q_rate, 1),
+            "quantise_65b_note": f"{w65} weights (80 layers x 7 projections of the 65B "
+                                 f"shapes) at the measured one-thread rate of "
+                                 f"{q_rate / 1e6:.1f} M weights/s",
             "sample": "oracle on the bench's own inputs: quantise+DQ+dequant of W 11008x4096 and "
                       "4096x11008, fp64 fwd+bwd_dx over all 2048 tokens (r=16) repeated "
-                      f"{reps}x, LoRA grads once; {total:.1f} s wall, fwd+bwd {t_gemm:.1f} s; "
+                      f"{reps}x, LoRA grads once; quantise+DQ, dequant and one M=1 decode "
+                      f"forward of W 4096x11008 once each; {total:.1f} s wall, fwd+bwd "
+                      f"{t_gemm:.1f} s; "
                       f"cpu_count={os.cpu_count()}, BLAS threads {threads}, {model}"}
 
 
@@ -286,6 +333,117 @@ def dropout_cost(qn, torch, layers, reps=10, p=0.05, seed=7):
             "added_ms_incl_lora_dropout": round(ms_dropped + ms_drop - ms_plain, 4)}
 
 
+def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise, reps=5):
+    """One decoder layer's seven projections on the device: bf16 N(0, std)
+    weights and N(0, 1) activations from torch's generator (seed), A, B
+    N(0, 0.01).  Phases (each over all seven, median of reps after a
+    warm-up): quantise (nf4_quantize + dq_quantize_scales), fwd, bwd_dx and,
+    with with_quantise, lora_grads on the saved u and t."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    bf = torch.bfloat16
+    projs, acts = [], {}
+    for (name, n, k) in targets:
+        W = (torch.randn(n, k, generator=gen, device=dev) * std).to(bf)
+        qw = qn.quantize_weight(W)
+        P = dict(name=name, N=n, K=k, qw=qw, absmax=torch.empty(n * k // 64, device=dev),
+                 A=(torch.randn(r, k, generator=gen, device=dev) * 0.01).to(bf),
+                 B=(torch.randn(n, r, generator=gen, device=dev) * 0.01).to(bf),
+                 u=torch.empty((M, r), dtype=bf, device=dev),
+                 t=torch.empty((M, r), dtype=bf, device=dev),
+                 dA=torch.empty((r, k), device=dev), dB=torch.empty((n, r), device=dev))
+        P["W"] = W if with_quantise else None
+        for key, dim in (("x", k), ("dy", n), ("y", n), ("dx", k)):
+            if (key, dim) not in acts:
+                acts[(key, dim)] = torch.randn(M, dim, generator=gen, device=dev).to(bf)
+            P[key] = acts[(key, dim)]
+        projs.append(P)
+    ws = qn.workspace(max(qn.qn_workspace_bytes(op, M, P["N"], P["K"], r)
+                          for P in projs for op in (0, 1, 2)), dev)
+    torch.cuda.synchronize()
+
+    def run(ph):
+        for P in projs:
+            if ph == "quantise":
+                qn.nf4_quantize(P["W"].reshape(-1), P["qw"].packed, P["absmax"])
+                qn.dq_quantize_scales(P["absmax"], P["qw"].qscale, P["qw"].gscale)
+            elif ph == "fwd":
+                qn.qlora_linear_fwd(P["qw"], P["x"], P["A"], P["B"], r, alpha, y=P["y"],
+                                    u_out=P["u"], ws=ws)
+            elif ph == "bwd":
+                qn.qlora_linear_bwd_dx(P["qw"], P["dy"], P["A"], P["B"], r, alpha, dx=P["dx"],
+                                       t_out=P["t"], ws=ws)
+            else:
+                qn.lora_grads(P["x"], P["dy"], P["A"], P["B"], r, alpha, u=P["u"], t=P["t"],
+                              dA=P["dA"], dB=P["dB"], ws=ws)
+
+    phases = (["quantise"] if with_quantise else []) + ["fwd", "bwd"] + \
+        (["grads"] if with_quantise else [])
+    ms = {}
+    for ph in phases:
+        run(ph)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            run(ph)
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        ms[ph] = float(np.median(ts))
+    flops = sum(linear_flops(P["N"], P["K"], M, r) for P in projs)
+    nk = sum(P["N"] * P["K"] for P in projs)
+    res = {"targets": [f"{P['name']} {P['N']}x{P['K']}" for P in projs], "M": M, "r": r,
+           "alpha": alpha, "weights": nk, "ms": {k: round(v, 4) for k, v in ms.items()},
+           "fwd_TFLOPs": round(flops / (ms["fwd"] * 1e-3) / 1e12, 2),
+           "bwd_TFLOPs": round(flops / (ms["bwd"] * 1e-3) / 1e12, 2)}
+    res["fwd_bwd_TFLOPs"] = round(2 * flops / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12, 2)
+    res["fwd_bwd_frac_mfma"] = round(res["fwd_bwd_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
+    if with_quantise:
+        qb = nk * (2.5 + 9 / 64)
+        res["quantise_GBps"] = round(qb / (ms["quantise"] * 1e-3) / 1e9, 1)
+        res["quantise_frac_hbm"] = round(res["quantise_GBps"] / PEAK_HBM_GBPS, 4)
+        gb = sum(2 * M * (P["N"] + P["K"]) + 2 * 2 * M * r + 4 * r * (P["N"] + P["K"])
+                 for P in projs)
+        res["grads_GBps"] = round(gb / (ms["grads"] * 1e-3) / 1e9, 1)
+        res["grads_frac_hbm"] = round(res["grads_GBps"] / PEAK_HBM_GBPS, 4)
+    del projs, acts, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_peak(torch, dev, reps=10):
+    """Achievable HBM rates measured with plain torch kernels on 1 GiB
+    buffers (context for the fractions of the 8 TB/s peak): a device copy
+    (read + write) and a float32 sum (read only)."""
+    a = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    nbytes = a.numel() * 4
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / reps
+
+    t_copy = timed(lambda: b.copy_(a))
+    t_read = timed(lambda: a.sum())
+    del a, b
+    torch.cuda.empty_cache()
+    return {"copy_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
+            "buffer_bytes": nbytes,
+            "kernels": "torch copy_ (read + write) and torch sum of fp32 (read), 1 GiB each"}
+
+
 def quantise_65b(qn, torch, dev, synth):
     """Quantiser throughput over Q65_LAYERS layers of the 65B shapes."""
     gen = torch.Generator(device=dev)
@@ -371,10 +529,20 @@ def main():
         layers.append(L)
     torch.cuda.synchronize()
 
+    # the q_proj decode shape: W 4096x4096 N(0, 0.02), its own x, A, B
+    sq = synth.decode_layer(max(DECODE_M), *DECODE_SQUARE, seed=2, r=RANK, alpha=ALPHA)
+    Lsq = dict(N=sq.N, K=sq.K, W=bf(sq.W).reshape(sq.N, sq.K), x=bf(sq.x), A=bf(sq.A),
+               B=bf(sq.B))
+    ncopy = int(np.ceil(ROTATE_BYTES / (sq.N * sq.K * BYTES_PER_WEIGHT)))
+    Lsq["copies"] = [qn.quantize_weight(Lsq["W"]) for _ in range(ncopy)]
+    Lsq["ydec"] = {m: torch.empty((m, sq.N), dtype=torch.bfloat16, device=dev) for m in DECODE_M}
+    Lsq["wsdec"] = qn.workspace(qn.qn_workspace_bytes(0, max(DECODE_M), sq.N, sq.K, RANK), dev)
+    torch.cuda.synchronize()
+
     # decode graphs: one per (shape, M), each call on the next copy
     stream = torch.cuda.current_stream()
     graphs = {}
-    for L in layers:
+    for L in layers + [Lsq]:
         for m in DECODE_M:
             def calls(L=L, m=m):
                 for c in L["copies"]:
@@ -518,7 +686,8 @@ def main():
         "config": {"workload": "training-step linear at the 7B MLP shapes, W 11008x4096 and "
                                "4096x11008 NF4+double-quant, M=2048 tokens, LoRA r=16 alpha=32: "
                                "quantise+DQ, dequant, fwd, bwd_dx, lora_grads; plus decode "
-                               "(LoRA-down + dequant GEMV) at M=1,4,16 on rotating copies",
+                               "(LoRA-down + dequant GEMV) at M=1,4,16 on rotating copies of "
+                               "both MLP weights and of W 4096x4096 N(0,0.02)",
                    "M": M_TRAIN, "r": RANK, "alpha": ALPHA,
                    "weights": [f"{n}x{k}" for n, k in SHAPES], "decode_M": list(DECODE_M)},
         "gemv": {"shape": f"{hN}x{hK}", "M": hM, "GBps": head["GBps"],
@@ -535,6 +704,15 @@ def main():
                      "traffic": traffic,
                      "us_per_launch": round(gemm_us_per_launch, 2)},
     }
+    for L in layers + [Lsq]:
+        del L["copies"]
+    del graphs
+    torch.cuda.empty_cache()
+    out["layer_7b"] = decoder_layer(qn, torch, dev, synth.LLAMA7B_TARGETS, with_quantise=True,
+                                    **LAYER7B)
+    out["layer_65b"] = decoder_layer(qn, torch, dev, synth.LLAMA65B_TARGETS,
+                                     with_quantise=False, **LAYER65B)
+    out["hbm_measured"] = hbm_peak(torch, dev)
     out["unfused_context"] = unfused_context(qn, torch, layers)
     out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
     out["adamw_7b_lora"] = adamw_7b_lora(qn, torch, dev, synth)
