@@ -6,7 +6,8 @@ linear workload at the Llama-7B MLP shapes, for both orientations of the
 weight (gate/up W 11008x4096 and down W 4096x11008; bf16 Student-t(5)
 weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
 
-  quantise  nf4_quantize + dq_quantize_scales of the bf16 weight
+  quantise  nf4_quantize_dq of the bf16 weight (quantise + double-quantise
+            in one launch)
   dequant   nf4_dequant to bf16 (the standalone bit-exact expansion)
   gemm      qlora_linear_fwd    at M = 2048 with r = 0: exactly one launch
             of the fused dequant GEMM kernel per call (the roofline kernel)
@@ -26,15 +27,14 @@ N(0, 0.02) (its own rotating copies, x, A, B from the same recipe).
 
 After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
 v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
-N(0, 0.02) drawn and quantised on the device: quantise + DQ, fwd, bwd_dx
+N(0, 0.02) drawn and quantised on the device: quantise + DQ (fused), fwd, bwd_dx
 and lora_grads of all seven at M = 2048, r = 64, alpha = 16.  "layer_65b"
 times fwd and bwd_dx of the 65B-shaped layer (8192 hidden, 22016 MLP, bf16
 N(0, 0.015)) at M = 4096, r = 64, alpha = 16.  "hbm_measured" gives the
 copy and read rates that plain torch kernels reach on 1 GiB, as context for
 the fractions of the 8 TB/s peak.
 
-"quantise_65b" times the quantiser (nf4_quantize +
-dq_quantize_scales) over 80 layers of the 65B shapes (7 projections,
+"quantise_65b" times the quantiser (nf4_quantize_dq) over 80 layers of the 65B shapes (7 projections,
 809.5M weights per layer): 8 distinct device-resident layers of bf16
 N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
 beyond the Infinity Cache) quantised in turn 10 times over.
@@ -346,7 +346,7 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     for (name, n, k) in targets:
         W = (torch.randn(n, k, generator=gen, device=dev) * std).to(bf)
         qw = qn.quantize_weight(W)
-        P = dict(name=name, N=n, K=k, qw=qw, absmax=torch.empty(n * k // 64, device=dev),
+        P = dict(name=name, N=n, K=k, qw=qw,
                  A=(torch.randn(r, k, generator=gen, device=dev) * 0.01).to(bf),
                  B=(torch.randn(n, r, generator=gen, device=dev) * 0.01).to(bf),
                  u=torch.empty((M, r), dtype=bf, device=dev),
@@ -365,8 +365,8 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     def run(ph):
         for P in projs:
             if ph == "quantise":
-                qn.nf4_quantize(P["W"].reshape(-1), P["qw"].packed, P["absmax"])
-                qn.dq_quantize_scales(P["absmax"], P["qw"].qscale, P["qw"].gscale)
+                qn.nf4_quantize_dq(P["W"].reshape(-1), packed=P["qw"].packed,
+                                   qscale=P["qw"].qscale, gscale=P["qw"].gscale)
             elif ph == "fwd":
                 qn.qlora_linear_fwd(P["qw"], P["x"], P["A"], P["B"], r, alpha, y=P["y"],
                                     u_out=P["u"], ws=ws)
@@ -402,7 +402,7 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     res["fwd_bwd_TFLOPs"] = round(2 * flops / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12, 2)
     res["fwd_bwd_frac_mfma"] = round(res["fwd_bwd_TFLOPs"] / PEAK_BF16_TFLOPS, 4)
     if with_quantise:
-        qb = nk * (2.5 + 9 / 64)
+        qb = nk * (2 + BYTES_PER_WEIGHT)
         res["quantise_GBps"] = round(qb / (ms["quantise"] * 1e-3) / 1e9, 1)
         res["quantise_frac_hbm"] = round(res["quantise_GBps"] / PEAK_HBM_GBPS, 4)
         gb = sum(2 * M * (P["N"] + P["K"]) + 2 * 2 * M * r + 4 * r * (P["N"] + P["K"])
@@ -454,7 +454,6 @@ def quantise_65b(qn, torch, dev, synth):
         for (_, n, k) in synth.LLAMA65B_TARGETS:
             w = (torch.randn(n * k, generator=gen, device=dev) * 0.015).to(torch.bfloat16)
             proj.append((w, torch.empty(n * k // 2, dtype=torch.uint8, device=dev),
-                         torch.empty(n * k // 64, dtype=torch.float32, device=dev),
                          torch.empty(n * k // 64, dtype=torch.uint8, device=dev),
                          torch.empty(-(-n * k // (64 * 256)), dtype=torch.float32, device=dev)))
         layers.append(proj)
@@ -462,9 +461,8 @@ def quantise_65b(qn, torch, dev, synth):
 
     def run():
         for i in range(Q65_LAYERS):
-            for (w, packed, absmax, q8, c2) in layers[i % Q65_DISTINCT]:
-                qn.nf4_quantize(w, packed, absmax)
-                qn.dq_quantize_scales(absmax, q8, c2)
+            for (w, packed, q8, c2) in layers[i % Q65_DISTINCT]:
+                qn.nf4_quantize_dq(w, packed=packed, qscale=q8, gscale=c2)
 
     run()  # warm-up
     torch.cuda.synchronize()
@@ -475,8 +473,8 @@ def quantise_65b(qn, torch, dev, synth):
     e.record()
     torch.cuda.synchronize()
     ms = s.elapsed_time(e)
-    # read bf16 W, write codes + fp32 absmax; DQ: read absmax, write q8 + c2
-    nbytes = Q65_LAYERS * numel * (2 + 0.5 + (4 + 4 + 1) / 64)
+    # read bf16 W, write the codes, q8 and c2
+    nbytes = Q65_LAYERS * numel * (2 + BYTES_PER_WEIGHT)
     gbps = nbytes / (ms * 1e-3) / 1e9
     del layers
     torch.cuda.empty_cache()
@@ -511,7 +509,6 @@ def main():
         L = dict(N=N, K=K, W=bf(wl.W).reshape(N, K), x=bf(wl.x), A=bf(wl.A), B=bf(wl.B),
                  dy=bf(wl.dy))
         L["qw"] = qn.quantize_weight(L["W"])
-        L["absmax_buf"] = torch.empty(N * K // 64, dtype=torch.float32, device=dev)
         L["deq"] = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
         L["y"] = torch.empty((M_TRAIN, N), dtype=torch.bfloat16, device=dev)
         L["dx"] = torch.empty((M_TRAIN, K), dtype=torch.bfloat16, device=dev)
@@ -579,8 +576,8 @@ def main():
             for L in layers:
                 qw = L["qw"]
                 if ph == "quantise":
-                    qn.nf4_quantize(L["W"].reshape(-1), qw.packed, L["absmax_buf"])
-                    qn.dq_quantize_scales(L["absmax_buf"], qw.qscale, qw.gscale)
+                    qn.nf4_quantize_dq(L["W"].reshape(-1), packed=qw.packed, qscale=qw.qscale,
+                                       gscale=qw.gscale)
                 elif ph == "dequant":
                     qn.nf4_dequant(qw, torch.bfloat16, out=L["deq"])
                 elif ph == "gemm":
@@ -641,9 +638,8 @@ def main():
     fwd_flops = sum(linear_flops(L["N"], L["K"], M_TRAIN, RANK) for L in layers)
     gemm_flops = sum(2 * M_TRAIN * L["N"] * L["K"] for L in layers)  # r = 0 calls
     gemm_tflops = 2 * fwd_flops / ((ms["fwd"] + ms["bwd"]) * 1e-3) / 1e12
-    # quantise: read bf16 W, write codes + fp32 absmax; DQ: read absmax, write q8, c2
-    q_bytes = sum(L["N"] * L["K"] * (2 + 0.5) + L["N"] * L["K"] / 64 * (4 + 4 + 1)
-                  for L in layers)
+    # quantise + DQ in one launch: read bf16 W, write the codes, q8 and c2
+    q_bytes = sum(L["N"] * L["K"] * (2 + BYTES_PER_WEIGHT) for L in layers)
     dq_bytes = sum(L["N"] * L["K"] * (BYTES_PER_WEIGHT + 2) for L in layers)
     # grads: read x, dy (bf16) and the saved u, t (bf16); write dA, dB (fp32)
     gr_bytes = sum(2 * M_TRAIN * (L["N"] + L["K"]) + 2 * 2 * M_TRAIN * RANK

@@ -29,7 +29,7 @@ EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scal
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
            "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc",
-           "dq_quantize_scales_centred")
+           "dq_quantize_scales_centred", "nf4_quantize_dq")
 
 
 class QnError(RuntimeError):
@@ -71,6 +71,7 @@ def load_library():
         "dq_quantize_scales": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "dq_quantize_scales_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "dq_quantize_scales_centred": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
+        "nf4_quantize_dq": (ctypes.c_int, [vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
         "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
         "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -186,6 +187,36 @@ def fp4_quantize(w, packed=None, absmax=None, stream=None):
     return _quantize("fp4_quantize", w, packed, absmax, stream)
 
 
+def nf4_quantize_dq(w, quant_type="nf4", scale_type="u8", packed=None, qscale=None, gscale=None,
+                    absmax=None, stream=None):
+    """Quantisation and double quantisation in one launch: returns (packed,
+    qscale, gscale); the block constants are written to absmax only when a
+    tensor is given for them."""
+    torch = _torch()
+    lib = load_library()
+    if quant_type not in _QUANT_TYPES or scale_type not in ("u8", "fp8"):
+        raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8' or 'fp8'")
+    if w.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("nf4_quantize_dq: weights must be float32 or bfloat16")
+    _dev(w, w.dtype, name="w")
+    n = w.numel()
+    nb = -(-n // BLOCKSIZE)
+    ng = -(-nb // GROUP)
+    dev = w.device
+    packed = torch.empty(n // 2, dtype=torch.uint8, device=dev) if packed is None else packed
+    qscale = torch.empty(nb, dtype=torch.uint8, device=dev) if qscale is None else qscale
+    gscale = torch.empty(ng, dtype=torch.float32, device=dev) if gscale is None else gscale
+    _dev(packed, torch.uint8, n // 2, "packed")
+    _dev(qscale, torch.uint8, nb, "qscale")
+    _dev(gscale, torch.float32, ng, "gscale")
+    _dev(absmax, torch.float32, nb, "absmax")
+    dt = QN_F32 if w.dtype == torch.float32 else QN_BF16
+    _check("nf4_quantize_dq", lib.nf4_quantize_dq(
+        _ptr(w), dt, n, BLOCKSIZE, GROUP, _QUANT_TYPES[quant_type], _SCALE_TYPES[scale_type],
+        _ptr(packed), _ptr(absmax), _ptr(qscale), _ptr(gscale), _stream(stream)))
+    return packed, qscale, gscale
+
+
 def _quantize(fn, w, packed, absmax, stream):
     torch = _torch()
     lib = load_library()
@@ -259,17 +290,17 @@ def quantize_weight(w, double_quant=True, stream=None, quant_type="nf4", scale_t
         raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8', 'fp8' or "
                          "'centred'")
     N, K = w.shape
+    if double_quant and scale_type != "centred":
+        packed, qscale, gscale = nf4_quantize_dq(w, quant_type, scale_type, stream=stream)
+        return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
+                           scale_type=scale_type)
     quant = fp4_quantize if quant_type == "fp4" else nf4_quantize
     packed, absmax = quant(w, stream=stream)
     if not double_quant:
         return QuantWeight(packed, N, K, absmax=absmax, quant_type=quant_type)
-    if scale_type == "centred":
-        qscale, gscale, offset = dq_quantize_scales_centred(absmax, stream=stream)
-        return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
-                           scale_type=scale_type, offset=offset)
-    qscale, gscale = dq_quantize_scales(absmax, stream=stream, fp8=scale_type == "fp8")
+    qscale, gscale, offset = dq_quantize_scales_centred(absmax, stream=stream)
     return QuantWeight(packed, N, K, qscale=qscale, gscale=gscale, quant_type=quant_type,
-                       scale_type=scale_type)
+                       scale_type=scale_type, offset=offset)
 
 
 def nf4_dequant(qw, out_dtype=None, out=None, stream=None):

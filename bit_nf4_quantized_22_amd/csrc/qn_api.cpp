@@ -283,6 +283,27 @@ int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t group,
   return dq(true, absmax, nblocks, group, qscale, gscale, stream);
 }
 
+int nf4_quantize_dq(const void* w, int32_t dtype, int64_t numel, int32_t blocksize, int32_t group,
+                    int32_t quant_type, int32_t scale_type, uint8_t* packed, float* absmax,
+                    uint8_t* qscale, float* gscale, void* stream) {
+  if (blocksize != kBlock || group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (dtype != QN_F32 && dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
+  if (quant_type != QN_NF4 && quant_type != QN_FP4) return QN_ERR_UNSUPPORTED;
+  if (scale_type != QN_SCALE_U8 && scale_type != QN_SCALE_FP8) return QN_ERR_UNSUPPORTED;
+  if (numel < 0 || (numel & 1)) return QN_ERR_SHAPE;
+  if (numel == 0) return QN_OK;
+  if (!w || !packed || !qscale || !gscale) return QN_ERR_NULL;
+  if (!aligned(w, 16) || !aligned(packed, 16) || !aligned(gscale, 4) ||
+      (absmax && !aligned(absmax, 4)))
+    return QN_ERR_ALIGN;
+  const int qt = quant_type == QN_FP4 ? qn::kQuantFP4 : qn::kQuantNF4;
+  if (!qn::tables(qt)) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_quantize_dq(w, dtype == QN_BF16, numel, qt,
+                                           scale_type == QN_SCALE_FP8, packed, absmax, qscale,
+                                           gscale, as_stream(stream)));
+}
+
 int dq_quantize_scales_centred(const float* absmax, int64_t nblocks, int32_t group,
                                uint8_t* qscale, float* gscale, float* offset, void* stream) {
   if (group != kGroup) return QN_ERR_UNSUPPORTED;

@@ -33,6 +33,11 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, int quant_ty
                            uint8_t* packed, float* absmax, hipStream_t s);
 hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qscale,
                      float* gscale, hipStream_t s);
+// Both in one launch (one workgroup per 256-block group); absmax may be
+// nullptr.
+hipError_t launch_quantize_dq(const void* w, bool bf16, int64_t numel, int quant_type, bool fp8,
+                              uint8_t* packed, float* absmax, uint8_t* qscale, float* gscale,
+                              hipStream_t s);
 // Mean-centred level-2 code: mu (pairwise fp64 sum of the constants / n,
 // written to *mu), then per 256-group c2 = max |c - mu| and signed codes.
 // gscale doubles as scratch for the partial sums before its final values.

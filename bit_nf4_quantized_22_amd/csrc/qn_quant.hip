@@ -106,14 +106,11 @@ __device__ __forceinline__ void fill_buckets(QuantBucket* sbk, const QuantParams
 //   exact path q = fl32(w / c) by IEEE division, then the same lookup
 //              (q = w for an all-zero block: the code of v = 0).
 // Writes the 8 packed bytes (numel is even) and returns the block constant.
-template <bool kBf16>
-__device__ __forceinline__ float quantize16(const QuantBucket* sbk, const QuantParams& P,
-                                            const void* __restrict__ w, int64_t e0, int64_t numel,
-                                            uint8_t* __restrict__ packed) {
+__device__ __forceinline__ float quantize16_loaded(const QuantBucket* sbk, const QuantParams& P,
+                                                   const float (&x)[16], int64_t e0,
+                                                   int64_t numel, uint8_t* __restrict__ packed) {
   const float sc = P.scale;
   const float top = static_cast<float>(P.nbuckets - 1);
-  float x[16];
-  load16<kBf16>(w, e0, numel, x);
 
   float m = 0.0f;
 #pragma unroll
@@ -164,6 +161,15 @@ __device__ __forceinline__ float quantize16(const QuantBucket* sbk, const QuantP
 }
 
 template <bool kBf16>
+__device__ __forceinline__ float quantize16(const QuantBucket* sbk, const QuantParams& P,
+                                            const void* __restrict__ w, int64_t e0, int64_t numel,
+                                            uint8_t* __restrict__ packed) {
+  float x[16];
+  load16<kBf16>(w, e0, numel, x);
+  return quantize16_loaded(sbk, P, x, e0, numel, packed);
+}
+
+template <bool kBf16>
 __global__ __launch_bounds__(kQThreads) void nf4_quantize_kernel(
     const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
     float* __restrict__ absmax, QuantParams P) {
@@ -205,6 +211,76 @@ __device__ __forceinline__ uint8_t dq_code(float c, float c2, const float* sthr)
     }
   }
   return static_cast<uint8_t>(q);
+}
+
+// Quantisation and double quantisation in one launch: a workgroup takes
+// one group of 256 blocks (16384 weights: 4 x 16 per lane; for bf16 all 64
+// are loaded before the first is quantised, 128 bytes per lane in flight),
+// keeps the group's block constants in LDS and ends with their level-2
+// codes and the group maximum: the same values as nf4_quantize_kernel
+// followed by dq_quantize_kernel.  The block constants themselves are
+// written too when absmax is not null.
+constexpr int kQDPasses = 4;
+
+template <bool kBf16, bool kFP8>
+__global__ __launch_bounds__(kQThreads) void quantize_dq_kernel(
+    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, uint8_t* __restrict__ qscale, float* __restrict__ gscale,
+    QuantParams P) {
+  static_assert(kQDPasses * kQPerGroup == 256 * 64, "one workgroup per 256-block group");
+  __shared__ QuantBucket sbk[kMaxBuckets];
+  __shared__ float sthr[256];
+  __shared__ float sconst[256];
+  __shared__ float smax[4];
+  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kQDPasses * kQPerGroup);
+  const bool full = g0 + kQDPasses * kQPerGroup <= numel;  // uniform
+  // whole groups of bf16 weights: the raw 16-byte words of all passes are
+  // loaded first (32 registers) and widened pass by pass
+  uint4 raw[kBf16 ? kQDPasses : 1][2];
+  if (kBf16 && full) {
+#pragma unroll
+    for (int s = 0; s < (kBf16 ? kQDPasses : 1); ++s) {
+      const uint4* p = reinterpret_cast<const uint4*>(
+          static_cast<const uint16_t*>(w) + g0 +
+          (static_cast<int64_t>(s) * kQThreads + threadIdx.x) * kQPerThread);
+      raw[s][0] = p[0];
+      raw[s][1] = p[1];
+    }
+  }
+  fill_buckets(sbk, P, kQThreads);
+  if constexpr (!kFP8) fill_l8_thresholds(sthr, threadIdx.x);
+  __syncthreads();
+  float cmax = 0.0f;
+#pragma unroll
+  for (int s = 0; s < kQDPasses; ++s) {
+    const int64_t e0 = g0 + (static_cast<int64_t>(s) * kQThreads + threadIdx.x) * kQPerThread;
+    float x[16];
+    if (kBf16 && full) {
+      const uint4 a = raw[kBf16 ? s : 0][0], b = raw[kBf16 ? s : 0][1];
+      const uint32_t v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x[2 * i] = bf16_lo(v[i]);
+        x[2 * i + 1] = bf16_hi(v[i]);
+      }
+    } else {
+      load16<kBf16>(w, e0, numel, x);
+    }
+    const float c = quantize16_loaded(sbk, P, x, e0, numel, packed);  // 0 past numel
+    if ((threadIdx.x & 3) == 0) {
+      sconst[s * (kQThreads / 4) + threadIdx.x / 4] = c;
+      if (absmax && e0 < numel) absmax[e0 / 64] = c;
+    }
+    cmax = fmaxf(cmax, c);
+  }
+  const float wm = wave_max(cmax);
+  if ((threadIdx.x & 63) == 0) smax[threadIdx.x >> 6] = wm;
+  __syncthreads();
+  const float c2 = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  const int64_t nblocks = (numel + 63) / 64;
+  const int64_t bi = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (threadIdx.x == 0) gscale[blockIdx.x] = c2;
+  if (bi < nblocks) qscale[bi] = dq_code<kFP8>(sconst[threadIdx.x], c2, sthr);
 }
 
 // One workgroup of 256 lanes per group of 256 block constants.
@@ -404,6 +480,26 @@ hipError_t launch_quantize(const void* w, bool bf16, int64_t numel, int quant_ty
   else
     hipLaunchKernelGGL(nf4_quantize_kernel<false>, dim3(static_cast<uint32_t>(groups)),
                        dim3(kQThreads), 0, s, w, numel, packed, absmax, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dq(const void* w, bool bf16, int64_t numel, int quant_type, bool fp8,
+                              uint8_t* packed, float* absmax, uint8_t* qscale, float* gscale,
+                              hipStream_t s) {
+  if (numel == 0) return hipSuccess;
+  const Tables* t = tables(quant_type);
+  QuantParams P;
+  P.scale = t->bucket_scale;
+  P.nbuckets = static_cast<uint32_t>(t->nbuckets);
+  for (int i = 0; i < 15; ++i) P.thr[i] = t->thr[i];
+  const int64_t per = static_cast<int64_t>(kQDPasses) * kQPerGroup;
+  const dim3 grid(static_cast<uint32_t>((numel + per - 1) / per));
+#define QN_QDQ(B, F)                                                                            \
+  if (bf16 == B && fp8 == F)                                                                   \
+    hipLaunchKernelGGL((quantize_dq_kernel<B, F>), grid, dim3(kQThreads), 0, s, w, numel, packed, \
+                       absmax, qscale, gscale, P);
+  QN_QDQ(true, false) QN_QDQ(true, true) QN_QDQ(false, false) QN_QDQ(false, true)
+#undef QN_QDQ
   return hipGetLastError();
 }
 

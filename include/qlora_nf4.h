@@ -192,6 +192,24 @@ QN_API int dq_quantize_scales_fp8(const float* absmax, int64_t nblocks, int32_t 
                                   uint8_t* qscale, float* gscale, void* stream);
 
 /*
+ * nf4_quantize_dq -- nf4_quantize (or fp4_quantize) and dq_quantize_scales
+ * (or dq_quantize_scales_fp8) in one call: [rkmt] §2.2.1-2.2.2 and [kwkr]
+ * §3.1, the 4-bit codes and the 8-bit codes of their block constants.
+ * Same packed, qscale and gscale bytes as the two calls, bit for bit; one
+ * pass over the weight, no round trip of the constants through memory.
+ *   quant_type  QN_NF4 or QN_FP4;  scale_type QN_SCALE_U8 or QN_SCALE_FP8
+ *               (the centred code needs the mean of all constants first:
+ *               QN_ERR_UNSUPPORTED here, use dq_quantize_scales_centred).
+ *   absmax  fp32[ceil(numel/64)] out (the block constants), or NULL to
+ *           skip writing them.
+ * Other arguments and errors as nf4_quantize and dq_quantize_scales.
+ */
+QN_API int nf4_quantize_dq(const void* w, int32_t dtype, int64_t numel, int32_t blocksize,
+                           int32_t group, int32_t quant_type, int32_t scale_type,
+                           uint8_t* packed, float* absmax, uint8_t* qscale, float* gscale,
+                           void* stream);
+
+/*
  * dq_quantize_scales_centred -- mean-centred double quantisation.
  * [rkmt] §2.2.2 and [kwkr] §3.1 quantise the block constants to 8 bits a
  * second time; the publication the pages summarise subtracts the constants'

@@ -297,3 +297,23 @@ def test_noalloc_forward_host_checks(lib):
                None) == qn.QN_ERR_NULL
     assert fwd(ctypes.byref(w), None, 32, FAKE, FAKE, 8, 16.0, FAKE, None,
                None) == qn.QN_ERR_NULL
+
+
+def test_fused_quantise_argument_errors(lib):
+    f = lib.nf4_quantize_dq
+    args = lambda **k: dict(dict(w=FAKE, dt=qn.QN_BF16, n=128, bs=64, grp=256, qt=0, st=0,
+                                 p=FAKE, a=None, q=FAKE, g=FAKE), **k)
+    call = lambda d: f(d["w"], d["dt"], d["n"], d["bs"], d["grp"], d["qt"], d["st"], d["p"],
+                       d["a"], d["q"], d["g"], None)
+    assert call(args(bs=32)) == qn.QN_ERR_UNSUPPORTED
+    assert call(args(grp=128)) == qn.QN_ERR_UNSUPPORTED
+    assert call(args(st=qn.QN_SCALE_CENTRED)) == qn.QN_ERR_UNSUPPORTED
+    assert call(args(qt=2)) == qn.QN_ERR_UNSUPPORTED
+    assert call(args(dt=2)) == qn.QN_ERR_UNSUPPORTED
+    assert call(args(n=63)) == qn.QN_ERR_SHAPE
+    assert call(args(n=-2)) == qn.QN_ERR_SHAPE
+    assert call(args(q=None)) == qn.QN_ERR_NULL
+    assert call(args(w=None)) == qn.QN_ERR_NULL
+    assert call(args(w=ODD)) == qn.QN_ERR_ALIGN
+    assert call(args(a=ODD)) == qn.QN_ERR_ALIGN
+    assert call(args(n=0, w=None, p=None, q=None, g=None)) == qn.QN_OK

@@ -178,3 +178,37 @@ def test_round_trip_is_idempotent_on_device():
     assert torch.equal(qw.gscale, qw2.gscale)
     live = (qw.qscale > 0).repeat_interleave(32)
     assert torch.equal(qw.packed[live], qw2.packed[live])
+
+
+@pytest.mark.parametrize("numel", [64, 4096 + 64 * 3, 16384, 16384 * 3 + 64 * 5 + 32, 4096 * 4096])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,scale", [("nf4", "u8"), ("nf4", "fp8"), ("fp4", "u8")])
+def test_fused_quantise_dq_equals_the_two_calls(numel, dtype, kind, scale):
+    """nf4_quantize_dq (one launch per 256-block group) writes the same codes,
+    block constants, level-2 codes and group maxima as the quantiser followed
+    by the double quantiser, for sizes with partial blocks and partial groups,
+    and both agree with the oracle."""
+    rng = np.random.default_rng(numel)
+    W = (rng.standard_t(5, numel) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        W = synth.bf16_bits(W)
+    w = weight_dev(W, dtype).reshape(-1)
+    quant = qn.fp4_quantize if kind == "fp4" else qn.nf4_quantize
+    p1, a1 = quant(w)
+    q1, g1 = qn.dq_quantize_scales(a1, fp8=scale == "fp8")
+    a2 = torch.full_like(a1, float("nan"))
+    p2, q2, g2 = qn.nf4_quantize_dq(w, kind, scale, absmax=a2)
+    p3, q3, g3 = qn.nf4_quantize_dq(w, kind, scale)  # no absmax output
+    torch.cuda.synchronize()
+    for a, b in ((p1, p2), (q1, q2), (p1, p3), (q1, q3)):
+        assert torch.equal(a, b)
+    for a, b in ((a1, a2), (g1, g2), (g1, g3)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    if numel <= 16384 * 4:
+        from oracle import codebooks
+        op, oa = codebooks.quantize_4bit(weight_f32(W, dtype), kind)
+        oq, og = (codebooks.double_quantize_fp8(oa) if scale == "fp8"
+                  else nf4.double_quantize(oa))
+        assert np.array_equal(p2.cpu().numpy(), op)
+        assert np.array_equal(q2.cpu().numpy(), oq)
+        assert np.array_equal(g2.cpu().numpy().view(np.uint32), og.view(np.uint32))
