@@ -23,7 +23,9 @@ weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
             launches would measure the host, not the GPU.
 
 The decode graphs also cover the q_proj decode shape, W 4096x4096
-N(0, 0.02) (its own rotating copies, x, A, B from the same recipe).
+N(0, 0.02) (its own rotating copies, x, A, B from the same recipe), and
+each shape at M = 1 without the LoRA term (r = 0: the GEMV kernel is then
+the whole call; "gemv.kernel_only_r0").
 
 After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
 v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
@@ -31,8 +33,9 @@ N(0, 0.02) drawn and quantised on the device: quantise + DQ (fused), fwd, bwd_dx
 and lora_grads of all seven at M = 2048, r = 64, alpha = 16.  "layer_65b"
 times fwd and bwd_dx of the 65B-shaped layer (8192 hidden, 22016 MLP, bf16
 N(0, 0.015)) at M = 4096, r = 64, alpha = 16.  "hbm_measured" gives the
-copy and read rates that plain torch kernels reach on 1 GiB, as context for
-the fractions of the 8 TB/s peak.
+streaming-read rate of qn_hbm_read_probe (16-byte loads, read only) and
+the copy and read rates of plain torch kernels on 1 GiB, as context for the
+fractions of the 8 TB/s peak.
 
 "quantise_65b" times the quantiser (nf4_quantize_dq) over 80 layers of the 65B shapes (7 projections,
 809.5M weights per layer): 8 distinct device-resident layers of bf16
@@ -414,7 +417,7 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     return res
 
 
-def hbm_peak(torch, dev, reps=10):
+def hbm_peak(qn, torch, dev, reps=10):
     """Achievable HBM rates measured with plain torch kernels on 1 GiB
     buffers (context for the fractions of the 8 TB/s peak): a device copy
     (read + write) and a float32 sum (read only)."""
@@ -434,14 +437,18 @@ def hbm_peak(torch, dev, reps=10):
         torch.cuda.synchronize()
         return s.elapsed_time(e) / reps
 
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
     t_copy = timed(lambda: b.copy_(a))
     t_read = timed(lambda: a.sum())
+    t_probe = timed(lambda: qn.hbm_read_probe(a, sink))
     del a, b
     torch.cuda.empty_cache()
-    return {"copy_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+    return {"read_probe_GBps": round(nbytes / (t_probe * 1e-3) / 1e9, 1),
+            "copy_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
             "read_GBps": round(nbytes / (t_read * 1e-3) / 1e9, 1),
             "buffer_bytes": nbytes,
-            "kernels": "torch copy_ (read + write) and torch sum of fp32 (read), 1 GiB each"}
+            "kernels": "qn_hbm_read_probe (16-byte streaming loads, read only), torch copy_ "
+                       "(read + write) and torch sum of fp32 (read), 1 GiB each"}
 
 
 def quantise_65b(qn, torch, dev, synth):
@@ -539,11 +546,14 @@ def main():
     # decode graphs: one per (shape, M), each call on the next copy
     stream = torch.cuda.current_stream()
     graphs = {}
+    # (N, K, M, r): the decode calls with the LoRA term, and at M = 1 also
+    # without it (r = 0: the GEMV kernel is the whole call)
     for L in layers + [Lsq]:
-        for m in DECODE_M:
-            def calls(L=L, m=m):
+        for m, r in [(m, RANK) for m in DECODE_M] + [(1, 0)]:
+            def calls(L=L, m=m, r=r):
                 for c in L["copies"]:
-                    qn.qlora_linear_fwd(c, L["x"][:m], L["A"], L["B"], RANK, ALPHA,
+                    qn.qlora_linear_fwd(c, L["x"][:m], L["A"] if r else None,
+                                        L["B"] if r else None, r, ALPHA,
                                         y=L["ydec"][m], ws=L["wsdec"])
             gs = torch.cuda.Stream()
             gs.wait_stream(stream)
@@ -553,7 +563,7 @@ def main():
                 with torch.cuda.graph(g, stream=gs):
                     calls()
             stream.wait_stream(gs)
-            graphs[(L["N"], L["K"], m)] = (g, len(L["copies"]))
+            graphs[(L["N"], L["K"], m, r)] = (g, len(L["copies"]))
     torch.cuda.synchronize()
 
     phases = ["quantise", "dequant", "gemm", "fwd", "bwd", "grads", "merge", "gemv"]
@@ -627,11 +637,12 @@ def main():
     for key, (g, n) in graphs.items():
         t = mean_ms(("gemv",) + key)
         gemv_ms_total += t
-        N, K, m = key
+        N, K, m, r = key
         us = t * 1e3 / n
-        gbps = gemv_bytes(N, K, m, RANK) / (us * 1e-6) / 1e9
-        gemv[f"{N}x{K}_M{m}"] = {"us_per_call": round(us, 3), "GBps": round(gbps, 1),
-                                 "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
+        gbps = gemv_bytes(N, K, m, r) / (us * 1e-6) / 1e9
+        gemv[f"{N}x{K}_M{m}" + ("" if r else "_r0")] = {
+            "us_per_call": round(us, 3), "GBps": round(gbps, 1),
+            "frac_hbm": round(gbps / PEAK_HBM_GBPS, 4)}
     ms["gemv"] = gemv_ms_total
     step_ms = wall / args.steps * 1e3
 
@@ -688,6 +699,7 @@ def main():
                    "weights": [f"{n}x{k}" for n, k in SHAPES], "decode_M": list(DECODE_M)},
         "gemv": {"shape": f"{hN}x{hK}", "M": hM, "GBps": head["GBps"],
                  "frac_hbm": head["frac_hbm"], "us_per_call": head["us_per_call"],
+                 "kernel_only_r0": gemv[f"{hN}x{hK}_M{hM}_r0"],
                  "all": gemv},
         "phases_ms": {k: round(v, 4) for k, v in ms.items()},
         "phases_ms_p10_p50_p90": spread,
@@ -708,7 +720,7 @@ def main():
                                     **LAYER7B)
     out["layer_65b"] = decoder_layer(qn, torch, dev, synth.LLAMA65B_TARGETS,
                                      with_quantise=False, **LAYER65B)
-    out["hbm_measured"] = hbm_peak(torch, dev)
+    out["hbm_measured"] = hbm_peak(qn, torch, dev)
     out["unfused_context"] = unfused_context(qn, torch, layers)
     out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
     out["adamw_7b_lora"] = adamw_7b_lora(qn, torch, dev, synth)

@@ -29,7 +29,7 @@ EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scal
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
            "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc",
-           "dq_quantize_scales_centred", "nf4_quantize_dq")
+           "dq_quantize_scales_centred", "nf4_quantize_dq", "qn_hbm_read_probe")
 
 
 class QnError(RuntimeError):
@@ -72,6 +72,7 @@ def load_library():
         "dq_quantize_scales_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "dq_quantize_scales_centred": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
         "nf4_quantize_dq": (ctypes.c_int, [vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "qn_hbm_read_probe": (ctypes.c_int, [vp, i64, vp, vp]),
         "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
         "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
         "qlora_linear_fwd": (ctypes.c_int, [wp, vp, i64, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -342,6 +343,16 @@ def qlora_linear_fwd_dropout(qw, x, x_drop, A, B, r, alpha, y=None, u_out=None, 
                              stream=None):
     """y = x W^T + (alpha/r) (x_drop A^T) B^T, x_drop from lora_dropout."""
     return _fwd(qw, x, x_drop, A, B, r, alpha, y, u_out, ws, stream)
+
+
+def hbm_read_probe(buf, sink, stream=None):
+    """Streaming read of a contiguous device tensor (a measurement aid);
+    sink is a device tensor of at least 4 bytes."""
+    if not buf.is_cuda or not buf.is_contiguous() or not sink.is_cuda:
+        raise ValueError("hbm_read_probe: contiguous device tensors required")
+    nbytes = buf.numel() * buf.element_size()
+    _check("qn_hbm_read_probe", load_library().qn_hbm_read_probe(
+        _ptr(buf), nbytes - nbytes % 16, _ptr(sink), _stream(stream)))
 
 
 def qlora_linear_fwd_noalloc(qw, x, A, B, r, alpha, y, u_out=None, stream=None):

@@ -346,6 +346,15 @@ int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_b
   return fwd_impl(w, x, x, M, A, B, r, alpha, y, u_out, ws, ws_bytes, stream);
 }
 
+int qn_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 != 0) return QN_ERR_SHAPE;
+  if (bytes == 0) return QN_OK;
+  if (!buf || !sink) return QN_ERR_NULL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return QN_ERR_ALIGN;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_read_probe(buf, bytes, sink, as_stream(stream)));
+}
+
 int qlora_linear_fwd_noalloc(const qn_weight* w, const qn_bf16* x, int64_t M, const qn_bf16* A,
                              const qn_bf16* B, int32_t r, float alpha, qn_bf16* y,
                              qn_bf16* u_out, void* stream) {

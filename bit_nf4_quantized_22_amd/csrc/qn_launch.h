@@ -63,6 +63,10 @@ constexpr int kWideMaxSlices = 16;
 // Number of L-slices launch_skinny uses for M > 16 tokens.
 int skinny_wide_splits(int64_t M, int64_t L);
 
+// Streaming read of `bytes` (a multiple of 16) with 16-byte loads (a
+// measurement aid).
+hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t st);
+
 // Size of the library's own per-device scratch array (qn_scratch.hip), the
 // workspace of the allocation-free forward.
 constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;

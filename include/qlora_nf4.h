@@ -275,6 +275,17 @@ QN_API int qlora_linear_fwd(const qn_weight* w, const qn_bf16* x, int64_t M,
                      void* stream);
 
 /*
+ * qn_hbm_read_probe -- a measurement aid, not an operation of the method:
+ * reads `bytes` bytes of device memory at buf with 16-byte loads (2048
+ * workgroups, a grid-stride loop) and discards them, so its duration gives
+ * the streaming-read rate that the HBM-bound kernels are measured against.
+ *   buf   device, 16-byte aligned;  bytes a multiple of 16 (QN_ERR_SHAPE).
+ *   sink  device uint32[1]; written only when the XOR of all the data equals
+ *         a fixed sentinel (it keeps the loads from being optimised away).
+ */
+QN_API int qn_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, void* stream);
+
+/*
  * qlora_linear_fwd_noalloc -- qlora_linear_fwd without a workspace
  * argument, for callers that cannot allocate device memory (code under
  * graph capture, tight serving loops, hosts that forbid allocation).

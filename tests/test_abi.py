@@ -317,3 +317,13 @@ def test_fused_quantise_argument_errors(lib):
     assert call(args(w=ODD)) == qn.QN_ERR_ALIGN
     assert call(args(a=ODD)) == qn.QN_ERR_ALIGN
     assert call(args(n=0, w=None, p=None, q=None, g=None)) == qn.QN_OK
+
+
+def test_read_probe_argument_errors(lib):
+    f = lib.qn_hbm_read_probe
+    assert f(FAKE, 100, FAKE, None) == qn.QN_ERR_SHAPE
+    assert f(FAKE, -16, FAKE, None) == qn.QN_ERR_SHAPE
+    assert f(None, 64, FAKE, None) == qn.QN_ERR_NULL
+    assert f(FAKE, 64, None, None) == qn.QN_ERR_NULL
+    assert f(ODD, 64, FAKE, None) == qn.QN_ERR_ALIGN
+    assert f(None, 0, None, None) == qn.QN_OK
