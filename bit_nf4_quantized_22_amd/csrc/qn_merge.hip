@@ -50,50 +50,10 @@ __global__ __launch_bounds__(256) void merge_kernel(
   const int64_t n0 = static_cast<int64_t>(blockIdx.y) * kMRows;
   const int64_t k0 = static_cast<int64_t>(blockIdx.x) * kMCols;
   const int64_t n = n0 + 16 * wave + nl;  // N % 64 == 0: always a valid row
-  const float mu = kDQ ? l2_offset(P) : 0.0f;
-  {
-    const CodeRegs R = code_regs(P);
-    for (int i = tid; i < 16 * 64; i += 256) scode[i] = code_value(R, i >> 6);
-  }
-  // B row n, columns 32 d + 8 g .. + 7 (zero past r), as MFMA operands
-  uint4 bfrag[kD > 0 ? kD : 1];
-  if constexpr (kR > 0) {
-    // A tile transposed: sat[kk][j] = A[j][k0 + kk], zero for j >= r or
-    // columns past K.  Thread tid handles column kk = tid of every row j;
-    // all loads are unconditional from clamped addresses (a branch around a
-    // load would wait for it at the join), the zeros selected afterwards.
-    {
-      const int kk = tid;
-      const int64_t kc = k0 + kk < K ? k0 + kk : K - 1;
-      const bool kin = k0 + kk < K;
-      uint32_t av[kR];
-#pragma unroll
-      for (int j = 0; j < kR; ++j) av[j] = A[static_cast<int64_t>(j < r ? j : r - 1) * K + kc];
-#pragma unroll
-      for (int j = 0; j < kR; ++j)
-        sat[kk * kRS + j] = (kin && j < r) ? static_cast<uint16_t>(av[j]) : uint16_t{0};
-    }
-#pragma unroll
-    for (int d = 0; d < kD; ++d) {
-      uint32_t bv[8];
-#pragma unroll
-      for (int h = 0; h < 8; ++h) {
-        const int j = 32 * d + 8 * g + h;
-        bv[h] = B[n * r + (j < r ? j : r - 1)];
-      }
-      uint32_t w4[4];
-#pragma unroll
-      for (int h = 0; h < 4; ++h) {
-        const int j = 32 * d + 8 * g + 2 * h;
-        w4[h] = (j < r ? bv[2 * h] : 0u) | ((j + 1 < r ? bv[2 * h + 1] : 0u) << 16);
-      }
-      bfrag[d] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
-    }
-  }
-  __syncthreads();
-
-  // Loads of all four blocks first (blocks past K re-read the last block
-  // and store nothing), then the arithmetic.
+  // The weight loads of all four blocks go first, before the LoRA operands
+  // are staged (blocks past K re-read the last block and store nothing):
+  // their latency then overlaps the staging and its barrier instead of
+  // following it.
   constexpr int kBlk = kMCols / 64;
   uint2 cw[kBlk];
   uint32_t q8[kBlk];
@@ -112,6 +72,64 @@ __global__ __launch_bounds__(256) void merge_kernel(
       c2[blk] = absmax[bi];
     }
   }
+  const float mu = kDQ ? l2_offset(P) : 0.0f;
+  {
+    const CodeRegs R = code_regs(P);
+    for (int i = tid; i < 16 * 64; i += 256) scode[i] = code_value(R, i >> 6);
+  }
+  // B row n, columns 32 d + 8 g .. + 7 (zero past r), as MFMA operands
+  uint4 bfrag[kD > 0 ? kD : 1];
+  if constexpr (kR > 0) {
+    // A tile transposed: sat[kk][j] = A[j][k0 + kk], zero for j >= r or
+    // columns past K.  Thread tid handles column kk = tid of every row j;
+    // all loads are unconditional from clamped addresses (a branch around a
+    // load would wait for it at the join), the zeros selected afterwards.
+    // Rows j >= r are zero and need no load (r is uniform); each thread's
+    // column goes to LDS as 16-byte runs of 8 ranks.
+    {
+      const int kk = tid;
+      const int64_t kc = k0 + kk < K ? k0 + kk : K - 1;
+      const bool kin = k0 + kk < K;
+      uint32_t av[kR];
+#pragma unroll
+      for (int j = 0; j < kR; ++j) av[j] = j < r ? A[static_cast<int64_t>(j) * K + kc] : 0u;
+#pragma unroll
+      for (int q = 0; q < kR / 8; ++q) {
+        uint32_t w4[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          w4[h] = kin ? ((av[8 * q + 2 * h] & 0xFFFFu) | (av[8 * q + 2 * h + 1] << 16)) : 0u;
+        *reinterpret_cast<uint4*>(sat + kk * kRS + 8 * q) = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    }
+    // B's row n as one 16-byte load per 8 ranks when r is a multiple of 8
+    // (rows of 16-byte multiples; B itself 16-byte aligned), else element
+    // by element
+    const bool bvec = (r & 7) == 0 && (reinterpret_cast<uintptr_t>(B) & 15) == 0;
+#pragma unroll
+    for (int d = 0; d < kD; ++d) {
+      const int j0 = 32 * d + 8 * g;
+      if (bvec) {
+        bfrag[d] = j0 < r ? *reinterpret_cast<const uint4*>(B + n * r + j0) : make_uint4(0, 0, 0, 0);
+      } else {
+        uint32_t bv[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const int j = j0 + h;
+          bv[h] = B[n * r + (j < r ? j : r - 1)];
+        }
+        uint32_t w4[4];
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const int j = j0 + 2 * h;
+          w4[h] = (j < r ? bv[2 * h] : 0u) | ((j + 1 < r ? bv[2 * h + 1] : 0u) << 16);
+        }
+        bfrag[d] = make_uint4(w4[0], w4[1], w4[2], w4[3]);
+      }
+    }
+  }
+  __syncthreads();
+
   const uint32_t lane4 = static_cast<uint32_t>(lane) << 2;
   const char* tab = reinterpret_cast<const char*>(scode);
 #pragma unroll
