@@ -523,7 +523,7 @@ def main():
         L["t"] = torch.empty((M_TRAIN, RANK), dtype=torch.bfloat16, device=dev)
         L["dA"] = torch.empty((RANK, K), dtype=torch.float32, device=dev)
         L["dB"] = torch.empty((N, RANK), dtype=torch.float32, device=dev)
-        ws_b = max(qn.qn_workspace_bytes(op, M_TRAIN, N, K, RANK) for op in (0, 1, 2))
+        ws_b = max(qn.qn_workspace_bytes(op, M_TRAIN, N, K, RANK) for op in (0, 1, 2, 3))
         L["ws"] = qn.workspace(ws_b, dev)
         # decode: distinct quantised copies (Infinity Cache defeat), own workspace
         ncopy = int(np.ceil(ROTATE_BYTES / (N * K * BYTES_PER_WEIGHT)))

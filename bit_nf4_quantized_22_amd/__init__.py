@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "libqlora_nf4.so")
 QN_OK, QN_ERR_NULL, QN_ERR_SHAPE, QN_ERR_ALIGN = 0, -1, -2, -3
 QN_ERR_UNSUPPORTED, QN_ERR_WORKSPACE, QN_ERR_HIP = -4, -5, -6
 QN_F32, QN_BF16 = 0, 1
-QN_OP_FWD, QN_OP_BWD_DX, QN_OP_LORA_GRADS = 0, 1, 2
+QN_OP_FWD, QN_OP_BWD_DX, QN_OP_LORA_GRADS, QN_OP_BWD_DX_DROPOUT = 0, 1, 2, 3
 BLOCKSIZE, GROUP = 64, 256
 
 EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scales",
@@ -427,7 +427,8 @@ def _bwd(qw, dy, A, B, r, alpha, p, seed, dx, t_out, ws, stream):
         dx = torch.empty((M, qw.K), dtype=torch.bfloat16, device=dy.device)
     _dev(dx, torch.bfloat16, M * qw.K, "dx")
     _dev(t_out, torch.bfloat16, M * r, "t_out")
-    ws, wsb = _workspace(QN_OP_BWD_DX, M, qw.N, qw.K, r, ws, dy.device)
+    ws, wsb = _workspace(QN_OP_BWD_DX if p is None else QN_OP_BWD_DX_DROPOUT, M, qw.N, qw.K, r,
+                         ws, dy.device)
     cw = qw.c_struct()
     a, b = (_ptr(A), _ptr(B)) if r else (None, None)
     if p is None:

@@ -103,6 +103,13 @@ size_t bwd_ws(int64_t M, int64_t N, int32_t r) {
          bt_bytes(N, r);
 }
 
+// Backward with dropout: the backward's workspace, then the fp32 product
+// dy W [M, K] that the masked LoRA pass adds to before rounding once.
+size_t bwd_drop_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
+  if (r == 0 || M == 0) return 0;
+  return bwd_ws(M, N, r) + round_up(static_cast<size_t>(M) * static_cast<size_t>(K) * 4, 256);
+}
+
 // Gradient workspace: bf16 u and t (recomputed when not given), B^T, the
 // partial sums of those projections, then the split-M partial sums.
 size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
@@ -214,7 +221,7 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
   if (!aligned(dy, 16) || !aligned(dx, 2) || (r > 0 && (!aligned(A, 2) || !aligned(B, 2))) ||
       (t_out && !aligned(t_out, 2)))
     return QN_ERR_ALIGN;
-  const size_t need = bwd_ws(M, w->N, r);
+  const size_t need = drop_p ? bwd_drop_ws(M, w->N, w->K, r) : bwd_ws(M, w->N, r);
   if (need > 0 && (!ws || ws_bytes < need)) return QN_ERR_WORKSPACE;
   if (need > 0 && !aligned(ws, 16)) return QN_ERR_ALIGN;
   if (!qn::tables()) return QN_ERR_UNSUPPORTED;
@@ -238,8 +245,10 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
     if (qn::launch_lora_reduce(t32, ks, M * r, scale, ts, t_out, s) != hipSuccess) return QN_ERR_HIP;
   }
   if (!drop_p || r == 0) return hip_status(qn::launch_gemm_bwd(v, dy, M, ts, A, r, dx, s));
-  if (qn::launch_gemm_bwd(v, dy, M, nullptr, nullptr, 0, dx, s) != hipSuccess) return QN_ERR_HIP;
-  return hip_status(qn::launch_dx_lora_dropout(dx, ts, A, M, w->K, r, *drop_p, seed, s));
+  float* base32 = reinterpret_cast<float*>(static_cast<char*>(ws) + bwd_ws(M, w->N, r));
+  if (qn::launch_gemm_bwd(v, dy, M, nullptr, nullptr, 0, dx, s, base32) != hipSuccess)
+    return QN_ERR_HIP;
+  return hip_status(qn::launch_dx_lora_dropout(base32, dx, ts, A, M, w->K, r, *drop_p, seed, s));
 }
 
 }  // namespace
@@ -336,6 +345,7 @@ size_t qn_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r
     case QN_OP_FWD: return fwd_ws(M, r);
     case QN_OP_BWD_DX: return bwd_ws(M, N, r);
     case QN_OP_LORA_GRADS: return grads_ws(M, N, K, r);
+    case QN_OP_BWD_DX_DROPOUT: return bwd_drop_ws(M, N, K, r);
     default: return 0;
   }
 }

@@ -18,9 +18,10 @@
 // Two streaming kernels:
 //   dropout_kernel   x -> bf16(x * fl32(1 / (1 - p))) or +0, 8 rows x 8
 //                    columns per thread (16-byte loads and stores)
-//   dx_lora_kernel   dx += D * (s t A) on a dx that holds dy W, one column
-//                    per thread with A's column in registers and the rows of
-//                    bf16(s t) in LDS; 32 rows per workgroup
+//   dx_lora_kernel   dx = bf16(dy W + D * (s t A)) from the fp32 product
+//                    dy W (one rounding), one column per thread with A's
+//                    column in registers and the rows of bf16(s t) in LDS;
+//                    32 rows per workgroup
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -105,7 +106,8 @@ constexpr int kDxRows = 32;  // rows of dx per workgroup (four Philox blocks per
 // dx[m, k] <- bf16(dx[m, k] + keep(m, k) * fl32(inv_keep * sum_j ts[m, j] A[j, k]))
 // with ts = bf16(s t); the sum is an fp32 fma chain in j order.
 template <int kR>
-__global__ __launch_bounds__(256) void dx_lora_kernel(uint16_t* __restrict__ dx,
+__global__ __launch_bounds__(256) void dx_lora_kernel(const float* __restrict__ base,
+                                                      uint16_t* __restrict__ dx,
                                                       const uint16_t* __restrict__ ts,
                                                       const uint16_t* __restrict__ A, int64_t M,
                                                       int64_t K, int r, uint64_t seed,
@@ -142,11 +144,11 @@ __global__ __launch_bounds__(256) void dx_lora_kernel(uint16_t* __restrict__ dx,
   const int64_t mlast = (m0 + kDxRows < M ? m0 + kDxRows : M) - 1;
   for (int rb = 0; rb < kDxRows; rb += 8) {
     const int64_t g = (m0 + rb) >> 3;
-    uint16_t d[8];
+    float d[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t m = m0 + rb + i < mlast ? m0 + rb + i : mlast;
-      d[i] = dx[m * K + kc];
+      d[i] = base[m * K + kc];
     }
     const uint32_t bits = keep_bits(static_cast<uint64_t>(kc), static_cast<uint64_t>(g), seed, thr);
 #pragma unroll
@@ -164,19 +166,20 @@ __global__ __launch_bounds__(256) void dx_lora_kernel(uint16_t* __restrict__ dx,
         acc = __fmaf_rn(trow[j], aj, acc);
       }
       const float add = ((bits >> i) & 1u) ? __fmul_rn(inv_keep, acc) : 0.f;
-      const float val = __fadd_rn(bf16_to_f32(d[i]), add);
+      const float val = __fadd_rn(d[i], add);
       if (kvalid && m <= mlast) dx[m * K + k] = static_cast<uint16_t>(pack_bf16x2(val, 0.f) & 0xFFFF);
     }
   }
 }
 
 template <int kR>
-void dx_lora_launch(uint16_t* dx, const uint16_t* ts, const uint16_t* A, int64_t M, int64_t K,
-                    int r, uint64_t seed, uint32_t thr, float inv_keep, hipStream_t st) {
+void dx_lora_launch(const float* base, uint16_t* dx, const uint16_t* ts, const uint16_t* A,
+                    int64_t M, int64_t K, int r, uint64_t seed, uint32_t thr, float inv_keep,
+                    hipStream_t st) {
   const dim3 grid(static_cast<uint32_t>((K + 255) / 256),
                   static_cast<uint32_t>((M + kDxRows - 1) / kDxRows));
-  hipLaunchKernelGGL((dx_lora_kernel<kR>), grid, dim3(256), 0, st, dx, ts, A, M, K, r, seed, thr,
-                     inv_keep);
+  hipLaunchKernelGGL((dx_lora_kernel<kR>), grid, dim3(256), 0, st, base, dx, ts, A, M, K, r, seed,
+                     thr, inv_keep);
 }
 
 }  // namespace
@@ -201,14 +204,15 @@ hipError_t launch_dropout(const uint16_t* x, int64_t M, int64_t K, float p, uint
   return hipGetLastError();
 }
 
-hipError_t launch_dx_lora_dropout(uint16_t* dx, const uint16_t* ts, const uint16_t* A, int64_t M,
-                                  int64_t K, int r, float p, uint64_t seed, hipStream_t st) {
+hipError_t launch_dx_lora_dropout(const float* base, uint16_t* dx, const uint16_t* ts,
+                                  const uint16_t* A, int64_t M, int64_t K, int r, float p,
+                                  uint64_t seed, hipStream_t st) {
   if (M == 0 || K == 0 || r == 0) return hipSuccess;
   const DropoutParams d = dropout_params(p);
-  if (r <= 16) dx_lora_launch<16>(dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
-  else if (r <= 32) dx_lora_launch<32>(dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
-  else if (r <= 64) dx_lora_launch<64>(dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
-  else dx_lora_launch<128>(dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
+  if (r <= 16) dx_lora_launch<16>(base, dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
+  else if (r <= 32) dx_lora_launch<32>(base, dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
+  else if (r <= 64) dx_lora_launch<64>(base, dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
+  else dx_lora_launch<128>(base, dx, ts, A, M, K, r, seed, d.threshold, d.inv_keep, st);
   return hipGetLastError();
 }
 

@@ -66,6 +66,7 @@ struct GemmArgs {
   const uint16_t* lw;    // B [N, r] (fwd) or A [r, K] (bwd)
   int r;
   uint16_t* out;         // y [M, N] or dx [M, K]
+  float* out32;          // if not null: the fp32 result goes here instead of out
 };
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -574,6 +575,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_kernel(GemmArgs g, CodeParam
     const int lane = t & 63, wave = t >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int li = lane & 31, lg = lane >> 5;
+    if (g.out32) {
+      // fp32 result (a later pass adds to it and rounds once): each lane's
+      // four adjacent columns as one 16-byte store (ncols % 64 == 0)
+#pragma unroll
+      for (int i = 0; i < kTM; ++i)
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t m = m0 + wm * (kBM / 2) + i * 32 + li;
+            const int64_t n = c0 + wn * (kBN / 2) + j * 32 + 8 * q + 4 * lg;
+            if (m < g.M && n < ncols)
+              *reinterpret_cast<float4*>(g.out32 + m * ncols + n) =
+                  make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                              acc[i][j][4 * q + 3]);
+          }
+      return;
+    }
     const bool vec16 = (ncols & 7) == 0 && (reinterpret_cast<uintptr_t>(g.out) & 15) == 0;
     if (vec16) {
       // stage the wave's 128 x 64 tile in LDS (the activation buffers and
@@ -635,7 +654,7 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
                            const uint16_t* us, const uint16_t* B, int r, uint16_t* y,
                            hipStream_t st) {
   if (M == 0 || w.N == 0) return hipSuccess;
-  GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, x, us, B, r, y};
+  GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, x, us, B, r, y, nullptr};
   const dim3 grid(static_cast<uint32_t>(((w.N + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
     hipLaunchKernelGGL((gemm_kernel<false, true>), grid, dim3(kThreads), 0, st, g, code_params(w));
@@ -646,9 +665,9 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
 
 hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
                            const uint16_t* ts, const uint16_t* A, int r, uint16_t* dx,
-                           hipStream_t st) {
+                           hipStream_t st, float* dx32) {
   if (M == 0 || w.K == 0) return hipSuccess;
-  GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, dy, ts, A, r, dx};
+  GemmArgs g{w.packed, w.qscale, w.gscale, w.absmax, w.N, w.K, M, dy, ts, A, r, dx, dx32};
   const dim3 grid(static_cast<uint32_t>(((w.K + kBN - 1) / kBN) * ((M + kBM - 1) / kBM)));
   if (w.qscale)
     hipLaunchKernelGGL((gemm_kernel<true, true>), grid, dim3(kThreads), 0, st, g, code_params(w));

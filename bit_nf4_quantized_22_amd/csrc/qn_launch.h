@@ -92,10 +92,11 @@ hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,
                            const uint16_t* us, const uint16_t* B, int r, uint16_t* y,
                            hipStream_t st);
 
-// Fused dequant GEMM, backward to the input: dx[M,K] = dy W + ts A.
+// Fused dequant GEMM, backward to the input: dx[M,K] = dy W + ts A; with
+// dx32 the fp32 result goes to dx32 [M, K] instead (dx untouched).
 hipError_t launch_gemm_bwd(const WeightView& w, const uint16_t* dy, int64_t M,
                            const uint16_t* ts, const uint16_t* A, int r, uint16_t* dx,
-                           hipStream_t st);
+                           hipStream_t st, float* dx32 = nullptr);
 
 // Sum of nslice (<= kWideMaxSlices) fp32 partial sums part[nslice][n] in
 // slice order: writes bf16(scale * sum) to out_scaled (and bf16(sum) to out
@@ -123,9 +124,11 @@ DropoutParams dropout_params(float p);
 // out[M, K] = x * keep / (1 - p) in bf16 (dropped elements +0); K % 8 == 0.
 hipError_t launch_dropout(const uint16_t* x, int64_t M, int64_t K, float p, uint64_t seed,
                           uint16_t* out, hipStream_t st);
-// dx[M, K] += keep * (ts A) / (1 - p), ts = bf16(s t) [M, r], A [r, K].
-hipError_t launch_dx_lora_dropout(uint16_t* dx, const uint16_t* ts, const uint16_t* A, int64_t M,
-                                  int64_t K, int r, float p, uint64_t seed, hipStream_t st);
+// dx[M, K] = bf16(base[M, K] + keep * (ts A) / (1 - p)), base the fp32
+// product dy W, ts = bf16(s t) [M, r], A [r, K]: one rounding.
+hipError_t launch_dx_lora_dropout(const float* base, uint16_t* dx, const uint16_t* ts,
+                                  const uint16_t* A, int64_t M, int64_t K, int r, float p,
+                                  uint64_t seed, hipStream_t st);
 
 // LoRA gradients (see lora_grads in the C ABI).  u and t are bf16 [M, r];
 // ws holds grads_workspace_bytes() of split-M partials.

@@ -65,6 +65,7 @@ extern "C" {
 #define QN_OP_FWD         0
 #define QN_OP_BWD_DX      1
 #define QN_OP_LORA_GRADS  2
+#define QN_OP_BWD_DX_DROPOUT 3
 
 typedef uint16_t qn_bf16; /* bf16 bit pattern */
 
@@ -248,7 +249,8 @@ QN_API int nf4_dequant(const qn_weight* w, int32_t out_dtype, void* out, void* s
 
 /*
  * qn_workspace_bytes -- HOST function.  Bytes of device workspace that op
- * (QN_OP_FWD, QN_OP_BWD_DX or QN_OP_LORA_GRADS) needs for these sizes.
+ * (QN_OP_FWD, QN_OP_BWD_DX, QN_OP_LORA_GRADS or QN_OP_BWD_DX_DROPOUT)
+ * needs for these sizes.
  * Returns 0 for invalid arguments.  The forward and backward keep the LoRA
  * projection (x A^T or dy B) there as fp32 partial sums over slices of the
  * contraction (at most 512 slices for M <= 16, 16 above), which are added
@@ -392,10 +394,12 @@ QN_API int qlora_linear_fwd_dropout(const qn_weight* w, const qn_bf16* x,
  * qlora_linear_bwd_dx_dropout -- dx = dy * dequant(W) + D * ((alpha/r) *
  * (dy * B) * A), D = keep / (1 - p) with the mask of lora_dropout for the
  * same (p, seed) regenerated in place: the chain rule through the dropped
- * adapter input ([rkmt] §3.3; [kwkr] §2.3).  The LoRA term is added to the
- * bf16 base product in a second pass, so dx is rounded to bf16 twice.
- * Arguments, workspace (QN_OP_BWD_DX) and errors as qlora_linear_bwd_dx;
- * p outside [0, 1) is QN_ERR_SHAPE.
+ * adapter input ([rkmt] §3.3; [kwkr] §2.3).  The base product dy * W is
+ * kept in fp32 in the workspace and the masked LoRA term is added to it
+ * before the one rounding to bf16, as on the plain path.
+ * Workspace: ws_bytes >= qn_workspace_bytes(QN_OP_BWD_DX_DROPOUT, ..), the
+ * backward's workspace plus M * K fp32.  Arguments and errors as
+ * qlora_linear_bwd_dx; p outside [0, 1) is QN_ERR_SHAPE.
  */
 QN_API int qlora_linear_bwd_dx_dropout(const qn_weight* w, const qn_bf16* dy, int64_t M,
                                        const qn_bf16* A, const qn_bf16* B, int32_t r,

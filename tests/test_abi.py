@@ -222,6 +222,15 @@ def test_dropout_argument_errors(lib):
                None) == qn.QN_ERR_WORKSPACE
     assert bwd(ctypes.byref(w), None, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, FAKE, None, FAKE, ws_b,
                None) == qn.QN_ERR_NULL
+    # the dropout backward keeps dy W in fp32: its workspace is the plain
+    # backward's plus M K fp32, and the plain size is too small for it
+    ws_d = qn.qn_workspace_bytes(qn.QN_OP_BWD_DX_DROPOUT, 32, 128, 128, 8)
+    assert ws_d >= ws_b + 32 * 128 * 4
+    assert qn.qn_workspace_bytes(qn.QN_OP_BWD_DX_DROPOUT, 32, 128, 128, 0) == 0
+    assert bwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, FAKE, None, FAKE, ws_b,
+               None) == qn.QN_ERR_WORKSPACE
+    assert bwd(ctypes.byref(w), FAKE, 32, FAKE, FAKE, 8, 16.0, 0.1, 1, ODD, None, FAKE, ws_d,
+               None) == qn.QN_ERR_ALIGN
 
 
 def test_fp4_codebook_bits_match_the_oracle(lib):
