@@ -1,6 +1,8 @@
 """Shared helpers of the GPU parity tests: numpy <-> device tensors and the
 oracle-side reference of one quantised layer."""
 
+import sys
+
 import numpy as np
 import torch
 
@@ -76,7 +78,9 @@ def max_elem_over_row_norm(got, ref):
 def check(name, got, ref, tol=TOL):
     e = rel_frob(got, ref)
     er = max_elem_over_row_norm(got, ref)
-    print(f"{name}: rel_frob={e:.3e} max_elem/row_norm={er:.3e}")
+    # written past pytest's capture, so the run's log keeps every measured error
+    sys.__stderr__.write(f"[check] {name}: rel_frob={e:.3e} max_elem/row_norm={er:.3e}\n")
+    sys.__stderr__.flush()
     assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol}"
     assert er <= tol, f"{name}: an element is off by {er:.3e} of its row's norm"
 
