@@ -31,6 +31,13 @@ constexpr int kStep = 64;     // tokens per step (two 32-deep MFMA steps)
 constexpr int kQ = kStep / 16;  // 16-token row groups per step
 constexpr int kPitch = kStep + 8;  // LDS row pitch of the transposed tiles, in bf16
 
+// The transposed X tile holds column c's 64 tokens as 8 chunks of 16 bytes;
+// chunk h of row c sits in slot h ^ ((c >> 3) & 7).  A loader lane writes
+// one 32-bit token pair into each of 8 rows that are 8 apart in one
+// instruction: without the swizzle those rows share their banks (row pitch
+// 36 words) and the stores serialise eight ways.
+__device__ __forceinline__ int xslot(int row, int chunk) { return chunk ^ ((row >> 3) & 7); }
+
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
@@ -128,7 +135,9 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = e & 1 ? a0[e >> 1] >> 16 : a0[e >> 1] & 0xFFFFu;
         const uint32_t hi = e & 1 ? a1[e >> 1] & 0xFFFF0000u : a1[e >> 1] << 16;
-        *reinterpret_cast<uint32_t*>(&sX[(8 * lcg + e) * kPitch + 16 * q + 2 * lrp]) = lo | hi;
+        const int row = 8 * lcg + e, tok = 16 * q + 2 * lrp;  // tok: first of the pair
+        *reinterpret_cast<uint32_t*>(&sX[row * kPitch + 8 * xslot(row, tok >> 3) + (tok & 7)]) =
+            lo | hi;
       }
     }
 #pragma unroll
@@ -149,8 +158,9 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const
         pa[a] = *reinterpret_cast<const uint4*>(&sP[(16 * a + l16) * kPitch + 32 * kk + 8 * g]);
 #pragma unroll
       for (int b = 0; b < 4; ++b) {
+        const int xrow = wave * 64 + 16 * b + l16;
         const uint4 xb = *reinterpret_cast<const uint4*>(
-            &sX[(wave * 64 + 16 * b + l16) * kPitch + 32 * kk + 8 * g]);
+            &sX[xrow * kPitch + 8 * xslot(xrow, 4 * kk + g)]);
 #pragma unroll
         for (int a = 0; a < RT / 16; ++a) acc[a][b] = mfma16(pa[a], xb, acc[a][b]);
       }
