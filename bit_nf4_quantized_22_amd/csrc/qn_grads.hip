@@ -17,7 +17,8 @@
 // token chunk, write fp32 partial sums [chunk][r][C], and a second pass
 // sums the chunks in a fixed order and applies s (bit-reproducible).  Both
 // products share each of the two launches.  The wide matrices are read
-// once; the partials are a small fraction of them.
+// once; the chunks are long enough that the partials stay a quarter of
+// them or less.
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -235,38 +236,45 @@ __global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restri
   else dA[j * C + col] = v;
 }
 
-// Token chunks for C columns: about 256 workgroups, chunks a multiple of 64.
-int64_t grads_chunk(int64_t M, int64_t C) {
+// Token chunks for C columns: about 256 workgroups, chunks a multiple of
+// 64, and at least 8 max(r, 16) tokens each, so that the fp32 partial sums
+// (chunks x r x C x 4 bytes, written and read back) stay within a quarter
+// of the bf16 input (M x C x 2 bytes).  At M = 2048, r = 64 the 16 chunks
+// of a 4096-column product had made the partials as large as the input
+// (44.8 against 40.4 us per call at 4096 x 4096).
+int64_t grads_chunk(int64_t M, int64_t C, int r) {
   const int64_t nct = (C + kCols - 1) / kCols;
   int64_t nch = 256 / nct;
+  const int64_t cap = M / (8 * (r > 16 ? r : 16));
+  if (nch > cap) nch = cap;
   if (nch < 1) nch = 1;
   int64_t chunk = (M + nch - 1) / nch;
   chunk = (chunk + kStep - 1) / kStep * kStep;
   return chunk < kStep ? kStep : chunk;
 }
 
-int64_t grads_nchunk(int64_t M, int64_t C) {
+int64_t grads_nchunk(int64_t M, int64_t C, int r) {
   if (M <= 0) return 0;
-  const int64_t chunk = grads_chunk(M, C);
+  const int64_t chunk = grads_chunk(M, C, r);
   return (M + chunk - 1) / chunk;
 }
 
-GradJob grad_job(const uint16_t* X, const uint16_t* P, int64_t M, int64_t C, float* part) {
+GradJob grad_job(const uint16_t* X, const uint16_t* P, int64_t M, int64_t C, float* part, int r) {
   GradJob j;
   j.X = X;
   j.P = P;
   j.part = part;
   j.C = C;
-  j.chunk = grads_chunk(M, C);
+  j.chunk = grads_chunk(M, C, r);
   j.ncol = static_cast<int>((C + kCols - 1) / kCols);
-  j.nwg = j.ncol * static_cast<int>(grads_nchunk(M, C));
+  j.nwg = j.ncol * static_cast<int>(grads_nchunk(M, C, r));
   return j;
 }
 
 }  // namespace
 
 size_t grads_workspace_bytes(int64_t M, int64_t N, int64_t K, int r) {
-  const int64_t elems = (grads_nchunk(M, K) * K + grads_nchunk(M, N) * N) * r;
+  const int64_t elems = (grads_nchunk(M, K, r) * K + grads_nchunk(M, N, r) * N) * r;
   return static_cast<size_t>(elems) * 4;
 }
 
@@ -274,12 +282,12 @@ hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16
                              const uint16_t* t, int64_t M, int64_t N, int64_t K, int r, float s,
                              float* dA, float* dB, void* ws, hipStream_t st) {
   if (r == 0) return hipSuccess;
-  const int nchA = static_cast<int>(grads_nchunk(M, K));
-  const int nchB = static_cast<int>(grads_nchunk(M, N));
+  const int nchA = static_cast<int>(grads_nchunk(M, K, r));
+  const int nchB = static_cast<int>(grads_nchunk(M, N, r));
   float* partA = static_cast<float*>(ws);
   float* partB = partA + static_cast<int64_t>(nchA) * r * K;
   if (M > 0) {
-    const GradJob ja = grad_job(x, t, M, K, partA), jb = grad_job(dy, u, M, N, partB);
+    const GradJob ja = grad_job(x, t, M, K, partA, r), jb = grad_job(dy, u, M, N, partB, r);
     const dim3 grid(static_cast<uint32_t>(ja.nwg + jb.nwg));
     if (r <= 16) hipLaunchKernelGGL((grads_mfma_kernel<16>), grid, dim3(256), 0, st, ja, jb, M, r);
     else if (r <= 32) hipLaunchKernelGGL((grads_mfma_kernel<32>), grid, dim3(256), 0, st, ja, jb, M, r);
