@@ -716,17 +716,22 @@ def main():
         del L["copies"]
     del graphs
     torch.cuda.empty_cache()
-    out["layer_7b"] = decoder_layer(qn, torch, dev, synth.LLAMA7B_TARGETS, with_quantise=True,
-                                    **LAYER7B)
-    out["layer_65b"] = decoder_layer(qn, torch, dev, synth.LLAMA65B_TARGETS,
-                                     with_quantise=False, **LAYER65B)
-    out["hbm_measured"] = hbm_peak(qn, torch, dev)
-    out["unfused_context"] = unfused_context(qn, torch, layers)
-    out["quantise_65b"] = quantise_65b(qn, torch, dev, synth)
-    out["adamw_7b_lora"] = adamw_7b_lora(qn, torch, dev, synth)
-    out["dropout"] = dropout_cost(qn, torch, layers)
+    sections = [
+        ("layer_7b", lambda: decoder_layer(qn, torch, dev, synth.LLAMA7B_TARGETS,
+                                           with_quantise=True, **LAYER7B)),
+        ("layer_65b", lambda: decoder_layer(qn, torch, dev, synth.LLAMA65B_TARGETS,
+                                            with_quantise=False, **LAYER65B)),
+        ("hbm_measured", lambda: hbm_peak(qn, torch, dev)),
+        ("unfused_context", lambda: unfused_context(qn, torch, layers)),
+        ("quantise_65b", lambda: quantise_65b(qn, torch, dev, synth)),
+        ("adamw_7b_lora", lambda: adamw_7b_lora(qn, torch, dev, synth)),
+        ("dropout", lambda: dropout_cost(qn, torch, layers)),
+    ]
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(workloads)
+        sections.append(("cpu_baseline", lambda: cpu_baseline(workloads)))
+    for name, run in sections:
+        out[name] = run()
+        print(f"{name} done", file=sys.stderr, flush=True)
     print(json.dumps(out))
 
 
