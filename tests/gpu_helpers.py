@@ -75,12 +75,17 @@ def max_elem_over_row_norm(got, ref):
     return float(np.max(np.abs(got - ref) / np.maximum(rn, 1e-300)))
 
 
+# every check's measured error, printed after the results by the terminal
+# summary hook in tests/conftest.py
+CHECKS = []
+
+
 def check(name, got, ref, tol=TOL):
     e = rel_frob(got, ref)
     er = max_elem_over_row_norm(got, ref)
-    # written past pytest's capture, so the run's log keeps every measured error
-    sys.__stderr__.write(f"[check] {name}: rel_frob={e:.3e} max_elem/row_norm={er:.3e}\n")
-    sys.__stderr__.flush()
+    line = f"[check] {name}: rel_frob={e:.3e} max_elem/row_norm={er:.3e}"
+    CHECKS.append(line)
+    sys.stderr.write(line + "\n")  # shown with a failing test's captured output
     assert e <= tol, f"{name}: relative Frobenius error {e:.3e} > {tol}"
     assert er <= tol, f"{name}: an element is off by {er:.3e} of its row's norm"
 

@@ -12,7 +12,10 @@ the decode GEMV's LoRA epilogue (M <= 16, including M r above the
 workgroup's thread count), the fused GEMM's LoRA contraction in both
 directions past the first 16 ranks (r = 32, 64, 100, 128) and the LoRA
 gradients at those ranks.  r = 128 with alpha = 32 is the setting [fg8] §8
-reports.
+reports.  The smallest ranks (r = 1, 3: one MFMA column tile, 15 or 13 of
+its 16 columns padding) and r = 17 (one rank past the GEMM's 16-wide early
+LoRA tile, so the late contraction with a 16-deep step that is almost all
+padding) check the rank edges.
 """
 
 import numpy as np
@@ -25,7 +28,7 @@ from tests.gpu_helpers import bf16_dev, check, f64, linear, synth, to_np
 pytestmark = pytest.mark.gpu
 
 N, K = 1088, 2112    # 8.5 column tiles of 128 (ragged), 33 quantisation blocks per row
-RANKS = [(32, 16.0), (64, 16.0), (100, 16.0), (128, 32.0)]
+RANKS = [(1, 2.0), (3, 6.0), (17, 16.0), (32, 16.0), (64, 16.0), (100, 16.0), (128, 32.0)]
 
 
 def _zero_weight():
@@ -72,7 +75,11 @@ def test_lora_only_backward_and_grads(r, alpha, M):
     check(f"t r={r} M={M}", to_np(t), linear.lora_up_input(f64(dy), f64(B)))
     rA, rB = linear.lora_grads(f64(x), f64(dy), f64(A), f64(B), alpha, r)
     check(f"dA r={r} M={M}", to_np(dA), rA)
-    check(f"dB r={r} M={M}", to_np(dB), rB)
+    # dB [N, r] is checked per rank, over its N outputs: a row of dB holds
+    # only r values, and at r = 1 the largest-element-over-row-norm bound
+    # would become one element's relative error, which a cancelling sum of
+    # M products with the bf16 u exceeds at M = 16
+    check(f"dB r={r} M={M} (per rank)", to_np(dB).T, rB.T)
 
 
 @pytest.mark.parametrize("M", [1, 64])
