@@ -94,10 +94,10 @@ def test_merge_training_weights(shape, r, alpha):
     _check_merge(got, want, f"{shape} r={r} sampled rows", mag)
 
 
-@pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33)])
+@pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33), (64, 192, 1)])
 def test_merge_ragged_columns_and_ranks(N, K, r):
     """K not a multiple of the 256-column workgroup tile, ranks that pad the
-    32-deep MFMA steps (5, 33, 100)."""
+    32-deep MFMA steps (1, 5, 33, 100)."""
     wl = synth.train_linear(N, K, M=16, seed=N + K + r, r=r, alpha=2.0 * r)
     _, _, _, got, want, mag = _merge_case(wl)
     _check_merge(got, want, f"{N}x{K} r={r}", mag)
