@@ -190,13 +190,16 @@ int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M,
   const bool decode = M <= kGemvMaxM;
   const int ks = decode ? qn::skinny_splits(M, w->K, r, qn::gemv_threads(w->N, w->K))
                         : qn::skinny_wide_splits(M, w->K);
-  if (r > 0) {
+  // one token on a one-pass GEMV (and no dropout): the GEMV launch computes
+  // u from the x it stages, and no LoRA-down launch runs
+  const bool self_u = decode && r > 0 && xa == x && qn::gemv_self_u(v, static_cast<int>(M), r);
+  if (r > 0 && !self_u) {
     if (qn::launch_skinny(xa, M, w->K, A, r, scale, u32, nullptr, nullptr, ks, s) != hipSuccess)
       return QN_ERR_HIP;
   }
   if (decode)
     return hip_status(qn::launch_gemv(v, x, static_cast<int>(M), u32, ks, B, r, scale, y,
-                                      r > 0 ? u_out : nullptr, s));
+                                      r > 0 ? u_out : nullptr, s, self_u ? A : nullptr));
   uint16_t* us = nullptr;
   if (r > 0) {
     us = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + lora_part_bytes(M, r));

@@ -30,6 +30,7 @@ namespace qn {
 namespace {
 
 constexpr int kUParts = 8;   // LoRA partial sums held per thread in the GEMV
+constexpr int kSelfUMaxBlocks = 8;  // one round of A loads after the walk: 2 kS uint4 per lane
 constexpr int kXAhead = 3;   // x prefetch distance, in blocks (register ring)
 
 __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_t c) {
@@ -221,6 +222,9 @@ struct GemvArgs {
   uint16_t* u_out;
   int M, usplit, r;
   float s;
+  // One token, one pass, r <= 16, in the kernel that computes u = x A^T
+  // itself from the x slices it staged: A [r, K] (u and usplit unused).
+  const uint16_t* A;
 };
 
 // The decode's LDS tables: kCopiesT interleaved copies of the 256-entry
@@ -302,7 +306,8 @@ __device__ __forceinline__ void gemv_lora_loads(const GemvArgs& a, int64_t n0, i
 // rows once every wave is done with the table (the first barrier below).
 template <int kWaves, int kUParts>
 __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const f32x4_t& acc,
-                                              float (*spart)[16][17], uint32_t* stab, int tid) {
+                                              float (*spart)[16][17], uint32_t* stab, int tid,
+                                              const float (*su_w)[16] = nullptr) {
   constexpr int kThreads = kWaves * 64;
   constexpr int kBPer = (16 * 128 + kThreads - 1) / kThreads;
   const int lane = tid & 63, wave = tid >> 6, nl = lane & 15, g = lane >> 4;
@@ -314,7 +319,22 @@ __device__ __forceinline__ void gemv_epilogue(const GemvArgs& a, const f32x4_t& 
   float* su = reinterpret_cast<float*>(stab);                  // [M][r] fp32
   uint16_t* sB = reinterpret_cast<uint16_t*>(stab + 16 * 128);  // [16][r] bf16
   float* sug = reinterpret_cast<float*>(stab + 16 * 128 + 16 * 128 / 2);  // [groups][M r]
-  if (r > 0) {
+  if (r > 0 && su_w) {
+    // the band's B rows; u (one token) is the waves' partial sums, added in
+    // wave order
+#pragma unroll
+    for (int q = 0; q < kBPer; ++q) {
+      const int e = tid + q * kThreads;
+      if (e < 16 * r) sB[e] = a.B[n0 * r + e];
+    }
+    if (tid < r) {
+      float v = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) v += su_w[w][tid];
+      su[tid] = v;
+    }
+    __syncthreads();
+  } else if (r > 0) {
     uint32_t bt[kBPer];
     float upart[kUParts];
     gemv_lora_loads<kThreads, kBPer, kUParts>(a, n0, tid, bt, upart);
@@ -522,8 +542,9 @@ __global__ __launch_bounds__(kWaves * 64) void gemv_ring_kernel(const GemvArgs a
 // the 8-bit block constants (aligned dwords covering the slice) and group
 // constants, then the weights block by block; the walk waits for one more
 // block per step.
-template <int kWaves, int kS, bool kDQ>
+template <int kWaves, int kS, bool kDQ, bool kSelfU = false>
 __global__ __launch_bounds__(kWaves * 64) void gemv1_kernel(const GemvArgs a, const CodeParams P) {
+  static_assert(!kSelfU || kS <= kSelfUMaxBlocks, "one round of A loads");
   constexpr int kThreads = kWaves * 64;
   constexpr int kCopiesT = kWaves == 16 ? 64 : 32;
   constexpr int kTabWords = 256 * kCopiesT;
@@ -677,15 +698,60 @@ __global__ __launch_bounds__(kWaves * 64) void gemv1_kernel(const GemvArgs a, co
       ccur = cnext;
     }
   }
-  __syncthreads();  // the partial sums below overwrite the x staging area
-  gemv_epilogue<kWaves, kUParts>(a, acc, spart, stab, tid);
+  // LoRA-down in the same launch (one pass, r <= 16): this wave's share of
+  // u = x A^T over its blocks, from its x slice still in LDS, with A's rows
+  // loaded in one round after the walk (the weight stream is done) and the
+  // same k-slot map as the walk's two MFMAs per block; row 0 of the
+  // product holds the wave's partial u.
+  if constexpr (kSelfU) {
+    __shared__ float su_w[kWaves][16];
+    const int64_t b_lo = nblk * wave / kWaves;
+    const int nb = static_cast<int>(nblk * (wave + 1) / kWaves - b_lo);
+    const int nbc = nb > 0 ? nb - 1 : 0;
+    const int r = a.r;
+    const uint16_t* arow = a.A + static_cast<int64_t>(nl < r ? nl : r - 1) * K + 16 * g;
+    uint4 af[kS][2];
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      const int64_t bi = b_lo + (i < nbc ? i : nbc);
+      af[i][0] = *reinterpret_cast<const uint4*>(arow + bi * 64);
+      af[i][1] = *reinterpret_cast<const uint4*>(arow + bi * 64 + 8);
+    }
+    f32x4_t au = zero;
+#pragma unroll
+    for (int i = 0; i < kS; ++i) {
+      uint4 x0 = make_uint4(0, 0, 0, 0), x1 = x0;
+      if (xon) {
+        x0 = *reinterpret_cast<const uint4*>(xb + i * 128);
+        x1 = *reinterpret_cast<const uint4*>(xb + i * 128 + 16);
+      }
+      const uint32_t m = i < nb && nl < r ? 0xFFFFFFFFu : 0u;  // an AND, not a select
+      au = mfma16(x0, make_uint4(af[i][0].x & m, af[i][0].y & m, af[i][0].z & m, af[i][0].w & m), au);
+      au = mfma16(x1, make_uint4(af[i][1].x & m, af[i][1].y & m, af[i][1].z & m, af[i][1].w & m), au);
+    }
+    if (g == 0) su_w[wave][nl] = au[0];
+    __syncthreads();  // the partial sums below overwrite the x staging area
+    gemv_epilogue<kWaves, kUParts>(a, acc, spart, stab, tid, su_w);
+  } else {
+    __syncthreads();  // the partial sums below overwrite the x staging area
+    gemv_epilogue<kWaves, kUParts>(a, acc, spart, stab, tid);
+  }
 }
 
 // One GEMV configuration: the staged kernel for one token, the register
 // ring above.
 template <int W, int S>
 void gemv_config(int M, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
-                 const CodeParams& P) {
+                 const CodeParams& P, bool self_u) {
+  if constexpr (W == 16 && (S == 4 || S == 8)) {
+    if (self_u) {
+      if (dq)
+        hipLaunchKernelGGL((gemv1_kernel<W, S, true, true>), grid, dim3(W * 64), 0, st, a, P);
+      else
+        hipLaunchKernelGGL((gemv1_kernel<W, S, false, true>), grid, dim3(W * 64), 0, st, a, P);
+      return;
+    }
+  }
   if (M == 1) {
     if (dq)
       hipLaunchKernelGGL((gemv1_kernel<W, S, true>), grid, dim3(W * 64), 0, st, a, P);
@@ -789,9 +855,43 @@ hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out,
   return hipGetLastError();
 }
 
+namespace {
+
+// Waves per band and blocks per wave of the GEMV for an N x K weight.
+// Waves per band from gemv_threads; blocks per wave the smallest of 4, 8,
+// 11, 12, 16 that covers the row (11: 172 blocks of a 11008-long row over
+// 16 waves); longer rows take several passes of 16 (of 12 at 16 waves,
+// where 16 x 16 would spill).
+void gemv_shape(int64_t N, int64_t K, int M, int& wv, int& sb) {
+  const int64_t nblk = K >> 6;
+  wv = gemv_threads(N, K) / 64;
+  const int64_t need = (nblk + wv - 1) / wv;
+  sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 11 ? 11 : need <= 12 ? 12 : 16;
+  if (wv == 16 && sb == 16) sb = 12;
+  // one token over 8 waves: two passes of 4 blocks rather than one of 8
+  // (the 8-block kernel needs 89 VGPRs, which allows two workgroups per CU
+  // instead of three; 11008 x 4096: 10.4 us against 10.9)
+  if (M == 1 && wv == 8 && sb == 8) sb = 4;
+}
+
+}  // namespace
+
+bool gemv_self_u(const WeightView& w, int M, int r) {
+  if (M != 1 || r <= 0 || r > 16 || w.N == 0) return false;
+  int wv, sb;
+  gemv_shape(w.N, w.K, M, wv, sb);
+  // one pass of the 16-wave kernel with 4 or 8 blocks per wave, and every
+  // band reads all of A [r, K] from L2: at about 10 TB/s that costs more
+  // than the LoRA-down launch it replaces (about 4.5 us) beyond some 40 MB
+  // (4096 x 4096, r = 16: 33.5 MB, 9.6 against 10.9 us per call; 4096 x
+  // 11008: 90 MB, 19.8 against 15.4 us)
+  const double a_bytes = static_cast<double>(w.N / 16) * r * static_cast<double>(w.K) * 2;
+  return wv == 16 && (sb == 4 || sb == 8) && (w.K >> 6) <= 16 * sb && a_bytes <= 40e6;
+}
+
 hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const float* u, int usplit,
                        const uint16_t* B, int r, float s, uint16_t* y, uint16_t* u_out,
-                       hipStream_t st) {
+                       hipStream_t st, const uint16_t* A_self) {
   if (M == 0 || w.N == 0) return hipSuccess;
   const CodeParams P = code_params(w);
   GemvArgs a;
@@ -811,23 +911,16 @@ hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const floa
   a.usplit = usplit < 1 ? 1 : usplit;
   a.r = r;
   a.s = s;
-  const int64_t nbands = w.N / 16, nblk = w.K >> 6;
+  a.A = A_self;
+  const bool self_u = A_self != nullptr && r > 0;
+  const int64_t nbands = w.N / 16;
   const dim3 grid(static_cast<uint32_t>(nbands));
-  // Waves per band from gemv_threads; blocks per wave the smallest of 4, 8,
-  // 11, 12, 16 that covers the row (11: 172 blocks of a 11008-long row over
-  // 16 waves); longer rows take several passes of 16 (of 12 at 16 waves,
-  // where 16 x 16 would spill).
-  const int wv = gemv_threads(w.N, w.K) / 64;
-  const int64_t need = (nblk + wv - 1) / wv;
-  int sb = need <= 4 ? 4 : need <= 8 ? 8 : need <= 11 ? 11 : need <= 12 ? 12 : 16;
-  if (wv == 16 && sb == 16) sb = 12;
-  // one token over 8 waves: two passes of 4 blocks rather than one of 8
-  // (the 8-block kernel needs 89 VGPRs, which allows two workgroups per CU
-  // instead of three; 11008 x 4096: 10.4 us against 10.9)
-  if (M == 1 && wv == 8 && sb == 8) sb = 4;
+  int wv, sb;
+  gemv_shape(w.N, w.K, M, wv, sb);
+  if (self_u && !gemv_self_u(w, M, r)) return hipErrorInvalidValue;
   const bool dq = w.qscale != nullptr;
 #define QN_GEMV(W, S) \
-  if (wv == W && sb == S) gemv_config<W, S>(M, dq, grid, st, a, P);
+  if (wv == W && sb == S) gemv_config<W, S>(M, dq, grid, st, a, P, self_u);
   QN_GEMV(4, 4) QN_GEMV(4, 8) QN_GEMV(4, 11) QN_GEMV(4, 12) QN_GEMV(4, 16)
   QN_GEMV(8, 4) QN_GEMV(8, 8) QN_GEMV(8, 11) QN_GEMV(8, 12) QN_GEMV(8, 16)
   QN_GEMV(16, 4) QN_GEMV(16, 8) QN_GEMV(16, 11) QN_GEMV(16, 12)

@@ -83,9 +83,15 @@ int skinny_splits(int64_t M, int64_t L, int r, int gemv_thr);
 
 // Decode path (M <= 16): y = x W^T + s u B^T with u given as usplit fp32
 // partial sums [usplit][M][r]; optionally writes bf16(u) to u_out.
+// With A_self (A [r, K]; only where gemv_self_u holds) the GEMV launch
+// computes u itself from x, and u / usplit are not read.
 hipError_t launch_gemv(const WeightView& w, const uint16_t* x, int M, const float* u, int usplit,
                        const uint16_t* B, int r, float s, uint16_t* y, uint16_t* u_out,
-                       hipStream_t st);
+                       hipStream_t st, const uint16_t* A_self = nullptr);
+// Whether the GEMV for this weight, M and r computes the LoRA-down in the
+// same launch (one token, r <= 16, one pass of the 16-wave kernel, and A
+// re-read by all bands in at most about 40 MB).
+bool gemv_self_u(const WeightView& w, int M, int r);
 
 // Fused dequant GEMM, forward: y[M,N] = x W^T + us B^T (us = bf16(s*u), [M, r]).
 hipError_t launch_gemm_fwd(const WeightView& w, const uint16_t* x, int64_t M,

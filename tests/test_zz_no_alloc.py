@@ -55,6 +55,7 @@ CASES = [
     (4096, 4096, 64, 16.0, 4096, 16),
     (4096, 11008, 16, 32.0, 16, 1),
     (1088, 2112, 128, 32.0, 64, 4),
+    (1088, 2112, 16, 32.0, 16, 1),  # the second call computes u inside the GEMV launch
 ]
 
 
