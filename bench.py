@@ -27,6 +27,11 @@ N(0, 0.02) (its own rotating copies, x, A, B from the same recipe), and
 each shape at M = 1 without the LoRA term (r = 0: the GEMV kernel is then
 the whole call; "gemv.kernel_only_r0").
 
+"decode_layer_7b" times one token (M = 1, r = 16) through the seven
+projections of a 7B-shaped layer, captured in one HIP graph over rotating
+layer copies beyond the Infinity Cache: microseconds per layer, and the
+32-layer product (linear layers only).
+
 After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
 v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
 N(0, 0.02) drawn and quantised on the device: quantise + DQ (fused), fwd, bwd_dx
@@ -417,6 +422,67 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     return res
 
 
+def decode_layer_7b(qn, torch, dev, synth, r=16, alpha=32.0, std=0.02, seed=9, reps=10):
+    """One token (M = 1) through the seven projections of a 7B-shaped layer
+    (q, k, v, o 4096x4096; gate, up 11008x4096; down 4096x11008): bf16 N(0,
+    std) weights quantised on the device, x N(0, 1), A, B N(0, 0.01), LoRA
+    r = 16.  The seven calls of each of enough layer copies to exceed the
+    256 MiB Infinity Cache are captured in one HIP graph; the time per layer
+    is a replay's time over the copies (median of reps)."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    bf = torch.bfloat16
+    targets = synth.LLAMA7B_TARGETS
+    layer_bytes = sum(n * k for _, n, k in targets) * BYTES_PER_WEIGHT
+    ncopy = int(np.ceil(ROTATE_BYTES / layer_bytes))
+    Ws = {(n, k): (torch.randn(n, k, generator=gen, device=dev) * std).to(bf) for _, n, k in targets}
+    copies = [[qn.quantize_weight(Ws[(n, k)]) for _, n, k in targets] for _ in range(ncopy)]
+    del Ws
+    xs = {k: torch.randn(1, k, generator=gen, device=dev).to(bf) for _, _, k in targets}
+    ys = {n: torch.empty((1, n), dtype=bf, device=dev) for _, n, _ in targets}
+    ada = [((torch.randn(r, k, generator=gen, device=dev) * 0.01).to(bf),
+            (torch.randn(n, r, generator=gen, device=dev) * 0.01).to(bf)) for _, n, k in targets]
+    ws = qn.workspace(max(qn.qn_workspace_bytes(0, 1, n, k, r) for _, n, k in targets), dev)
+
+    def calls():
+        for layer in copies:
+            for (name, n, k), qw, (A, B) in zip(targets, layer, ada):
+                qn.qlora_linear_fwd(qw, xs[k], A, B, r, alpha, y=ys[n], ws=ws)
+
+    stream = torch.cuda.current_stream()
+    gs = torch.cuda.Stream()
+    gs.wait_stream(stream)
+    with torch.cuda.stream(gs):
+        calls()  # eager warm-up on the capture stream
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=gs):
+            calls()
+    stream.wait_stream(gs)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        ts.append(s.elapsed_time(e))
+    us = float(np.median(ts)) * 1e3 / ncopy
+    nbytes = layer_bytes + sum(2 * (n + k) + 2 * r * (n + k) for _, n, k in targets)
+    res = {"targets": [f"{name} {n}x{k}" for name, n, k in targets], "M": 1, "r": r,
+           "alpha": alpha, "layer_copies": ncopy, "us_per_layer": round(us, 3),
+           "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+           "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+           "ms_per_token_32_layers": round(32 * us / 1e3, 4),
+           "note": "the seven linear layers only (no attention, norms or sampling)"}
+    del g, copies, xs, ys, ada, ws
+    torch.cuda.empty_cache()
+    return res
+
+
 def hbm_peak(qn, torch, dev, reps=10):
     """Achievable HBM rates measured with plain torch kernels on 1 GiB
     buffers (context for the fractions of the 8 TB/s peak): a device copy
@@ -721,6 +787,7 @@ def main():
                                            with_quantise=True, **LAYER7B)),
         ("layer_65b", lambda: decoder_layer(qn, torch, dev, synth.LLAMA65B_TARGETS,
                                             with_quantise=False, **LAYER65B)),
+        ("decode_layer_7b", lambda: decode_layer_7b(qn, torch, dev, synth)),
         ("hbm_measured", lambda: hbm_peak(qn, torch, dev)),
         ("unfused_context", lambda: unfused_context(qn, torch, layers)),
         ("quantise_65b", lambda: quantise_65b(qn, torch, dev, synth)),
