@@ -91,16 +91,11 @@ size_t fwd_ws(int64_t M, int32_t r) {
   return lora_part_bytes(M, r) + lora_bf16_bytes(M, r);
 }
 
-// B^T [r, N] bf16: the row-major operand of t = dy B.
-size_t bt_bytes(int64_t N, int32_t r) {
-  return round_up(static_cast<size_t>(N) * static_cast<size_t>(r) * 2, 256);
-}
-
-// Backward workspace: the partial sums of t, bf16(s t), then B^T.
+// Backward workspace: the partial sums of t, then bf16(s t).
 size_t bwd_ws(int64_t M, int64_t N, int32_t r) {
+  (void)N;
   if (r == 0 || M == 0) return 0;
-  return lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) + lora_bf16_bytes(M, r) +
-         bt_bytes(N, r);
+  return lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) + lora_bf16_bytes(M, r);
 }
 
 // Backward with dropout: the backward's workspace, then the fp32 product
@@ -110,12 +105,11 @@ size_t bwd_drop_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   return bwd_ws(M, N, r) + round_up(static_cast<size_t>(M) * static_cast<size_t>(K) * 4, 256);
 }
 
-// Gradient workspace: bf16 u and t (recomputed when not given), B^T, the
+// Gradient workspace: bf16 u and t (recomputed when not given), the
 // partial sums of those projections, then the split-M partial sums.
 size_t grads_ws(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (r == 0) return 0;
-  return 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r) +
-         lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) +
+  return 2 * lora_bf16_bytes(M, r) + lora_part_bytes(M > kGemvMaxM ? M : kGemvMaxM + 1, r) +
          round_up(qn::grads_workspace_bytes(M, N, K, r), 256);
 }
 
@@ -231,8 +225,8 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   const float scale = r > 0 ? alpha / static_cast<float>(r) : 0.0f;
-  // t = dy B (through B^T, so both operands are row-major) as fp32 partial
-  // sums over N-slices, added up by the GEMM
+  // t = dy B as fp32 partial sums over N-slices (B read where it lies,
+  // [N, r]), added up in slice order into bf16(s t), the GEMM's operand
   uint16_t* ts = nullptr;
   const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
   const int ks = qn::skinny_wide_splits(mp, w->N);
@@ -240,10 +234,8 @@ int bwd_impl(const qn_weight* w, const qn_bf16* dy, int64_t M, const qn_bf16* A,
     char* base = static_cast<char*>(ws);
     float* t32 = reinterpret_cast<float*>(base);
     ts = reinterpret_cast<uint16_t*>(base + lora_part_bytes(mp, r));
-    uint16_t* bt = reinterpret_cast<uint16_t*>(base + lora_part_bytes(mp, r) +
-                                               lora_bf16_bytes(M, r));
-    if (qn::launch_transpose(B, w->N, r, bt, s) != hipSuccess) return QN_ERR_HIP;
-    if (qn::launch_skinny(dy, M, w->N, bt, r, scale, t32, nullptr, nullptr, ks, s) != hipSuccess)
+    if (qn::launch_skinny(dy, M, w->N, B, r, scale, t32, nullptr, nullptr, ks, s, true) !=
+        hipSuccess)
       return QN_ERR_HIP;
     if (qn::launch_lora_reduce(t32, ks, M * r, scale, ts, t_out, s) != hipSuccess) return QN_ERR_HIP;
   }
@@ -466,9 +458,8 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   const int64_t mp = M > kGemvMaxM ? M : kGemvMaxM + 1;
   uint16_t* u16 = reinterpret_cast<uint16_t*>(base);
   uint16_t* t16 = reinterpret_cast<uint16_t*>(base + lora_bf16_bytes(M, r));
-  uint16_t* bt = reinterpret_cast<uint16_t*>(base + 2 * lora_bf16_bytes(M, r));
-  float* lpart = reinterpret_cast<float*>(base + 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r));
-  void* part = base + 2 * lora_bf16_bytes(M, r) + bt_bytes(N, r) + lora_part_bytes(mp, r);
+  float* lpart = reinterpret_cast<float*>(base + 2 * lora_bf16_bytes(M, r));
+  void* part = base + 2 * lora_bf16_bytes(M, r) + lora_part_bytes(mp, r);
   if (M > 0 && !u) {
     const int ks = qn::skinny_wide_splits(mp, K);
     if (qn::launch_skinny(x, M, K, A, r, 1.0f, lpart, nullptr, nullptr, ks, s) != hipSuccess ||
@@ -477,8 +468,7 @@ int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u, const qn_b
   }
   if (M > 0 && !t) {
     const int ks = qn::skinny_wide_splits(mp, N);
-    if (qn::launch_transpose(B, N, r, bt, s) != hipSuccess ||
-        qn::launch_skinny(dy, M, N, bt, r, 1.0f, lpart, nullptr, nullptr, ks, s) != hipSuccess ||
+    if (qn::launch_skinny(dy, M, N, B, r, 1.0f, lpart, nullptr, nullptr, ks, s, true) != hipSuccess ||
         qn::launch_lora_reduce(lpart, ks, M * r, 1.0f, t16, nullptr, s) != hipSuccess)
       return QN_ERR_HIP;
   }

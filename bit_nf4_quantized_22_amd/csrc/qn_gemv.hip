@@ -50,7 +50,7 @@ __device__ __forceinline__ f32x4_t mfma16(const uint4& a, const uint4& b, f32x4_
 // (r <= 16 kCols); the kRT row tiles of a workgroup share each P load.
 // ksplit == 1: writes the finished result (fp32 and/or bf16 forms).
 // ksplit > 1: writes fp32 partial sums out_f32[slice][M][r].
-template <int kCols, int kWaves, int kRT>
+template <int kCols, int kWaves, int kRT, bool kPT>
 __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     const uint16_t* __restrict__ in, int64_t M, int64_t L, const uint16_t* __restrict__ P, int r,
     float scale, int ksplit, float* __restrict__ out_f32, uint16_t* __restrict__ out_sbf16,
@@ -71,14 +71,18 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
     arow[rt] = in + (m < M ? m : M - 1) * L + 8 * g;
   }
   // Column j = 16 c + mi of P, clamped into [0, r); columns >= r read row
-  // r - 1 and are zeroed.
+  // r - 1 and are zeroed.  kPT: P is stored [L, r] (B for t = dy B, read
+  // where it lies), and a lane's 8 consecutive l of column j are 8 loads
+  // r elements apart.
   const uint16_t* prow[kCols];
   bool pvalid[kCols];
 #pragma unroll
   for (int c = 0; c < kCols; ++c) {
     const int j = c * 16 + mi;
     pvalid[c] = j < r;
-    prow[c] = P + static_cast<int64_t>(j < r ? j : r - 1) * L + 8 * g;
+    const int jc = j < r ? j : r - 1;
+    prow[c] = kPT ? P + static_cast<int64_t>(8 * g) * r + jc
+                  : P + static_cast<int64_t>(jc) * L + 8 * g;
   }
   f32x4_t acc[kRT][kCols];
 #pragma unroll
@@ -101,7 +105,18 @@ __global__ __launch_bounds__(kWaves * 64) void skinny_kernel(
 #pragma unroll
       for (int rt = 0; rt < kRT; ++rt) a[i][rt] = *reinterpret_cast<const uint4*>(arow[rt] + kk);
 #pragma unroll
-      for (int c = 0; c < kCols; ++c) b[i][c] = *reinterpret_cast<const uint4*>(prow[c] + kk);
+      for (int c = 0; c < kCols; ++c) {
+        if constexpr (kPT) {
+          const uint16_t* pc = prow[c] + kk * r;
+          uint32_t h[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) h[e] = pc[static_cast<int64_t>(e) * r];
+          b[i][c] = make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                               h[6] | (h[7] << 16));
+        } else {
+          b[i][c] = *reinterpret_cast<const uint4*>(prow[c] + kk);
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < kCh; ++i) {
@@ -169,26 +184,6 @@ __global__ __launch_bounds__(256) void lora_reduce_kernel(const float* __restric
   if (e < n) {
     out_scaled[e] = static_cast<uint16_t>(pack_bf16x2(scale * sum, 0.f) & 0xFFFF);
     if (out) out[e] = static_cast<uint16_t>(pack_bf16x2(sum, 0.f) & 0xFFFF);
-  }
-}
-
-// out[c][l] = in[l][c] for a row-major [L, C] bf16 matrix (C <= 128): turns
-// B [N, r] into the row-major [r, N] operand of the skinny kernel.  One
-// workgroup per 64 rows of `in`, staged through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const uint16_t* __restrict__ in,
-                                                        int64_t L, int C,
-                                                        uint16_t* __restrict__ out) {
-  __shared__ uint16_t t[64][129];
-  const int64_t l0 = static_cast<int64_t>(blockIdx.x) * 64;
-  const int rows = static_cast<int>(L - l0 < 64 ? L - l0 : 64);
-  for (int idx = threadIdx.x; idx < rows * C; idx += 256) {
-    const int lr = idx / C, c = idx % C;
-    t[lr][c] = in[(l0 + lr) * C + c];
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < rows * C; idx += 256) {
-    const int c = idx / rows, lr = idx % rows;
-    out[static_cast<int64_t>(c) * L + l0 + lr] = t[lr][c];
   }
 }
 
@@ -764,24 +759,24 @@ void gemv_config(int M, bool dq, dim3 grid, hipStream_t st, const GemvArgs& a,
   }
 }
 
-template <int kCols>
+template <int kCols, bool kPT>
 void skinny_launch(int rows, hipStream_t s, const uint16_t* in, int64_t M, int64_t L,
                    const uint16_t* P, int r, float scale, int ksplit, float* out_f32,
                    uint16_t* out_sbf16, uint16_t* out_bf16) {
   const dim3 grid(static_cast<uint32_t>((M + rows - 1) / rows), static_cast<uint32_t>(ksplit));
   if constexpr (kCols <= 4) {
     if (rows == 64) {
-      hipLaunchKernelGGL((skinny_kernel<kCols, 16, 4>), grid, dim3(1024), 0, s, in, M, L, P, r,
-                         scale, ksplit, out_f32, out_sbf16, out_bf16);
+      hipLaunchKernelGGL((skinny_kernel<kCols, 16, 4, kPT>), grid, dim3(1024), 0, s, in, M, L, P,
+                         r, scale, ksplit, out_f32, out_sbf16, out_bf16);
       return;
     }
   }
   if (M > 16)
-    hipLaunchKernelGGL((skinny_kernel<kCols, 16, 1>), grid, dim3(1024), 0, s, in, M, L, P, r, scale,
-                       ksplit, out_f32, out_sbf16, out_bf16);
+    hipLaunchKernelGGL((skinny_kernel<kCols, 16, 1, kPT>), grid, dim3(1024), 0, s, in, M, L, P, r,
+                       scale, ksplit, out_f32, out_sbf16, out_bf16);
   else
-    hipLaunchKernelGGL((skinny_kernel<kCols, 1, 1>), grid, dim3(64), 0, s, in, M, L, P, r, scale,
-                       ksplit, out_f32, out_sbf16, out_bf16);
+    hipLaunchKernelGGL((skinny_kernel<kCols, 1, 1, kPT>), grid, dim3(64), 0, s, in, M, L, P, r,
+                       scale, ksplit, out_f32, out_sbf16, out_bf16);
 }
 
 int skinny_cols(int r) { return r <= 16 ? 1 : r <= 32 ? 2 : r <= 64 ? 4 : 8; }
@@ -824,19 +819,27 @@ int skinny_wide_splits(int64_t M, int64_t L) {
 
 hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P, int r,
                          float scale, float* out_f32, uint16_t* out_scaled_bf16,
-                         uint16_t* out_bf16, int ksplit, hipStream_t s) {
+                         uint16_t* out_bf16, int ksplit, hipStream_t s, bool p_rows_l) {
   if (M == 0 || r == 0) return hipSuccess;
   // Decode (M <= 16): one 16-row tile, one wave per 32-wide L-slice.  Token batches:
   // 64-row workgroups of 16 waves (each load of P serves four row tiles);
   // r > 64 keeps 16-row workgroups (the accumulators of 4 x 8 tiles would
   // not fit).
   const int rows = M > 16 && r <= 64 ? 64 : 16;
+#define QN_SKINNY(C)                                                                          \
+  if (p_rows_l)                                                                               \
+    skinny_launch<C, true>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16,  \
+                           out_bf16);                                                         \
+  else                                                                                        \
+    skinny_launch<C, false>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, \
+                            out_bf16);
   switch (skinny_cols(r)) {
-    case 1: skinny_launch<1>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    case 2: skinny_launch<2>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    case 4: skinny_launch<4>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
-    default: skinny_launch<8>(rows, s, in, M, L, P, r, scale, ksplit, out_f32, out_scaled_bf16, out_bf16); break;
+    case 1: QN_SKINNY(1) break;
+    case 2: QN_SKINNY(2) break;
+    case 4: QN_SKINNY(4) break;
+    default: QN_SKINNY(8) break;
   }
+#undef QN_SKINNY
   return hipGetLastError();
 }
 
@@ -845,13 +848,6 @@ hipError_t launch_lora_reduce(const float* part, int nslice, int64_t n, float sc
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(lora_reduce_kernel, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256),
                      0, st, part, nslice, n, scale, out_scaled, out);
-  return hipGetLastError();
-}
-
-hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out, hipStream_t s) {
-  if (L == 0 || C == 0) return hipSuccess;
-  hipLaunchKernelGGL(transpose_kernel, dim3(static_cast<uint32_t>((L + 63) / 64)), dim3(256), 0, s,
-                     in, L, C, out);
   return hipGetLastError();
 }
 

@@ -49,11 +49,10 @@ hipError_t launch_dequant(const WeightView& w, bool out_bf16, void* out, hipStre
 // aligned, L % 32 == 0).  ksplit == 1 writes any of: fp32 result,
 // bf16(scale * result), bf16(result); ksplit > 1 splits L over ksplit
 // workgroups and writes fp32 partial sums out_f32[ksplit][M][r].
+// With p_rows_l, P is stored [L, r] instead (B for t = dy B, read in place).
 hipError_t launch_skinny(const uint16_t* in, int64_t M, int64_t L, const uint16_t* P, int r,
                          float scale, float* out_f32, uint16_t* out_scaled_bf16,
-                         uint16_t* out_bf16, int ksplit, hipStream_t s);
-// out[C, L] = in[L, C]^T (bf16, C <= 128).
-hipError_t launch_transpose(const uint16_t* in, int64_t L, int C, uint16_t* out, hipStream_t s);
+                         uint16_t* out_bf16, int ksplit, hipStream_t s, bool p_rows_l = false);
 // Largest number of L-slices of the decode LoRA-down (the forward
 // workspace holds that many fp32 partial sums of u).
 constexpr int kDecodeMaxSlices = 512;
