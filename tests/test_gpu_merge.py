@@ -94,10 +94,13 @@ def test_merge_training_weights(shape, r, alpha):
     _check_merge(got, want, f"{shape} r={r} sampled rows", mag)
 
 
-@pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33), (64, 192, 1)])
+@pytest.mark.parametrize("N,K,r", [(192, 320, 100), (128, 576, 5), (64, 64, 33), (64, 192, 1),
+                                   (19200, 320, 5), (12352, 576, 100)])
 def test_merge_ragged_columns_and_ranks(N, K, r):
     """K not a multiple of the 256-column workgroup tile, ranks that pad the
-    32-deep MFMA steps (1, 5, 33, 100)."""
+    32-deep MFMA steps (1, 5, 33, 100).  The two tall weights have more than
+    512 (64-row group, 256-column block) pairs, so each workgroup walks two
+    row groups and the last one only one."""
     wl = synth.train_linear(N, K, M=16, seed=N + K + r, r=r, alpha=2.0 * r)
     _, _, _, got, want, mag = _merge_case(wl)
     _check_merge(got, want, f"{N}x{K} r={r}", mag)
