@@ -65,7 +65,9 @@ __device__ __forceinline__ void load16(const void* __restrict__ w, int64_t e0, i
 // function is monotone (the host built the table with the same function).
 __device__ __forceinline__ uint32_t bucket_code(const QuantBucket* sbk, float v, float sc,
                                                 float top, float& thr) {
-  float f = fminf(fmaxf(fmaf(v, sc, sc), 0.0f), top);
+  // median of (v sc + sc, 0, top): the clamp min(max(., 0), top) in one
+  // instruction (a NaN, which the clamp maps to 0, converts to bucket 0 too)
+  float f = __builtin_amdgcn_fmed3f(fmaf(v, sc, sc), 0.0f, top);
   QuantBucket e = sbk[static_cast<uint32_t>(f)];
   thr = e.thr;
   return e.base + (v > e.thr ? 1u : 0u);
