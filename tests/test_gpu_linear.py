@@ -229,3 +229,25 @@ def test_decode_gemv_long_rows(shape, M, dq):
                                  wl.alpha, wl.r)
     _check(f"y {shape} M={M} dq={dq}", to_np(y), want)
     _check(f"u {shape} M={M}", to_np(u), linear.lora_down(f64(x), f64(wl.A)))
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("shape", [(8192, 22016), (22016, 8192), (8256, 4160)],
+                         ids=["65b-down", "65b-gate", "uneven"])
+def test_decode_gemv_long_rows_rank16(shape, M):
+    """The long-row and uneven decode shapes at r = 16, alpha = 32 (the
+    decode rank of the bench; M r then stays within the thread count, the
+    other branch of the epilogue's u sum): y and u_out against the oracle,
+    with the first 16 ranks of the shape's adapter."""
+    N, K = shape
+    wl, qw, What = _decode_weight(N, K)
+    r, alpha = 16, 32.0
+    x = wl.x[:M]
+    A = np.ascontiguousarray(wl.A[:r])
+    B = np.ascontiguousarray(wl.B[:, :r])
+    u = torch.empty((M, r), dtype=torch.bfloat16, device="cuda:0")
+    y = qn.qlora_linear_fwd(qw[True], bf16_dev(x), bf16_dev(A), bf16_dev(B), r, alpha, u_out=u)
+    torch.cuda.synchronize()
+    want = linear.linear_forward(f64(x), What[True].astype(np.float64), f64(A), f64(B), alpha, r)
+    _check(f"y {shape} r=16 M={M}", to_np(y), want)
+    _check(f"u {shape} r=16 M={M}", to_np(u), linear.lora_down(f64(x), f64(A)))

@@ -98,3 +98,27 @@ def test_null_adapter_pointers_are_the_frozen_layer(M):
     qn.qlora_linear_bwd_dx(qw, dy, None, None, 16, 32.0, dx=dx1, ws=ws)
     torch.cuda.synchronize()
     assert torch.equal(y0, y1) and torch.equal(dx0, dx1)
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+@pytest.mark.parametrize("shape", [(11008, 4096), (8192, 22016), (4096, 4096)],
+                         ids=["11008x4096", "8192x22016", "4096x4096"])
+def test_lora_only_decode_rank16(shape, M):
+    """W = 0 at decode shapes and r = 16, the decode rank of the bench: the
+    LoRA-down launch's partial sums as the GEMV's epilogue adds them up
+    (11008 x 4096 at M = 1 and 8192 x 22016 take several GEMV passes), and
+    at 4096 x 4096, M = 1, u computed inside the GEMV launch from the x
+    slices it stages."""
+    n, k = shape
+    r, alpha = 16, 32.0
+    qw = qn.quantize_weight(torch.zeros((n, k), dtype=torch.bfloat16, device="cuda:0"))
+    rng = np.random.default_rng(9100 + M + n // 64)
+    x = synth.bf16_bits(rng.standard_normal((M, k), dtype=np.float32))
+    A = synth.bf16_bits((rng.standard_normal((r, k)) * 0.01).astype(np.float32))
+    B = synth.bf16_bits((rng.standard_normal((n, r)) * 0.01).astype(np.float32))
+    u = torch.empty((M, r), dtype=torch.bfloat16, device="cuda:0")
+    y = qn.qlora_linear_fwd(qw, bf16_dev(x), bf16_dev(A), bf16_dev(B), r, alpha, u_out=u)
+    torch.cuda.synchronize()
+    check(f"lora-only y {shape} r=16 M={M}", to_np(y),
+          linear.linear_forward(f64(x), np.zeros((n, k)), f64(A), f64(B), alpha, r))
+    check(f"u {shape} r=16 M={M}", to_np(u), linear.lora_down(f64(x), f64(A)))
