@@ -6,8 +6,8 @@ linear workload at the Llama-7B MLP shapes, for both orientations of the
 weight (gate/up W 11008x4096 and down W 4096x11008; bf16 Student-t(5)
 weights scaled to std 0.02, M = 2048 tokens, LoRA r = 16, alpha = 32):
 
-  quantise  nf4_quantize_dq of the bf16 weight (quantise + double-quantise
-            in one launch)
+  quantise  nf4_quantize_dq_batch of both bf16 weights (quantise +
+            double-quantise of the two in one launch)
   dequant   nf4_dequant to bf16 (the standalone bit-exact expansion)
   gemm      qlora_linear_fwd    at M = 2048 with r = 0: exactly one launch
             of the fused dequant GEMM kernel per call (the roofline kernel)
@@ -34,7 +34,7 @@ layer copies beyond the Infinity Cache: microseconds per layer, and the
 
 After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
 v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
-N(0, 0.02) drawn and quantised on the device: quantise + DQ (fused), fwd, bwd_dx
+N(0, 0.02) drawn and quantised on the device: quantise + DQ (one launch), fwd, bwd_dx
 and lora_grads of all seven at M = 2048, r = 64, alpha = 16.  "layer_65b"
 times fwd and bwd_dx of the 65B-shaped layer (8192 hidden, 22016 MLP, bf16
 N(0, 0.015)) at M = 4096, r = 64, alpha = 16.  "hbm_measured" gives the
@@ -42,10 +42,11 @@ streaming-read rate of qn_hbm_read_probe (16-byte loads, read only) and
 the copy and read rates of plain torch kernels on 1 GiB, as context for the
 fractions of the 8 TB/s peak.
 
-"quantise_65b" times the quantiser (nf4_quantize_dq) over 80 layers of the 65B shapes (7 projections,
-809.5M weights per layer): 8 distinct device-resident layers of bf16
-N(0, 0.015) weights (torch's generator, seed 5; each layer is 1.6 GB, far
-beyond the Infinity Cache) quantised in turn 10 times over.
+"quantise_65b" times the quantiser (nf4_quantize_dq_batch, one launch per
+layer) over 80 layers of the 65B shapes (7 projections, 809.5M weights per
+layer): 8 distinct device-resident layers of bf16 N(0, 0.015) weights
+(torch's generator, seed 5; each layer is 1.6 GB, far beyond the Infinity
+Cache) quantised in turn 10 times over.
 
 "adamw_7b_lora" times lora_adamw_step over all 40 M LoRA parameters of a
 7B model at r = 16 (seven projections x 32 layers).
@@ -345,8 +346,9 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     """One decoder layer's seven projections on the device: bf16 N(0, std)
     weights and N(0, 1) activations from torch's generator (seed), A, B
     N(0, 0.01).  Phases (each over all seven, median of reps after a
-    warm-up): quantise (nf4_quantize + dq_quantize_scales), fwd, bwd_dx and,
-    with with_quantise, lora_grads on the saved u and t."""
+    warm-up): quantise (quantise + DQ of all seven weights in one
+    nf4_quantize_dq_batch launch), fwd, bwd_dx and, with with_quantise,
+    lora_grads on the saved u and t."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     bf = torch.bfloat16
@@ -371,11 +373,13 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     torch.cuda.synchronize()
 
     def run(ph):
+        if ph == "quantise":  # the layer's seven weights in one launch
+            qn.nf4_quantize_dq_batch([P["W"].reshape(-1) for P in projs],
+                                     outs=[(P["qw"].packed, P["qw"].qscale, P["qw"].gscale)
+                                           for P in projs])
+            return
         for P in projs:
-            if ph == "quantise":
-                qn.nf4_quantize_dq(P["W"].reshape(-1), packed=P["qw"].packed,
-                                   qscale=P["qw"].qscale, gscale=P["qw"].gscale)
-            elif ph == "fwd":
+            if ph == "fwd":
                 qn.qlora_linear_fwd(P["qw"], P["x"], P["A"], P["B"], r, alpha, y=P["y"],
                                     u_out=P["u"], ws=ws)
             elif ph == "bwd":
@@ -532,10 +536,11 @@ def quantise_65b(qn, torch, dev, synth):
         layers.append(proj)
     numel = sum(n * k for (_, n, k) in synth.LLAMA65B_TARGETS)
 
-    def run():
+    def run():  # one nf4_quantize_dq_batch launch per layer (its seven weights)
         for i in range(Q65_LAYERS):
-            for (w, packed, q8, c2) in layers[i % Q65_DISTINCT]:
-                qn.nf4_quantize_dq(w, packed=packed, qscale=q8, gscale=c2)
+            proj = layers[i % Q65_DISTINCT]
+            qn.nf4_quantize_dq_batch([w for (w, _, _, _) in proj],
+                                     outs=[(packed, q8, c2) for (_, packed, q8, c2) in proj])
 
     run()  # warm-up
     torch.cuda.synchronize()
@@ -649,11 +654,14 @@ def main():
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record()
+            if ph == "quantise":  # both weights in one launch
+                qn.nf4_quantize_dq_batch([L["W"].reshape(-1) for L in layers],
+                                         outs=[(L["qw"].packed, L["qw"].qscale, L["qw"].gscale)
+                                               for L in layers])
             for L in layers:
                 qw = L["qw"]
                 if ph == "quantise":
-                    qn.nf4_quantize_dq(L["W"].reshape(-1), packed=qw.packed, qscale=qw.qscale,
-                                       gscale=qw.gscale)
+                    break
                 elif ph == "dequant":
                     qn.nf4_dequant(qw, torch.bfloat16, out=L["deq"])
                 elif ph == "gemm":

@@ -29,7 +29,8 @@ EXPORTS = ("qn_status_string", "nf4_codebook", "nf4_quantize", "dq_quantize_scal
            "lora_grads", "qlora_merge", "lora_adamw_step", "lora_dropout",
            "qlora_linear_fwd_dropout", "qlora_linear_bwd_dx_dropout", "fp4_codebook",
            "fp4_quantize", "dq_quantize_scales_fp8", "qlora_linear_fwd_noalloc",
-           "dq_quantize_scales_centred", "nf4_quantize_dq", "qn_hbm_read_probe")
+           "dq_quantize_scales_centred", "nf4_quantize_dq", "nf4_quantize_dq_batch",
+           "qn_hbm_read_probe")
 
 
 class QnError(RuntimeError):
@@ -72,6 +73,8 @@ def load_library():
         "dq_quantize_scales_fp8": (ctypes.c_int, [vp, i64, i32, vp, vp, vp]),
         "dq_quantize_scales_centred": (ctypes.c_int, [vp, i64, i32, vp, vp, vp, vp]),
         "nf4_quantize_dq": (ctypes.c_int, [vp, i32, i64, i32, i32, i32, i32, vp, vp, vp, vp, vp]),
+        "nf4_quantize_dq_batch": (ctypes.c_int, [i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp,
+                                                 vp, vp]),
         "qn_hbm_read_probe": (ctypes.c_int, [vp, i64, vp, vp]),
         "nf4_dequant": (ctypes.c_int, [wp, i32, vp, vp]),
         "qn_workspace_bytes": (sz, [i32, i64, i64, i64, i32]),
@@ -216,6 +219,68 @@ def nf4_quantize_dq(w, quant_type="nf4", scale_type="u8", packed=None, qscale=No
         _ptr(w), dt, n, BLOCKSIZE, GROUP, _QUANT_TYPES[quant_type], _SCALE_TYPES[scale_type],
         _ptr(packed), _ptr(absmax), _ptr(qscale), _ptr(gscale), _stream(stream)))
     return packed, qscale, gscale
+
+
+def nf4_quantize_dq_batch(ws, quant_type="nf4", scale_type="u8", outs=None, absmax=None,
+                          stream=None):
+    """nf4_quantize_dq over up to 8 weights of one dtype in one launch:
+    returns a list of (packed, qscale, gscale), one per weight.  outs, if
+    given, holds such triples to write into; absmax, if given, a list of
+    fp32 tensors (or None entries) for the block constants."""
+    torch = _torch()
+    lib = load_library()
+    if quant_type not in _QUANT_TYPES or scale_type not in ("u8", "fp8"):
+        raise ValueError("quant_type must be 'nf4' or 'fp4', scale_type 'u8' or 'fp8'")
+    n = len(ws)
+    if n == 0:
+        return []
+    dtypes = {w.dtype for w in ws}
+    if len(dtypes) != 1 or dtypes.pop() not in (torch.float32, torch.bfloat16):
+        raise ValueError("nf4_quantize_dq_batch: weights must all be float32 or all bfloat16")
+    res = []
+    for i, w in enumerate(ws):
+        _dev(w, w.dtype, name="w")
+        m = w.numel()
+        nb = -(-m // BLOCKSIZE)
+        ng = -(-nb // GROUP)
+        dev = w.device
+        if outs is not None:
+            packed, qscale, gscale = outs[i]
+        else:
+            packed = torch.empty(m // 2, dtype=torch.uint8, device=dev)
+            qscale = torch.empty(nb, dtype=torch.uint8, device=dev)
+            gscale = torch.empty(ng, dtype=torch.float32, device=dev)
+        _dev(packed, torch.uint8, m // 2, "packed")
+        _dev(qscale, torch.uint8, nb, "qscale")
+        _dev(gscale, torch.float32, ng, "gscale")
+        if absmax is not None:
+            _dev(absmax[i], torch.float32, nb, "absmax")
+        res.append((packed, qscale, gscale))
+    vpa = ctypes.c_void_p * n
+    wa = vpa(*[_ptr(w) for w in ws])
+    na = (ctypes.c_int64 * n)(*[w.numel() for w in ws])
+    pa = vpa(*[_ptr(r[0]) for r in res])
+    qa = vpa(*[_ptr(r[1]) for r in res])
+    ga = vpa(*[_ptr(r[2]) for r in res])
+    aa = vpa(*[_ptr(a) for a in absmax]) if absmax is not None else None
+    dt = QN_F32 if ws[0].dtype == torch.float32 else QN_BF16
+    _check("nf4_quantize_dq_batch", lib.nf4_quantize_dq_batch(
+        n, wa, na, dt, BLOCKSIZE, GROUP, _QUANT_TYPES[quant_type], _SCALE_TYPES[scale_type],
+        pa, aa, qa, ga, _stream(stream)))
+    return res
+
+
+def quantize_weights(ws, stream=None, quant_type="nf4", scale_type="u8"):
+    """Double-quantised QuantWeight of each [N, K] tensor in ws (one dtype),
+    at most 8 per launch (nf4_quantize_dq_batch)."""
+    out = []
+    for i in range(0, len(ws), 8):
+        part = ws[i:i + 8]
+        for w, (packed, qscale, gscale) in zip(part, nf4_quantize_dq_batch(
+                part, quant_type, scale_type, stream=stream)):
+            out.append(QuantWeight(packed, w.shape[0], w.shape[1], qscale=qscale, gscale=gscale,
+                                   quant_type=quant_type, scale_type=scale_type))
+    return out
 
 
 def _quantize(fn, w, packed, absmax, stream):

@@ -308,6 +308,49 @@ int nf4_quantize_dq(const void* w, int32_t dtype, int64_t numel, int32_t blocksi
                                            gscale, as_stream(stream)));
 }
 
+int nf4_quantize_dq_batch(int32_t n, const void* const* w, const int64_t* numel, int32_t dtype,
+                          int32_t blocksize, int32_t group, int32_t quant_type,
+                          int32_t scale_type, uint8_t* const* packed, float* const* absmax,
+                          uint8_t* const* qscale, float* const* gscale, void* stream) {
+  if (blocksize != kBlock || group != kGroup) return QN_ERR_UNSUPPORTED;
+  if (dtype != QN_F32 && dtype != QN_BF16) return QN_ERR_UNSUPPORTED;
+  if (quant_type != QN_NF4 && quant_type != QN_FP4) return QN_ERR_UNSUPPORTED;
+  if (scale_type != QN_SCALE_U8 && scale_type != QN_SCALE_FP8) return QN_ERR_UNSUPPORTED;
+  if (n < 0 || n > qn::kQdqMaxBatch) return QN_ERR_SHAPE;
+  if (n == 0) return QN_OK;
+  if (!w || !numel || !packed || !qscale || !gscale) return QN_ERR_NULL;
+  qn::QdqBatch b{};
+  const int64_t per = static_cast<int64_t>(kBlock) * kGroup;  // weights per group
+  int64_t groups = 0;
+  for (int i = 0; i < n; ++i) {
+    const int64_t m = numel[i];
+    if (m < 0 || (m & 1)) return QN_ERR_SHAPE;
+    if (m > 0) {
+      float* am = absmax ? absmax[i] : nullptr;
+      if (!w[i] || !packed[i] || !qscale[i] || !gscale[i]) return QN_ERR_NULL;
+      if (!aligned(w[i], 16) || !aligned(packed[i], 16) || !aligned(gscale[i], 4) ||
+          (am && !aligned(am, 4)))
+        return QN_ERR_ALIGN;
+      b.w[b.n] = w[i];
+      b.numel[b.n] = m;
+      b.packed[b.n] = packed[i];
+      b.absmax[b.n] = am;
+      b.qscale[b.n] = qscale[i];
+      b.gscale[b.n] = gscale[i];
+      groups += (m + per - 1) / per;
+      if (groups > INT32_MAX) return QN_ERR_SHAPE;
+      b.gend[b.n] = static_cast<uint32_t>(groups);
+      ++b.n;
+    }
+  }
+  if (b.n == 0) return QN_OK;
+  const int qt = quant_type == QN_FP4 ? qn::kQuantFP4 : qn::kQuantNF4;
+  if (!qn::tables(qt)) return QN_ERR_UNSUPPORTED;
+  (void)hipGetLastError();
+  return hip_status(qn::launch_quantize_dq_batch(b, dtype == QN_BF16, qt,
+                                                 scale_type == QN_SCALE_FP8, as_stream(stream)));
+}
+
 int dq_quantize_scales_centred(const float* absmax, int64_t nblocks, int32_t group,
                                uint8_t* qscale, float* gscale, float* offset, void* stream) {
   if (group != kGroup) return QN_ERR_UNSUPPORTED;

@@ -38,6 +38,23 @@ hipError_t launch_dq(const float* absmax, int64_t nblocks, bool fp8, uint8_t* qs
 hipError_t launch_quantize_dq(const void* w, bool bf16, int64_t numel, int quant_type, bool fp8,
                               uint8_t* packed, float* absmax, uint8_t* qscale, float* gscale,
                               hipStream_t s);
+// Several weights of one dtype and code type in one launch: entry i is
+// weight w[i] of numel[i] elements and its outputs; gend[i] is one past the
+// last group (workgroup) of entries 0..i.  The struct travels by value as
+// a kernel argument.
+constexpr int kQdqMaxBatch = 8;
+struct QdqBatch {
+  const void* w[kQdqMaxBatch];
+  int64_t numel[kQdqMaxBatch];
+  uint8_t* packed[kQdqMaxBatch];
+  float* absmax[kQdqMaxBatch];
+  uint8_t* qscale[kQdqMaxBatch];
+  float* gscale[kQdqMaxBatch];
+  uint32_t gend[kQdqMaxBatch];
+  int n;
+};
+hipError_t launch_quantize_dq_batch(const QdqBatch& batch, bool bf16, int quant_type, bool fp8,
+                                    hipStream_t s);
 // Mean-centred level-2 code: mu (pairwise fp64 sum of the constants / n,
 // written to *mu), then per 256-group c2 = max |c - mu| and signed codes.
 // gscale doubles as scratch for the partial sums before its final values.

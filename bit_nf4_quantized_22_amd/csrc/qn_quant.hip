@@ -224,17 +224,29 @@ __device__ __forceinline__ uint8_t dq_code(float c, float c2, const float* sthr)
 // written too when absmax is not null.
 constexpr int kQDPasses = 4;
 
+// LDS of one group's quantise + double-quantise.
+struct QdqShared {
+  QuantBucket sbk[kMaxBuckets];
+  float sthr[256];
+  float sconst[256];
+  float smax[4];
+};
+
+// Group `grp` (256 blocks of 64 weights) of one weight: its 4-bit codes,
+// block constants, their 8-bit codes and the group constant.
 template <bool kBf16, bool kFP8>
-__global__ __launch_bounds__(kQThreads) void quantize_dq_kernel(
-    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
-    float* __restrict__ absmax, uint8_t* __restrict__ qscale, float* __restrict__ gscale,
-    QuantParams P) {
+__device__ __forceinline__ void quantize_dq_group(QdqShared& sh, const void* __restrict__ w,
+                                                  int64_t numel, uint8_t* __restrict__ packed,
+                                                  float* __restrict__ absmax,
+                                                  uint8_t* __restrict__ qscale,
+                                                  float* __restrict__ gscale,
+                                                  const QuantParams& P, int64_t grp) {
   static_assert(kQDPasses * kQPerGroup == 256 * 64, "one workgroup per 256-block group");
-  __shared__ QuantBucket sbk[kMaxBuckets];
-  __shared__ float sthr[256];
-  __shared__ float sconst[256];
-  __shared__ float smax[4];
-  const int64_t g0 = static_cast<int64_t>(blockIdx.x) * (kQDPasses * kQPerGroup);
+  QuantBucket* sbk = sh.sbk;
+  float* sthr = sh.sthr;
+  float* sconst = sh.sconst;
+  float* smax = sh.smax;
+  const int64_t g0 = grp * (kQDPasses * kQPerGroup);
   const bool full = g0 + kQDPasses * kQPerGroup <= numel;  // uniform
   // whole groups of bf16 weights: the raw 16-byte words of all passes are
   // loaded first (32 registers) and widened pass by pass
@@ -280,9 +292,33 @@ __global__ __launch_bounds__(kQThreads) void quantize_dq_kernel(
   __syncthreads();
   const float c2 = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
   const int64_t nblocks = (numel + 63) / 64;
-  const int64_t bi = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (threadIdx.x == 0) gscale[blockIdx.x] = c2;
+  const int64_t bi = grp * 256 + threadIdx.x;
+  if (threadIdx.x == 0) gscale[grp] = c2;
   if (bi < nblocks) qscale[bi] = dq_code<kFP8>(sconst[threadIdx.x], c2, sthr);
+}
+
+template <bool kBf16, bool kFP8>
+__global__ __launch_bounds__(kQThreads) void quantize_dq_kernel(
+    const void* __restrict__ w, int64_t numel, uint8_t* __restrict__ packed,
+    float* __restrict__ absmax, uint8_t* __restrict__ qscale, float* __restrict__ gscale,
+    QuantParams P) {
+  __shared__ QdqShared sh;
+  quantize_dq_group<kBf16, kFP8>(sh, w, numel, packed, absmax, qscale, gscale, P, blockIdx.x);
+}
+
+// Several weights in one launch: workgroup b serves entry j, the first with
+// b < gend[j], at group b - gend[j - 1] (j and the entry's fields are
+// uniform, read from the kernel arguments with scalar loads).
+template <bool kBf16, bool kFP8>
+__global__ __launch_bounds__(kQThreads) void quantize_dq_batch_kernel(QdqBatch B, QuantParams P) {
+  __shared__ QdqShared sh;
+  const uint32_t b = blockIdx.x;
+  int j = 0;
+  while (j + 1 < B.n && b >= B.gend[j]) ++j;
+  j = __builtin_amdgcn_readfirstlane(j);
+  const uint32_t g = b - (j > 0 ? B.gend[j - 1] : 0u);
+  quantize_dq_group<kBf16, kFP8>(sh, B.w[j], B.numel[j], B.packed[j], B.absmax[j], B.qscale[j],
+                                 B.gscale[j], P, g);
 }
 
 // One workgroup of 256 lanes per group of 256 block constants.
@@ -502,6 +538,24 @@ hipError_t launch_quantize_dq(const void* w, bool bf16, int64_t numel, int quant
                        absmax, qscale, gscale, P);
   QN_QDQ(true, false) QN_QDQ(true, true) QN_QDQ(false, false) QN_QDQ(false, true)
 #undef QN_QDQ
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_dq_batch(const QdqBatch& batch, bool bf16, int quant_type, bool fp8,
+                                    hipStream_t s) {
+  const uint32_t groups = batch.n > 0 ? batch.gend[batch.n - 1] : 0u;
+  if (groups == 0) return hipSuccess;
+  const Tables* t = tables(quant_type);
+  QuantParams P;
+  P.scale = t->bucket_scale;
+  P.nbuckets = static_cast<uint32_t>(t->nbuckets);
+  for (int i = 0; i < 15; ++i) P.thr[i] = t->thr[i];
+#define QN_QDQB(B, F)                                                                          \
+  if (bf16 == B && fp8 == F)                                                                   \
+    hipLaunchKernelGGL((quantize_dq_batch_kernel<B, F>), dim3(groups), dim3(kQThreads), 0, s,  \
+                       batch, P);
+  QN_QDQB(true, false) QN_QDQB(true, true) QN_QDQB(false, false) QN_QDQB(false, true)
+#undef QN_QDQB
   return hipGetLastError();
 }
 

@@ -211,6 +211,28 @@ QN_API int nf4_quantize_dq(const void* w, int32_t dtype, int64_t numel, int32_t 
                            void* stream);
 
 /*
+ * nf4_quantize_dq_batch -- nf4_quantize_dq over n weights in one launch,
+ * for callers that quantise many weights at once (the projections of a
+ * layer, a model at load time): [rkmt] §2.2.1-2.2.2 and [kwkr] §3.1 per
+ * weight, as in nf4_quantize_dq.  Entry i is the weight w[i] of numel[i]
+ * elements with its own outputs packed[i], qscale[i], gscale[i] and
+ * absmax[i] (absmax itself may be NULL: no constants written for any
+ * entry; a NULL absmax[i] skips entry i's).  All entries share dtype,
+ * quant_type and scale_type.  The bytes written equal those of n separate
+ * nf4_quantize_dq calls, bit for bit; outputs of different entries must
+ * not overlap.  The host arrays are read during the call only.
+ *   n  0..8 (QN_ERR_SHAPE otherwise); entries with numel[i] == 0 are
+ *      skipped (their pointers are not read).
+ * Other arguments and errors as nf4_quantize_dq, checked for every entry
+ * before anything runs.
+ */
+QN_API int nf4_quantize_dq_batch(int32_t n, const void* const* w, const int64_t* numel,
+                                 int32_t dtype, int32_t blocksize, int32_t group,
+                                 int32_t quant_type, int32_t scale_type, uint8_t* const* packed,
+                                 float* const* absmax, uint8_t* const* qscale,
+                                 float* const* gscale, void* stream);
+
+/*
  * dq_quantize_scales_centred -- mean-centred double quantisation.
  * [rkmt] §2.2.2 and [kwkr] §3.1 quantise the block constants to 8 bits a
  * second time; the publication the pages summarise subtracts the constants'

@@ -336,3 +336,34 @@ def test_read_probe_argument_errors(lib):
     assert f(FAKE, 64, None, None) == qn.QN_ERR_NULL
     assert f(ODD, 64, FAKE, None) == qn.QN_ERR_ALIGN
     assert f(None, 0, None, None) == qn.QN_OK
+
+
+def test_batched_quantise_argument_errors(lib):
+    """nf4_quantize_dq_batch checks every entry before anything runs."""
+    f = lib.nf4_quantize_dq_batch
+    vp2 = ctypes.c_void_p * 2
+
+    def call(n=2, w=(FAKE, FAKE), numel=(128, 256), dt=qn.QN_BF16, bs=64, grp=256, qt=0, st=0,
+             p=(FAKE, FAKE), a=None, q=(FAKE, FAKE), g=(FAKE, FAKE)):
+        arr = lambda t: None if t is None else vp2(*t)
+        return f(n, arr(w), None if numel is None else (ctypes.c_int64 * 2)(*numel), dt, bs, grp,
+                 qt, st, arr(p), arr(a), arr(q), arr(g), None)
+
+    assert call(n=9) == qn.QN_ERR_SHAPE
+    assert call(n=-1) == qn.QN_ERR_SHAPE
+    assert call(n=0, w=None, numel=None, p=None, q=None, g=None) == qn.QN_OK
+    assert call(bs=32) == qn.QN_ERR_UNSUPPORTED
+    assert call(grp=128) == qn.QN_ERR_UNSUPPORTED
+    assert call(st=qn.QN_SCALE_CENTRED) == qn.QN_ERR_UNSUPPORTED
+    assert call(qt=2) == qn.QN_ERR_UNSUPPORTED
+    assert call(dt=2) == qn.QN_ERR_UNSUPPORTED
+    assert call(numel=(128, 63)) == qn.QN_ERR_SHAPE
+    assert call(numel=(-2, 128)) == qn.QN_ERR_SHAPE
+    assert call(w=None) == qn.QN_ERR_NULL
+    assert call(numel=None) == qn.QN_ERR_NULL
+    assert call(q=(FAKE, None)) == qn.QN_ERR_NULL
+    assert call(w=(FAKE, ODD)) == qn.QN_ERR_ALIGN
+    assert call(a=(None, ODD)) == qn.QN_ERR_ALIGN
+    # entries of zero elements are skipped without reading their pointers
+    assert call(numel=(0, 0), w=(None, None), p=(None, None), q=(None, None),
+                g=(None, None)) == qn.QN_OK

@@ -212,3 +212,66 @@ def test_fused_quantise_dq_equals_the_two_calls(numel, dtype, kind, scale):
         assert np.array_equal(p2.cpu().numpy(), op)
         assert np.array_equal(q2.cpu().numpy(), oq)
         assert np.array_equal(g2.cpu().numpy().view(np.uint32), og.view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("kind,scale", [("nf4", "u8"), ("nf4", "fp8"), ("fp4", "u8")])
+def test_batched_quantise_dq_equals_one_call_per_weight(dtype, kind, scale):
+    """nf4_quantize_dq_batch over eight weights in one launch (sizes with
+    partial blocks and groups, one empty, whole-group and multi-group ones)
+    writes the bytes of eight nf4_quantize_dq calls, bit for bit, with and
+    without block-constant outputs for some entries; the batch of one and
+    the small entries also against the oracle."""
+    sizes = [64, 4096 + 64 * 3, 0, 16384, 16384 * 3 + 64 * 5 + 32, 1000, 4096 * 1024, 256 * 258]
+    ws, Ws = [], []
+    for i, n in enumerate(sizes):
+        rng = np.random.default_rng(4200 + i)
+        W = (rng.standard_t(5, n) * 0.02).astype(np.float32)
+        if dtype == "bf16":
+            W = synth.bf16_bits(W)
+        Ws.append(W)
+        ws.append(weight_dev(W, dtype).reshape(-1))
+    nb = [-(-n // 64) for n in sizes]
+    am = [torch.full((b,), float("nan"), device="cuda:0") if i % 2 == 0 else None
+          for i, b in enumerate(nb)]
+    got = qn.nf4_quantize_dq_batch(ws, kind, scale, absmax=am)
+    one = qn.nf4_quantize_dq_batch(ws[1:2], kind, scale)
+    torch.cuda.synchronize()
+    for i, w in enumerate(ws):
+        a1 = torch.full((nb[i],), float("nan"), device="cuda:0")
+        p1, q1, g1 = qn.nf4_quantize_dq(w, kind, scale, absmax=a1 if am[i] is not None else None)
+        torch.cuda.synchronize()
+        p2, q2, g2 = got[i]
+        assert torch.equal(p1, p2) and torch.equal(q1, q2), f"entry {i}"
+        assert torch.equal(g1.view(torch.int32), g2.view(torch.int32)), f"entry {i}"
+        if am[i] is not None:
+            assert torch.equal(a1.view(torch.int32), am[i].view(torch.int32)), f"entry {i}"
+    from oracle import codebooks
+    for i in (0, 1, 5):
+        op, oa = codebooks.quantize_4bit(weight_f32(Ws[i], dtype), kind)
+        oq, og = (codebooks.double_quantize_fp8(oa) if scale == "fp8"
+                  else nf4.double_quantize(oa))
+        p, q, g = got[i]
+        assert np.array_equal(p.cpu().numpy(), op)
+        assert np.array_equal(q.cpu().numpy(), oq)
+        assert np.array_equal(g.cpu().numpy().view(np.uint32), og.view(np.uint32))
+    for a, b in zip(one[0], got[1]):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_quantize_weights_matches_quantize_weight():
+    """quantize_weights (batches of up to 8 per launch) gives the weights
+    quantize_weight gives one by one: nine 7B-like projections, so two
+    launches."""
+    rng = np.random.default_rng(77)
+    shapes = [(256, 512)] * 4 + [(704, 256)] * 2 + [(256, 704)] * 3
+    ws = [weight_dev(synth.bf16_bits((rng.standard_normal(s) * 0.02).astype(np.float32)),
+                     "bf16").reshape(s) for s in shapes]
+    got = qn.quantize_weights(ws)
+    torch.cuda.synchronize()
+    for w, g in zip(ws, got):
+        want = qn.quantize_weight(w)
+        torch.cuda.synchronize()
+        assert (g.N, g.K) == (want.N, want.K)
+        assert torch.equal(g.packed, want.packed) and torch.equal(g.qscale, want.qscale)
+        assert torch.equal(g.gscale.view(torch.int32), want.gscale.view(torch.int32))
