@@ -168,7 +168,7 @@ int fwd_impl(const qn_weight* w, const qn_bf16* x, const qn_bf16* xa, int64_t M,
     ws = nullptr;
     ws_bytes = 0;
     if (need > 0) {
-      if (qn::scratch_address(&ws) != hipSuccess) return QN_ERR_HIP;
+      if (qn::scratch_address(as_stream(stream), &ws) != hipSuccess) return QN_ERR_HIP;
       ws_bytes = qn::kScratchBytes;
     }
   }

@@ -86,9 +86,10 @@ hipError_t launch_read_probe(const void* buf, int64_t bytes, uint32_t* sink, hip
 // Size of the library's own per-device scratch array (qn_scratch.hip), the
 // workspace of the allocation-free forward.
 constexpr size_t kScratchBytes = static_cast<size_t>(64) << 20;
-// Device address of the current device's scratch array (resolved once per
-// device, then cached).
-hipError_t scratch_address(void** out);
+// Device address of the scratch array of the device that `stream` belongs
+// to (the current device for the null stream), resolved once per device
+// with that device current, then cached.
+hipError_t scratch_address(hipStream_t stream, void** out);
 
 // Threads per workgroup of the decode GEMV for an N x K weight.
 int gemv_threads(int64_t N, int64_t K);

@@ -24,15 +24,24 @@ void* g_addr[kMaxDevices] = {};
 
 }  // namespace
 
-hipError_t scratch_address(void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
+hipError_t scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return e;
+  // the stream's device (the null stream belongs to the current one)
+  int dev = cur;
+  if (stream && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
   if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lock(g_mu);
   if (!g_addr[dev]) {
+    // resolved with that device current, then the caller's device restored
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
     g_addr[dev] = p;

@@ -321,7 +321,8 @@ QN_API int qn_hbm_read_probe(const void* buf, int64_t bytes, uint32_t* sink, voi
  * 64 MiB return QN_ERR_WORKSPACE before anything runs (r = 64: M up to
  * 15887 tokens; r = 128: 7943).  The first call on a device resolves that
  * device's array address (hipGetSymbolAddress, with the stream's device
- * current); make it once before capturing a graph.  Every call on one GPU
+ * made current for it and the caller's device restored); make it once
+ * before capturing a graph.  Every call on one GPU
  * shares its array and nothing in it needs to start at zero, but calls
  * that may overlap on one GPU (different streams, or threads without
  * ordering) race on it and must be serialised by the caller.
