@@ -395,15 +395,20 @@ def decoder_layer(qn, torch, dev, targets, M, r, alpha, std, seed, with_quantise
     for ph in phases:
         run(ph)
         torch.cuda.synchronize()
+        # the quantise phase is a single launch: four of them back to back
+        # per timing, so the host's preparation of one overlaps the device's
+        # work on the previous one instead of being timed
+        k = 4 if ph == "quantise" else 1
         ts = []
         for _ in range(reps):
             s = torch.cuda.Event(enable_timing=True)
             e = torch.cuda.Event(enable_timing=True)
             s.record()
-            run(ph)
+            for _ in range(k):
+                run(ph)
             e.record()
             torch.cuda.synchronize()
-            ts.append(s.elapsed_time(e))
+            ts.append(s.elapsed_time(e) / k)
         ms[ph] = float(np.median(ts))
     flops = sum(linear_flops(P["N"], P["K"], M, r) for P in projs)
     nk = sum(P["N"] * P["K"] for P in projs)
