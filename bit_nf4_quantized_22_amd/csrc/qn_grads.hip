@@ -13,12 +13,15 @@
 // [column][token], row pitch 72 halves so the operand reads are
 // conflict-free); P is staged the same way.  Loads run two steps ahead
 // (64 KB in flight per workgroup): with one or two workgroups per CU the
-// bytes in flight set the streaming rate.  Workgroups own 256 columns and a
-// token chunk, write fp32 partial sums [chunk][r][C], and a second pass
-// sums the chunks in a fixed order and applies s (bit-reproducible).  Both
-// products share each of the two launches.  The wide matrices are read
-// once; the chunks are long enough that the partials stay a quarter of
-// them or less.
+// bytes in flight set the streaming rate.  Both products share each launch.
+// Two forms, each bit-reproducible:
+//   * column tiles (r % 8 == 0, u and t 16-byte aligned): a workgroup owns
+//     64 columns over all M tokens and writes s * sum directly, one launch;
+//   * token chunks (any r): workgroups own 256 columns and a token chunk,
+//     write fp32 partial sums [chunk][r][C], and a second pass sums the
+//     chunks in a fixed order and applies s.  The chunks are long enough
+//     that the partials stay a quarter of the input or less.
+// The wide matrices are read once in both.
 
 #include "qn_device.h"
 #include "qn_launch.h"
@@ -198,6 +201,181 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const
     }
 }
 
+// Column-tile form, no partial sums: a workgroup owns 64 columns of X over
+// all M tokens and writes s * sum straight into dA or dB, so one launch
+// does what the chunked kernel and its reduction do in two.  The four waves
+// take interleaved 64-token steps (wave w: steps w, w + 4, ...), each in its
+// own LDS region, so the main loop has no workgroup barrier: a wave's LDS
+// instructions are processed in issue order, which orders its transposed
+// stores, its operand reads and the next step's stores.  The waves' sums
+// are added in LDS in wave order at the end.  Needs r % 8 == 0 and P
+// 16-byte aligned: a lane loads 8 consecutive ranks of two adjacent tokens
+// as two 16-byte loads and stores them transposed as token pairs.
+//   X: lane (cg = lane / 8, rp = lane % 8) loads rows 16 q + 2 rp + {0, 1}
+//      (q < 4) of columns 8 cg .. + 7: 8 rows x 128 bytes per instruction.
+//   P: lane (tp = lane % 32, jh = lane / 32) loads tokens 2 tp + {0, 1},
+//      ranks 8 (jh + 2 q) .. + 7 (q < RT / 16).
+// Tokens past M read row M - 1 and are stored as zero P, ranks past r read
+// a valid chunk and are stored as zero.
+template <int RT>
+__global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const GradJob jb,
+                                                         int64_t M, int r, float s,
+                                                         float* __restrict__ dA,
+                                                         float* __restrict__ dB) {
+  // steps in flight per wave (four at r <= 32 was slower: 17.4 against 16.2 us at
+  // 11008 x 4096, M = 2048, r = 16)
+  constexpr int kDepth = RT <= 64 ? 2 : 1;
+  constexpr int kPV = RT / 8;                       // 16-byte P loads per lane per step
+  constexpr int kSX = 64 * kPitch, kSP = RT * kPitch;  // bf16 per wave region
+  constexpr int kSlab = RT < 64 ? RT : 64;          // ranks per cross-wave pass
+  constexpr int kRP = 65;                           // fp32 pitch of the pass buffer
+  constexpr int kStage = 4 * (kSX + kSP) * 2, kRed = 4 * kSlab * kRP * 4;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kStage > kRed ? kStage : kRed];
+
+  const bool second = static_cast<int>(blockIdx.x) >= ja.nwg;  // uniform
+  const uint16_t* X = second ? jb.X : ja.X;
+  const uint16_t* P = second ? jb.P : ja.P;
+  const int64_t C = second ? jb.C : ja.C;
+  const int ct = static_cast<int>(blockIdx.x) - (second ? ja.nwg : 0);
+  const int64_t c0 = static_cast<int64_t>(ct) * 64;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  uint16_t* sX = reinterpret_cast<uint16_t*>(smem) + wave * (kSX + kSP);
+  uint16_t* sP = sX + kSX;
+  const int nsteps = static_cast<int>((M + kStep - 1) / kStep);
+  const int nown = (nsteps + 3) / 4;                          // steps of wave 0
+  const int niter = (nown + kDepth - 1) / kDepth * kDepth;    // same count for every wave
+
+  const int cg = lane >> 3, rp = lane & 7;
+  const int tp = lane & 31, jh = lane >> 5;
+  const int rc = r >> 3;  // valid 8-rank chunks
+  const uint16_t* Xc = X + c0 + 8 * cg;
+  auto load_step = [&](int i, uint4 (&xv)[2 * kQ], uint4 (&pv)[kPV]) {
+    const int64_t mb = static_cast<int64_t>(4 * i + wave) * kStep;
+#pragma unroll
+    for (int q = 0; q < kQ; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t m = mb + 16 * q + 2 * rp + h;
+        m = m < M ? m : M - 1;
+        xv[2 * q + h] = *reinterpret_cast<const uint4*>(Xc + m * C);
+      }
+#pragma unroll
+    for (int q = 0; q < RT / 16; ++q)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        int64_t m = mb + 2 * tp + h;
+        m = m < M ? m : M - 1;
+        int jc = jh + 2 * q;
+        jc = jc < rc ? jc : rc - 1;
+        pv[2 * q + h] = *reinterpret_cast<const uint4*>(P + m * r + 8 * jc);
+      }
+  };
+
+  f32x4_t acc[RT / 16][4];
+#pragma unroll
+  for (int a = 0; a < RT / 16; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int l16 = lane & 15, g = lane >> 4;
+  auto step = [&](int i, uint4 (&xv)[2 * kQ], uint4 (&pv)[kPV]) {
+    const int64_t mb = static_cast<int64_t>(4 * i + wave) * kStep;
+    // X transposed: word (token pair rp + 8 q) of column 8 cg + e
+#pragma unroll
+    for (int q = 0; q < kQ; ++q) {
+      const uint32_t a0[4] = {xv[2 * q].x, xv[2 * q].y, xv[2 * q].z, xv[2 * q].w};
+      const uint32_t a1[4] = {xv[2 * q + 1].x, xv[2 * q + 1].y, xv[2 * q + 1].z, xv[2 * q + 1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = e & 1 ? a0[e >> 1] >> 16 : a0[e >> 1] & 0xFFFFu;
+        const uint32_t hi = e & 1 ? a1[e >> 1] & 0xFFFF0000u : a1[e >> 1] << 16;
+        const int row = 8 * cg + e, tok = 16 * q + 2 * rp;
+        *reinterpret_cast<uint32_t*>(&sX[row * kPitch + 8 * xslot(row, tok >> 3) + (tok & 7)]) =
+            lo | hi;
+      }
+    }
+    // P transposed: word (token pair tp) of rank 8 jc + e
+    const bool ok0 = mb + 2 * tp < M, ok1 = mb + 2 * tp + 1 < M;
+#pragma unroll
+    for (int q = 0; q < RT / 16; ++q) {
+      const int jc = jh + 2 * q;
+      const bool okj = jc < rc;
+      const uint4 p0 = pv[2 * q], p1 = pv[2 * q + 1];
+      const uint32_t w0[4] = {p0.x, p0.y, p0.z, p0.w}, w1[4] = {p1.x, p1.y, p1.z, p1.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = e & 1 ? w0[e >> 1] >> 16 : w0[e >> 1] & 0xFFFFu;
+        const uint32_t hi = e & 1 ? w1[e >> 1] & 0xFFFF0000u : w1[e >> 1] << 16;
+        const uint32_t word = (okj && ok0 ? lo : 0u) | (okj && ok1 ? hi : 0u);
+        *reinterpret_cast<uint32_t*>(&sP[(8 * jc + e) * kPitch + 2 * tp]) = word;
+      }
+    }
+    load_step(i + kDepth, xv, pv);
+#pragma unroll
+    for (int kk = 0; kk < kStep / 32; ++kk) {
+      uint4 pa[RT / 16];
+#pragma unroll
+      for (int a = 0; a < RT / 16; ++a)
+        pa[a] = *reinterpret_cast<const uint4*>(&sP[(16 * a + l16) * kPitch + 32 * kk + 8 * g]);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int xrow = 16 * b + l16;
+        const uint4 xb = *reinterpret_cast<const uint4*>(
+            &sX[xrow * kPitch + 8 * xslot(xrow, 4 * kk + g)]);
+#pragma unroll
+        for (int a = 0; a < RT / 16; ++a) acc[a][b] = mfma16(pa[a], xb, acc[a][b]);
+      }
+    }
+    asm volatile("" ::: "memory");  // keep this step's reads before the next step's stores
+  };
+  if (niter > 0) {
+    uint4 xv[kDepth][2 * kQ];
+    uint4 pv[kDepth][kPV];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d) load_step(d, xv[d], pv[d]);
+    for (int i = 0; i < niter; i += kDepth) {
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d) step(i + d, xv[d], pv[d]);
+    }
+  }
+
+  // Cross-wave sum in wave order, kSlab ranks per pass.  Lane (l16, g)
+  // holds ranks 16 a + 4 g + v of columns 16 b + l16.
+  float* red = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int sl = 0; sl < RT; sl += kSlab) {
+    __syncthreads();  // staging reads (or the previous pass's reads) are done
+#pragma unroll
+    for (int a = sl / 16; a < (sl + kSlab) / 16; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          red[(wave * kSlab + 16 * a + 4 * g + v - sl) * kRP + 16 * b + l16] = acc[a][b][v];
+    __syncthreads();
+    const int nj = r - sl < kSlab ? r - sl : kSlab;  // ranks of this pass
+    if (nj > 0) {
+      auto sum4 = [&](int jj, int c) {
+        const float* p = red + jj * kRP + c;
+        return s * (((p[0] + p[kSlab * kRP]) + p[2 * kSlab * kRP]) + p[3 * kSlab * kRP]);
+      };
+      if (!second) {  // dA [r, C]: 64 consecutive columns per rank
+        for (int idx = tid; idx < nj * 64; idx += 256) {
+          const int jj = idx >> 6, c = idx & 63;
+          dA[static_cast<int64_t>(sl + jj) * C + c0 + c] = sum4(jj, c);
+        }
+      } else {  // dB [C, r]: the tile's rows are contiguous
+        for (int idx = tid; idx < nj * 64; idx += 256) {
+          const int c = idx / nj, jj = idx - c * nj;
+          dB[(c0 + c) * r + sl + jj] = sum4(jj, c);
+        }
+      }
+    }
+  }
+}
+
 // dA[j][k] = s * sum over chunks of partA, then dB[n][j] (transposed) from
 // partB, in one launch; each element's chunks are added in a fixed order.
 __global__ __launch_bounds__(256) void grads_reduce_kernel(const float* __restrict__ partA,
@@ -282,6 +460,18 @@ hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16
                              const uint16_t* t, int64_t M, int64_t N, int64_t K, int r, float s,
                              float* dA, float* dB, void* ws, hipStream_t st) {
   if (r == 0) return hipSuccess;
+  if (r % 8 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0 &&
+      reinterpret_cast<uintptr_t>(t) % 16 == 0) {
+    GradJob ja{}, jb{};
+    ja.X = x; ja.P = t; ja.C = K; ja.ncol = static_cast<int>(K / 64); ja.nwg = ja.ncol;
+    jb.X = dy; jb.P = u; jb.C = N; jb.ncol = static_cast<int>(N / 64); jb.nwg = jb.ncol;
+    const dim3 grid(static_cast<uint32_t>(ja.nwg + jb.nwg));
+    if (r <= 16) hipLaunchKernelGGL((grads_cols_kernel<16>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
+    else if (r <= 32) hipLaunchKernelGGL((grads_cols_kernel<32>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
+    else if (r <= 64) hipLaunchKernelGGL((grads_cols_kernel<64>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
+    else hipLaunchKernelGGL((grads_cols_kernel<128>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
+    return hipGetLastError();
+  }
   const int nchA = static_cast<int>(grads_nchunk(M, K, r));
   const int nchB = static_cast<int>(grads_nchunk(M, N, r));
   float* partA = static_cast<float*>(ws);

@@ -122,3 +122,40 @@ def test_lora_only_decode_rank16(shape, M):
     check(f"lora-only y {shape} r=16 M={M}", to_np(y),
           linear.linear_forward(f64(x), np.zeros((n, k)), f64(A), f64(B), alpha, r))
     check(f"u {shape} r=16 M={M}", to_np(u), linear.lora_down(f64(x), f64(A)))
+
+
+GRAD_CASES = [(8, 16.0, 1), (16, 32.0, 200), (24, 16.0, 1000), (64, 16.0, 4095), (128, 32.0, 130),
+              (32, 16.0, 0)]
+
+
+@pytest.mark.parametrize("r,alpha,M", GRAD_CASES,
+                         ids=[f"r{r}-M{M}" for r, _, M in GRAD_CASES])
+def test_lora_grads_token_edges(r, alpha, M):
+    """LoRA gradients where the token count ends inside a 64-token step and
+    the steps do not divide evenly over a workgroup's waves (M = 1, 200,
+    1000, 4095), ranks below the rank tile (r = 24 of 32), and no tokens
+    (M = 0: both gradients are exactly zero).  With r % 8 == 0 and u, t
+    16-byte aligned the column-tile launch runs; u and t passed one element
+    off 16-byte alignment take the token-chunk launches and its reduction,
+    and both must match the fp64 oracle."""
+    x, dy, A, B = _inputs(M, r, 9000 + 10 * r + M)
+    dxt, dyt, At, Bt = bf16_dev(x), bf16_dev(dy), bf16_dev(A), bf16_dev(B)
+    rA, rB = linear.lora_grads(f64(x), f64(dy), f64(A), f64(B), alpha, r)
+    u_ref = synth.bf16_bits(linear.lora_down(f64(x), f64(A)).astype(np.float32))
+    t_ref = synth.bf16_bits(linear.lora_up_input(f64(dy), f64(B)).astype(np.float32))
+    runs = {"own u, t": qn.lora_grads(dxt, dyt, At, Bt, r, alpha)}
+    for off in (0, 1):
+        ub = torch.zeros(M * r + off, dtype=torch.bfloat16, device="cuda:0")
+        tb = torch.zeros(M * r + off, dtype=torch.bfloat16, device="cuda:0")
+        u = ub[off:].view(M, r)
+        t = tb[off:].view(M, r)
+        u.copy_(bf16_dev(u_ref))
+        t.copy_(bf16_dev(t_ref))
+        runs[f"u, t at +{off}"] = qn.lora_grads(dxt, dyt, At, Bt, r, alpha, u=u, t=t)
+    torch.cuda.synchronize()
+    for name, (dA, dB) in runs.items():
+        if M == 0:
+            assert not torch.any(dA) and not torch.any(dB), name
+            continue
+        check(f"dA r={r} M={M} {name}", to_np(dA), rA)
+        check(f"dB r={r} M={M} {name} (per rank)", to_np(dB).T, rB.T)
