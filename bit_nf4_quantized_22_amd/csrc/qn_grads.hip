@@ -201,7 +201,7 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const
     }
 }
 
-// Column-tile form, no partial sums: a workgroup owns 64 columns of X over
+// Column-tile form, no partial sums: a workgroup owns kCW (64 or 32) columns of X over
 // all M tokens and writes s * sum straight into dA or dB, so one launch
 // does what the chunked kernel and its reduction do in two.  The four waves
 // take interleaved 64-token steps (wave w: steps w, w + 4, ...), each in its
@@ -211,13 +211,14 @@ __global__ __launch_bounds__(256) void grads_mfma_kernel(const GradJob ja, const
 // are added in LDS in wave order at the end.  Needs r % 8 == 0 and P
 // 16-byte aligned: a lane loads 8 consecutive ranks of two adjacent tokens
 // as two 16-byte loads and stores them transposed as token pairs.
-//   X: lane (cg = lane / 8, rp = lane % 8) loads rows 16 q + 2 rp + {0, 1}
-//      (q < 4) of columns 8 cg .. + 7: 8 rows x 128 bytes per instruction.
+//   X: lane (cg = lane / kRPn, rp = lane % kRPn, kRPn = 512 / kCW) loads rows
+//      2 kRPn q + 2 rp + {0, 1} of columns 8 cg .. + 7: 8 rows x 128 bytes
+//      (kCW = 64) or 16 rows x 64 bytes (kCW = 32) per instruction.
 //   P: lane (tp = lane % 32, jh = lane / 32) loads tokens 2 tp + {0, 1},
 //      ranks 8 (jh + 2 q) .. + 7 (q < RT / 16).
 // Tokens past M read row M - 1 and are stored as zero P, ranks past r read
 // a valid chunk and are stored as zero.
-template <int RT>
+template <int RT, int kCW>
 __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const GradJob jb,
                                                          int64_t M, int r, float s,
                                                          float* __restrict__ dA,
@@ -226,7 +227,11 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
   // 11008 x 4096, M = 2048, r = 16)
   constexpr int kDepth = RT <= 64 ? 2 : 1;
   constexpr int kPV = RT / 8;                       // 16-byte P loads per lane per step
-  constexpr int kSX = 64 * kPitch, kSP = RT * kPitch;  // bf16 per wave region
+  constexpr int kCG = kCW / 8;        // 8-column groups of the tile
+  constexpr int kRPn = 64 / kCG;      // lanes per column group: token pairs per load
+  constexpr int kQn = kStep / (2 * kRPn);  // loads of each row of a pair per step
+  constexpr int kCT = kCW / 16;       // 16-column MFMA tiles
+  constexpr int kSX = kCW * kPitch, kSP = RT * kPitch;  // bf16 per wave region
   constexpr int kSlab = RT < 64 ? RT : 64;          // ranks per cross-wave pass
   constexpr int kRP = 65;                           // fp32 pitch of the pass buffer
   constexpr int kStage = 4 * (kSX + kSP) * 2, kRed = 4 * kSlab * kRP * 4;
@@ -237,7 +242,7 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
   const uint16_t* P = second ? jb.P : ja.P;
   const int64_t C = second ? jb.C : ja.C;
   const int ct = static_cast<int>(blockIdx.x) - (second ? ja.nwg : 0);
-  const int64_t c0 = static_cast<int64_t>(ct) * 64;
+  const int64_t c0 = static_cast<int64_t>(ct) * kCW;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -247,17 +252,17 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
   const int nown = (nsteps + 3) / 4;                          // steps of wave 0
   const int niter = (nown + kDepth - 1) / kDepth * kDepth;    // same count for every wave
 
-  const int cg = lane >> 3, rp = lane & 7;
+  const int cg = lane / kRPn, rp = lane % kRPn;
   const int tp = lane & 31, jh = lane >> 5;
   const int rc = r >> 3;  // valid 8-rank chunks
   const uint16_t* Xc = X + c0 + 8 * cg;
-  auto load_step = [&](int i, uint4 (&xv)[2 * kQ], uint4 (&pv)[kPV]) {
+  auto load_step = [&](int i, uint4 (&xv)[2 * kQn], uint4 (&pv)[kPV]) {
     const int64_t mb = static_cast<int64_t>(4 * i + wave) * kStep;
 #pragma unroll
-    for (int q = 0; q < kQ; ++q)
+    for (int q = 0; q < kQn; ++q)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        int64_t m = mb + 16 * q + 2 * rp + h;
+        int64_t m = mb + 2 * kRPn * q + 2 * rp + h;
         m = m < M ? m : M - 1;
         xv[2 * q + h] = *reinterpret_cast<const uint4*>(Xc + m * C);
       }
@@ -273,25 +278,25 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
       }
   };
 
-  f32x4_t acc[RT / 16][4];
+  f32x4_t acc[RT / 16][kCT];
 #pragma unroll
   for (int a = 0; a < RT / 16; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kCT; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int l16 = lane & 15, g = lane >> 4;
-  auto step = [&](int i, uint4 (&xv)[2 * kQ], uint4 (&pv)[kPV]) {
+  auto step = [&](int i, uint4 (&xv)[2 * kQn], uint4 (&pv)[kPV]) {
     const int64_t mb = static_cast<int64_t>(4 * i + wave) * kStep;
-    // X transposed: word (token pair rp + 8 q) of column 8 cg + e
+    // X transposed: word (token pair rp + kRPn q) of column 8 cg + e
 #pragma unroll
-    for (int q = 0; q < kQ; ++q) {
+    for (int q = 0; q < kQn; ++q) {
       const uint32_t a0[4] = {xv[2 * q].x, xv[2 * q].y, xv[2 * q].z, xv[2 * q].w};
       const uint32_t a1[4] = {xv[2 * q + 1].x, xv[2 * q + 1].y, xv[2 * q + 1].z, xv[2 * q + 1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const uint32_t lo = e & 1 ? a0[e >> 1] >> 16 : a0[e >> 1] & 0xFFFFu;
         const uint32_t hi = e & 1 ? a1[e >> 1] & 0xFFFF0000u : a1[e >> 1] << 16;
-        const int row = 8 * cg + e, tok = 16 * q + 2 * rp;
+        const int row = 8 * cg + e, tok = 2 * kRPn * q + 2 * rp;
         *reinterpret_cast<uint32_t*>(&sX[row * kPitch + 8 * xslot(row, tok >> 3) + (tok & 7)]) =
             lo | hi;
       }
@@ -320,7 +325,7 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
       for (int a = 0; a < RT / 16; ++a)
         pa[a] = *reinterpret_cast<const uint4*>(&sP[(16 * a + l16) * kPitch + 32 * kk + 8 * g]);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+      for (int b = 0; b < kCT; ++b) {
         const int xrow = 16 * b + l16;
         const uint4 xb = *reinterpret_cast<const uint4*>(
             &sX[xrow * kPitch + 8 * xslot(xrow, 4 * kk + g)]);
@@ -331,7 +336,7 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
     asm volatile("" ::: "memory");  // keep this step's reads before the next step's stores
   };
   if (niter > 0) {
-    uint4 xv[kDepth][2 * kQ];
+    uint4 xv[kDepth][2 * kQn];
     uint4 pv[kDepth][kPV];
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) load_step(d, xv[d], pv[d]);
@@ -350,7 +355,7 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
 #pragma unroll
     for (int a = sl / 16; a < (sl + kSlab) / 16; ++a)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
+      for (int b = 0; b < kCT; ++b)
 #pragma unroll
         for (int v = 0; v < 4; ++v)
           red[(wave * kSlab + 16 * a + 4 * g + v - sl) * kRP + 16 * b + l16] = acc[a][b][v];
@@ -361,13 +366,13 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
         const float* p = red + jj * kRP + c;
         return s * (((p[0] + p[kSlab * kRP]) + p[2 * kSlab * kRP]) + p[3 * kSlab * kRP]);
       };
-      if (!second) {  // dA [r, C]: 64 consecutive columns per rank
-        for (int idx = tid; idx < nj * 64; idx += 256) {
-          const int jj = idx >> 6, c = idx & 63;
+      if (!second) {  // dA [r, C]: kCW consecutive columns per rank
+        for (int idx = tid; idx < nj * kCW; idx += 256) {
+          const int jj = idx / kCW, c = idx % kCW;
           dA[static_cast<int64_t>(sl + jj) * C + c0 + c] = sum4(jj, c);
         }
       } else {  // dB [C, r]: the tile's rows are contiguous
-        for (int idx = tid; idx < nj * 64; idx += 256) {
+        for (int idx = tid; idx < nj * kCW; idx += 256) {
           const int c = idx / nj, jj = idx - c * nj;
           dB[(c0 + c) * r + sl + jj] = sum4(jj, c);
         }
@@ -462,14 +467,28 @@ hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16
   if (r == 0) return hipSuccess;
   if (r % 8 == 0 && reinterpret_cast<uintptr_t>(u) % 16 == 0 &&
       reinterpret_cast<uintptr_t>(t) % 16 == 0) {
+    // 32-column tiles where 64-column ones would leave most CUs idle, for
+    // r > 16, whose t/u staging dominates a step (4096 x 4096, M = 2048: 128
+    // workgroups; r = 64 22.4 -> 19.6 us, while r = 16 went 13.6 -> 14.2 us)
+    const int cw = r > 16 && (K / 64 + N / 64) < 200 ? 32 : 64;
     GradJob ja{}, jb{};
-    ja.X = x; ja.P = t; ja.C = K; ja.ncol = static_cast<int>(K / 64); ja.nwg = ja.ncol;
-    jb.X = dy; jb.P = u; jb.C = N; jb.ncol = static_cast<int>(N / 64); jb.nwg = jb.ncol;
+    ja.X = x; ja.P = t; ja.C = K; ja.ncol = static_cast<int>(K / cw); ja.nwg = ja.ncol;
+    jb.X = dy; jb.P = u; jb.C = N; jb.ncol = static_cast<int>(N / cw); jb.nwg = jb.ncol;
     const dim3 grid(static_cast<uint32_t>(ja.nwg + jb.nwg));
-    if (r <= 16) hipLaunchKernelGGL((grads_cols_kernel<16>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
-    else if (r <= 32) hipLaunchKernelGGL((grads_cols_kernel<32>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
-    else if (r <= 64) hipLaunchKernelGGL((grads_cols_kernel<64>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
-    else hipLaunchKernelGGL((grads_cols_kernel<128>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB);
+#define QN_GRADS_COLS(RT, CW) \
+  hipLaunchKernelGGL((grads_cols_kernel<RT, CW>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB)
+    if (cw == 64) {
+      if (r <= 16) QN_GRADS_COLS(16, 64);
+      else if (r <= 32) QN_GRADS_COLS(32, 64);
+      else if (r <= 64) QN_GRADS_COLS(64, 64);
+      else QN_GRADS_COLS(128, 64);
+    } else {
+      if (r <= 16) QN_GRADS_COLS(16, 32);
+      else if (r <= 32) QN_GRADS_COLS(32, 32);
+      else if (r <= 64) QN_GRADS_COLS(64, 32);
+      else QN_GRADS_COLS(128, 32);
+    }
+#undef QN_GRADS_COLS
     return hipGetLastError();
   }
   const int nchA = static_cast<int>(grads_nchunk(M, K, r));
