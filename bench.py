@@ -30,7 +30,8 @@ the whole call; "gemv.kernel_only_r0").
 "decode_layer_7b" times one token (M = 1, r = 16) through the seven
 projections of a 7B-shaped layer, captured in one HIP graph over rotating
 layer copies beyond the Infinity Cache: microseconds per layer, and the
-32-layer product (linear layers only).
+32-layer product (linear layers only); "stacked" is the same layer as four
+calls, q|k|v and gate|up each one call on row-stacked weights and adapters.
 
 After the K steps, "layer_7b" times a full 7B-shaped decoder layer (q, k,
 v, o 4096x4096; gate, up 11008x4096; down 4096x11008), its weights bf16
@@ -437,7 +438,10 @@ def decode_layer_7b(qn, torch, dev, synth, r=16, alpha=32.0, std=0.02, seed=9, r
     std) weights quantised on the device, x N(0, 1), A, B N(0, 0.01), LoRA
     r = 16.  The seven calls of each of enough layer copies to exceed the
     256 MiB Infinity Cache are captured in one HIP graph; the time per layer
-    is a replay's time over the copies (median of reps)."""
+    is a replay's time over the copies (median of reps).  "stacked" times the
+    same layer as four calls: q|k|v and gate|up each as one call on
+    row-stacked weights with stacked adapters (rank 3r and 2r, block-diagonal
+    B, alpha scaled so alpha / r is unchanged)."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
     bf = torch.bfloat16
@@ -446,48 +450,105 @@ def decode_layer_7b(qn, torch, dev, synth, r=16, alpha=32.0, std=0.02, seed=9, r
     ncopy = int(np.ceil(ROTATE_BYTES / layer_bytes))
     Ws = {(n, k): (torch.randn(n, k, generator=gen, device=dev) * std).to(bf) for _, n, k in targets}
     copies = [[qn.quantize_weight(Ws[(n, k)]) for _, n, k in targets] for _ in range(ncopy)]
-    del Ws
     xs = {k: torch.randn(1, k, generator=gen, device=dev).to(bf) for _, _, k in targets}
-    ys = {n: torch.empty((1, n), dtype=bf, device=dev) for _, n, _ in targets}
+    ys = [torch.empty((1, n), dtype=bf, device=dev) for _, n, _ in targets]
     ada = [((torch.randn(r, k, generator=gen, device=dev) * 0.01).to(bf),
             (torch.randn(n, r, generator=gen, device=dev) * 0.01).to(bf)) for _, n, k in targets]
     ws = qn.workspace(max(qn.qn_workspace_bytes(0, 1, n, k, r) for _, n, k in targets), dev)
 
     def calls():
         for layer in copies:
-            for (name, n, k), qw, (A, B) in zip(targets, layer, ada):
-                qn.qlora_linear_fwd(qw, xs[k], A, B, r, alpha, y=ys[n], ws=ws)
+            for t, ((name, n, k), qw, (A, B)) in enumerate(zip(targets, layer, ada)):
+                qn.qlora_linear_fwd(qw, xs[k], A, B, r, alpha, y=ys[t], ws=ws)
 
-    stream = torch.cuda.current_stream()
-    gs = torch.cuda.Stream()
-    gs.wait_stream(stream)
-    with torch.cuda.stream(gs):
-        calls()  # eager warm-up on the capture stream
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=gs):
-            calls()
-    stream.wait_stream(gs)
-    torch.cuda.synchronize()
-    g.replay()
-    torch.cuda.synchronize()
-    ts = []
-    for _ in range(reps):
-        s = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        s.record()
-        g.replay()
-        e.record()
+    # Projections that read the same input as one call on row-stacked
+    # weights: q|k|v ([12288, 4096], adapters stacked to rank 3r with a
+    # block-diagonal B and alpha scaled by 3, so alpha / r is unchanged) and
+    # gate|up ([22016, 4096], rank 2r); o and down as before.  Quantising the
+    # stack gives the separate codes and constants byte for byte.
+    def stack_adapters(idx):
+        A = torch.cat([ada[i][0] for i in idx])
+        n = sum(targets[i][1] for i in idx)
+        B = torch.zeros((n, r * len(idx)), dtype=bf, device=dev)
+        row = 0
+        for j, i in enumerate(idx):
+            B[row:row + targets[i][1], j * r:(j + 1) * r] = ada[i][1]
+            row += targets[i][1]
+        return A, B
+    fused = [([0, 1, 2], stack_adapters([0, 1, 2])), ([3], ada[3]),
+             ([4, 5], stack_adapters([4, 5])), ([6], ada[6])]
+    Wcat = {}
+    for idx, _ in fused:
+        Wcat[tuple(idx)] = torch.cat([Ws[(targets[i][1], targets[i][2])] for i in idx])
+    fcopies = [[qn.quantize_weight(Wcat[tuple(idx)]) for idx, _ in fused] for _ in range(ncopy)]
+    del Wcat, Ws
+    ys_f = [torch.empty((1, sum(targets[i][1] for i in idx)), dtype=bf, device=dev)
+            for idx, _ in fused]
+    ws_f = qn.workspace(max(qn.qn_workspace_bytes(0, 1, y.shape[1], targets[idx[0]][2],
+                                                  r * len(idx))
+                            for (idx, _), y in zip(fused, ys_f)), dev)
+
+    def calls_fused():
+        for layer in fcopies:
+            for qw, (idx, (A, B)), y in zip(layer, fused, ys_f):
+                qn.qlora_linear_fwd(qw, xs[targets[idx[0]][2]], A, B, r * len(idx),
+                                    alpha * len(idx), y=y, ws=ws_f)
+
+    def graph_of(fn):
+        stream = torch.cuda.current_stream()
+        gs = torch.cuda.Stream()
+        gs.wait_stream(stream)
+        with torch.cuda.stream(gs):
+            fn()  # eager warm-up on the capture stream
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=gs):
+                fn()
+        stream.wait_stream(gs)
         torch.cuda.synchronize()
-        ts.append(s.elapsed_time(e))
-    us = float(np.median(ts)) * 1e3 / ncopy
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def time_replays(g):
+        ts = []
+        for _ in range(reps):
+            s = torch.cuda.Event(enable_timing=True)
+            e = torch.cuda.Event(enable_timing=True)
+            s.record()
+            g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            ts.append(s.elapsed_time(e))
+        return float(np.median(ts)) * 1e3 / ncopy
+
+    g = graph_of(calls)
+    us = time_replays(g)
+    gf = graph_of(calls_fused)
+    us_f = time_replays(gf)
+    # the last copy's outputs, stacked call against separate calls
+    diff = 0.0
+    for (idx, _), y in zip(fused, ys_f):
+        col = 0
+        for i in idx:
+            n_i = targets[i][1]
+            a, b = y[0, col:col + n_i].float(), ys[i][0].float()
+            diff = max(diff, float((a - b).norm() / b.norm()))
+            col += n_i
     nbytes = layer_bytes + sum(2 * (n + k) + 2 * r * (n + k) for _, n, k in targets)
     res = {"targets": [f"{name} {n}x{k}" for name, n, k in targets], "M": 1, "r": r,
            "alpha": alpha, "layer_copies": ncopy, "us_per_layer": round(us, 3),
            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
            "frac_hbm": round(nbytes / (us * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
            "ms_per_token_32_layers": round(32 * us / 1e3, 4),
+           "stacked": {"us_per_layer": round(us_f, 3),
+                       "GBps": round(nbytes / (us_f * 1e-6) / 1e9, 1),
+                       "frac_hbm": round(nbytes / (us_f * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                       "ms_per_token_32_layers": round(32 * us_f / 1e3, 4),
+                       "max_rel_diff_vs_separate": round(diff, 6),
+                       "calls": "q|k|v stacked (rank 3r, block-diagonal B), o, gate|up "
+                                "stacked (rank 2r), down: four calls per layer"},
            "note": "the seven linear layers only (no attention, norms or sampling)"}
-    del g, copies, xs, ys, ada, ws
+    del g, gf, copies, fcopies, xs, ys, ys_f, ada, fused, ws, ws_f
     torch.cuda.empty_cache()
     return res
 
