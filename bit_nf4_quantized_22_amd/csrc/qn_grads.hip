@@ -56,6 +56,7 @@ struct GradJob {
   int64_t C, chunk;
   int ncol;  // 256-column tiles
   int nwg;   // workgroups: ncol x chunks
+  int pair;  // column-tile kernel: adjacent tiles on one XCD (see grads_cols_kernel)
 };
 
 // RT: rank tile (r <= RT, a multiple of 16).  1-D grid: the workgroups of
@@ -241,7 +242,12 @@ __global__ __launch_bounds__(256) void grads_cols_kernel(const GradJob ja, const
   const uint16_t* X = second ? jb.X : ja.X;
   const uint16_t* P = second ? jb.P : ja.P;
   const int64_t C = second ? jb.C : ja.C;
-  const int ct = static_cast<int>(blockIdx.x) - (second ? ja.nwg : 0);
+  int ct = static_cast<int>(blockIdx.x) - (second ? ja.nwg : 0);
+  // Workgroup b runs on XCD b mod 8.  With 32-column tiles two tiles share
+  // each 128-byte line of a row; with pair set (both jobs' tile counts
+  // multiples of 16, so b mod 8 is the job-local index mod 8) each group of
+  // 16 workgroups takes its 16 tiles as 8 adjacent pairs, a pair on one XCD.
+  if (kCW == 32 && (second ? jb.pair : ja.pair)) ct = (ct & ~15) | ((ct & 7) << 1) | ((ct >> 3) & 1);
   const int64_t c0 = static_cast<int64_t>(ct) * kCW;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -474,6 +480,7 @@ hipError_t launch_grads_impl(const uint16_t* x, const uint16_t* dy, const uint16
     GradJob ja{}, jb{};
     ja.X = x; ja.P = t; ja.C = K; ja.ncol = static_cast<int>(K / cw); ja.nwg = ja.ncol;
     jb.X = dy; jb.P = u; jb.C = N; jb.ncol = static_cast<int>(N / cw); jb.nwg = jb.ncol;
+    ja.pair = jb.pair = ja.ncol % 16 == 0 && jb.ncol % 16 == 0;
     const dim3 grid(static_cast<uint32_t>(ja.nwg + jb.nwg));
 #define QN_GRADS_COLS(RT, CW) \
   hipLaunchKernelGGL((grads_cols_kernel<RT, CW>), grid, dim3(256), 0, st, ja, jb, M, r, s, dA, dB)

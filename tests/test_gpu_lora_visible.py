@@ -159,3 +159,22 @@ def test_lora_grads_token_edges(r, alpha, M):
             continue
         check(f"dA r={r} M={M} {name}", to_np(dA), rA)
         check(f"dB r={r} M={M} {name} (per rank)", to_np(dB).T, rB.T)
+
+
+@pytest.mark.parametrize("NK,r,M", [((1024, 1024), 32, 300), ((512, 1536), 64, 2048)],
+                         ids=["1024x1024-r32", "512x1536-r64"])
+def test_lora_grads_paired_column_tiles(NK, r, M):
+    """32-column gradient tiles with both tile counts multiples of 16, where
+    each group of 16 workgroups takes its tiles as adjacent pairs (one XCD
+    per pair): every column of dA and dB is written once, with its own sum."""
+    n, k = NK
+    rng = np.random.default_rng(9500 + r + M)
+    x = synth.bf16_bits(rng.standard_normal((M, k), dtype=np.float32))
+    dy = synth.bf16_bits(rng.standard_normal((M, n), dtype=np.float32))
+    A = synth.bf16_bits((rng.standard_normal((r, k)) * 0.01).astype(np.float32))
+    B = synth.bf16_bits((rng.standard_normal((n, r)) * 0.01).astype(np.float32))
+    dA, dB = qn.lora_grads(bf16_dev(x), bf16_dev(dy), bf16_dev(A), bf16_dev(B), r, 16.0)
+    torch.cuda.synchronize()
+    rA, rB = linear.lora_grads(f64(x), f64(dy), f64(A), f64(B), 16.0, r)
+    check(f"dA paired tiles {n}x{k} r={r} M={M}", to_np(dA), rA)
+    check(f"dB paired tiles {n}x{k} r={r} M={M} (per rank)", to_np(dB).T, rB.T)
