@@ -371,11 +371,14 @@ QN_API int qlora_merge(const qn_weight* w, const qn_bf16* A, const qn_bf16* B, i
  *   t bf16[M, r] (dy B, the backward's t_out) or NULL to recompute it.
  *   A recomputed u or t is the bf16 value the forward or backward returns
  *   in u_out / t_out (same launches and summation order), so both ways
- *   give the same dA (any M) and dB (M > 16) bit for bit.
+ *   give the same dA (any M) and dB (M > 16) bit for bit when the given
+ *   u and t are 16-byte aligned (as the library's own workspace copies are).
  *   ws     device workspace of ws_bytes >= qn_workspace_bytes(QN_OP_LORA_GRADS,..).
  *   dA fp32[r, K] and dB fp32[N, r] out (overwritten, not accumulated).
- *   r must be 1..128.  The reduction over M is split into fixed chunks and
- *   summed in a fixed order, so results are bit-reproducible.
+ *   r must be 1..128.  The sum over M is taken in a fixed order, so results
+ *   are bit-reproducible: with r % 8 == 0 and u, t 16-byte aligned one
+ *   launch, each workgroup summing all M tokens for its columns; otherwise
+ *   fixed token chunks whose partial sums (in ws) a second launch adds.
  */
 QN_API int lora_grads(const qn_bf16* x, const qn_bf16* dy, const qn_bf16* u,
                const qn_bf16* t, const qn_bf16* A, const qn_bf16* B,
